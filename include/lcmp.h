@@ -1,0 +1,205 @@
+/*
+ * lcmp.h -- C ABI of the teacher-forced logit comparison library (liblcmp.so,
+ * HIP kernels for AMD CDNA4 / gfx950).
+ *
+ * The method is the one of the page "在 agent 时代如何快速验证 kernel 对精度的影响"
+ * (susun-blog, verify-kernel-precision-with-logits; cited below as [logits]):
+ * feed the same fixed text to a ground-truth implementation (the baseline)
+ * and to the implementation under test (the candidate), record at every
+ * position the next-token logits over the full vocabulary, and compare the two
+ * distributions row by row (section 看 logits，而不是 token, teacher forcing).
+ * The bitwise statistics follow the full-logit integer compare of the page
+ * "Kestrel_VLLM - 18 · 投机解码位级对拍收口" (section 二; cited as [bitexact]) and the
+ * arithmetic layer of the correctness ladder on the page "海光 DCU 实测：BF16
+ * 逐位一致为什么仍可能出现文本漂移" (sections 1 and 7; cited as [dcu]).
+ *
+ * Conventions shared by every entry point
+ *   - Tensors are row-major [rows, ld] with ld >= the number of columns used;
+ *     leading dimensions count elements.  Element types: LCMP_F32 (IEEE
+ *     binary32) or LCMP_BF16 (bfloat16 bit patterns, uint16 storage).
+ *   - Every data pointer (inputs, outputs, workspace) is DEVICE memory on the
+ *     current HIP device, except the lcmp_row_out struct itself and `edges`,
+ *     which are host memory read during the call.
+ *   - The caller owns every buffer.  The library allocates and frees nothing,
+ *     keeps no mutable global state, is reentrant, and calls on different
+ *     streams may run concurrently if their workspaces differ.
+ *   - Work is enqueued on `stream` (a hipStream_t; NULL = the default
+ *     stream) and is asynchronous: results are valid once the caller has
+ *     synchronised with that stream.
+ *   - Arguments are validated on the host before anything is enqueued.  On a
+ *     negative return nothing has been launched and no output was written.
+ *     A launch failure returns LCMP_EHIP.  The library never aborts, exits
+ *     or prints.
+ *   - Results are deterministic: the same inputs, sizes and flags give
+ *     bit-identical outputs on every run (fixed-order reductions, no floating
+ *     atomics).
+ */
+#ifndef LCMP_H
+#define LCMP_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define LCMP_ABI_VERSION 1
+#define LCMP_MAX_K 64       /* largest top-k */
+#define LCMP_MAX_EDGES 32   /* largest number of margin-bin edges */
+#define LCMP_MAX_GROUPS 4096
+
+typedef enum { LCMP_F32 = 0, LCMP_BF16 = 1 } lcmp_dtype;
+
+typedef enum {
+  LCMP_OK = 0,
+  LCMP_EINVAL = -1,     /* NULL required pointer, negative count, bad flag, misaligned workspace */
+  LCMP_EDTYPE = -2,     /* unknown element type */
+  LCMP_ESHAPE = -3,     /* v < 2, k out of [1, LCMP_MAX_K], ld < columns, sizes too large */
+  LCMP_EWORKSPACE = -4, /* workspace NULL or smaller than the matching *_workspace_bytes() */
+  LCMP_EHIP = -5,       /* a HIP launch or runtime call failed */
+  LCMP_EEDGES = -6      /* edges not strictly ascending, not positive, NaN, or too many */
+} lcmp_status;
+
+/* flags of lcmp_compare_logits */
+#define LCMP_WITH_BITDIFF 1u /* also fill per-row bitwise statistics in the same pass */
+
+/* per-row status bits (lcmp_row_out.status) */
+#define LCMP_ROW_NONFINITE 1u /* a NaN or +inf on either side */
+#define LCMP_ROW_EMPTY 2u     /* the baseline or the candidate row is entirely -inf */
+
+/*
+ * Per-position outputs of lcmp_compare_logits: device arrays of n entries
+ * (topk_idx: n*k).  Any pointer may be NULL to skip that output.
+ *
+ *   kl_full   KL(P||Q) = sum_i p_i ln(p_i / q_i) over the full vocabulary, P the
+ *             baseline softmax and Q the candidate softmax at temperature 1
+ *             ([logits] 怎么比两个分布, KL equation).  +inf when some p_i > 0 has
+ *             q_i = 0 (candidate -inf where the baseline is finite).
+ *   kl_topk   KL over the baseline's top-k tokens plus one "other" bucket holding
+ *             the rest of the mass on each side ([logits] 怎么比两个分布, top-20
+ *             paragraph).  Equals kl_full when k >= v - 1.
+ *   margin    baseline top-1 logit minus top-2 logit, one double subtraction
+ *             ([logits] 怎么比两个分布, margin paragraph).
+ *   lse_base, lse_cand   log of each side's softmax normaliser.
+ *   top1_base, top2_base baseline's two largest logits, lower index first on ties.
+ *   top1_cand candidate's largest logit, lowest index on ties.
+ *   flip      1 when top1_cand != top1_base ([logits] 怎么比两个分布, top-1 flip).
+ *   topk_idx  the baseline's k largest logits, value descending, index ascending;
+ *             entries past min(k, v) are -1.
+ *   status    0 or a mask of LCMP_ROW_* bits.  A flagged row reports NaN in the
+ *             double fields, -1 in the index fields and 0 in flip.
+ */
+typedef struct {
+  double *kl_topk, *kl_full, *margin, *lse_base, *lse_cand;
+  int32_t *top1_base, *top2_base, *top1_cand;
+  uint8_t *flip, *status;
+  int32_t *topk_idx;
+} lcmp_row_out;
+
+/*
+ * Per-row bitwise statistics ([bitexact] 二: compare full rows as integers,
+ * report the number of differing elements and the first nonzero-ULP position;
+ * [dcu] §1, §7: finite check, max abs, mean abs, relative L2, mismatch count).
+ *
+ *   ndiff        elements whose bit patterns differ
+ *   first_diff   lowest such column, -1 if none
+ *   max_ulp      largest |o(a) - o(b)| with o(u) = u | signbit for a clear sign bit
+ *                and ~u otherwise (a monotone integer image; +0 and -0 are 1 apart)
+ *   nonfinite_a, nonfinite_b   NaN / +-inf elements on each side
+ *   max_abs, sum_abs, sum_sq_diff, sum_sq_base   over columns where both values
+ *                are finite: max |a-b|, sum |a-b|, sum (a-b)^2, sum a^2
+ *   mean_abs     sum_abs / cols
+ *   rel_l2       sqrt(sum_sq_diff / sum_sq_base); 0 if both sums are 0, +inf if
+ *                only sum_sq_base is 0
+ * Same element type on both sides: patterns compared at that width (16 or 32
+ * bits).  Mixed types: bf16 widened exactly to fp32 patterns, compared at 32.
+ */
+typedef struct {
+  int64_t ndiff, first_diff, nonfinite_a, nonfinite_b;
+  uint32_t max_ulp, pad_;
+  double max_abs, sum_abs, sum_sq_diff, sum_sq_base, mean_abs, rel_l2;
+} lcmp_bitdiff_row;
+
+/* One margin bin of one group ([logits] 三者联合起来验证精度问题: flips counted per
+ * margin bin).  max_kl_topk is -inf for an empty bin. */
+typedef struct {
+  int64_t count, flips, ties, tie_flips;
+  double sum_kl_topk, sum_kl_full, max_kl_topk;
+} lcmp_bin;
+
+/* Per-group totals: flips at margin strictly above the big-margin threshold (the
+ * page's stop rule uses 1), rows excluded by a nonzero status, rows whose margin
+ * lies in no bin. */
+typedef struct {
+  int64_t big_margin_flips, excluded, unbinned;
+} lcmp_group_summary;
+
+int lcmp_abi_version(void);
+const char *lcmp_strerror(int status);
+
+/* ---------------------------------------------------------------- compare */
+
+/* Workspace bytes that lcmp_compare_logits needs for these sizes and flags
+ * (0 on invalid sizes).  The workspace must be 16-byte aligned. */
+size_t lcmp_compare_workspace_bytes(int64_t n, int64_t v, int k, uint32_t flags);
+
+/*
+ * Compare n teacher-forced positions: baseline row i against candidate row i,
+ * the first v columns of each ([logits] 看 logits，而不是 token and 怎么比两个分布).
+ *   base, cand    device, [n, ld_base] of type tb and [n, ld_cand] of type tc; the
+ *                 two types may differ.
+ *   k             top-k size, 1..LCMP_MAX_K (the page uses 20); v >= 2.
+ *   flags         0 or LCMP_WITH_BITDIFF; with it, bd (device [n]) receives the
+ *                 bitwise statistics of each row pair (bd may be NULL otherwise).
+ *   out           host struct of device output pointers (see lcmp_row_out).
+ * Returns LCMP_OK or a negative lcmp_status.
+ */
+int lcmp_compare_logits(const void *base, int tb, int64_t ld_base, const void *cand, int tc,
+                        int64_t ld_cand, int64_t n, int64_t v, int k, uint32_t flags,
+                        const lcmp_row_out *out, lcmp_bitdiff_row *bd, void *workspace,
+                        size_t ws_bytes, void *stream);
+
+/* ---------------------------------------------------------------- bitwise */
+
+size_t lcmp_bitdiff_workspace_bytes(int64_t rows, int64_t cols);
+
+/*
+ * Bitwise / ULP statistics of a [rows, cols] pair (see lcmp_bitdiff_row).
+ *   a, b   device, [rows, lda] of type ta and [rows, ldb] of type tb.
+ *   out    device [rows].
+ */
+int lcmp_bitdiff(const void *a, int ta, int64_t lda, const void *b, int tb, int64_t ldb,
+                 int64_t rows, int64_t cols, lcmp_bitdiff_row *out, void *workspace,
+                 size_t ws_bytes, void *stream);
+
+/* ---------------------------------------------------------------- margin bins */
+
+size_t lcmp_bin_workspace_bytes(int64_t n, int n_groups, int n_edges);
+
+/*
+ * Flip counts and KL sums per margin bin and group ([logits] 三者联合起来验证精度
+ * 问题: bin flips by margin, compare each bin with the normal difference, and
+ * treat a flip at a large margin as a stop).
+ *   margin, flip, kl_topk, kl_full   device [n], typically lcmp_compare_logits output.
+ *   status   device [n] or NULL; rows with a nonzero status count as `excluded`.
+ *   group    device [n] or NULL (all rows in group 0); ids outside [0, n_groups)
+ *            are skipped.
+ *   edges    HOST [n_edges], strictly ascending, positive, the last may be +inf.
+ *            Bin j holds margins in [edges[j-1], edges[j]) with edges[-1] = 0.
+ *   big_margin   threshold of the stop rule (the page uses 1): a flip with
+ *            margin > big_margin is counted in big_margin_flips.
+ *   bins     device [n_groups * n_edges]; summary device [n_groups].
+ * Sums are formed in a fixed order, so repeated calls are bit-identical.
+ */
+int lcmp_bin_report(const double *margin, const uint8_t *flip, const double *kl_topk,
+                    const double *kl_full, const uint8_t *status, const int32_t *group,
+                    int n_groups, int64_t n, const double *edges, int n_edges, double big_margin,
+                    lcmp_bin *bins, lcmp_group_summary *summary, void *workspace,
+                    size_t ws_bytes, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LCMP_H */

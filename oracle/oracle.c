@@ -1,0 +1,408 @@
+/*
+ * oracle.c -- plain, slow, double-precision reference for the teacher-forced
+ * logit comparison.  TEST INFRASTRUCTURE ONLY: the parity tests, the smoke
+ * check and the CPU-baseline leg of the benchmark are its only users.  It
+ * shares no code, header, table or constant with the GPU library.
+ *
+ * Every quantity is computed from its plain definition, row by row, with
+ * sequential sums in ascending index order and a full sort for the top-k.
+ * OpenMP only splits independent rows between threads; results do not depend
+ * on the thread count.
+ *
+ * Pages cited (by title and section):
+ *   [logits]  "在 agent 时代如何快速验证 kernel 对精度的影响" (susun-blog,
+ *             verify-kernel-precision-with-logits)
+ *   [bitexact] "Kestrel_VLLM - 18 · 投机解码位级对拍收口" (wsisp.com helps/117433)
+ *   [dcu]     "海光 DCU 实测：BF16 逐位一致为什么仍可能出现文本漂移" (forum.sourcefind.cn)
+ *
+ * Readings taken where the pages leave a step open (each one is restated in
+ * the design notes of the repository):
+ *   - KL is KL(baseline || candidate) in nats, softmax at temperature 1 over
+ *     the full vocabulary.
+ *   - The top-k set is the baseline's k largest logits, ties broken by the
+ *     lower index; the "other" bucket is the complement, summed on each side.
+ *   - The candidate's top-1 is the lowest index among its maximal logits.
+ *   - margin = x[top1] - x[top2] of the baseline, one double subtraction.
+ *   - A row holding NaN or +inf on either side is flagged NONFINITE; a row
+ *     whose baseline or candidate is entirely -inf is flagged EMPTY.  Flagged
+ *     rows report NaN / -1 / 0 in every other field.
+ *   - ULP distance uses the monotone integer ordering o(u) = u | signbit for
+ *     patterns with a clear sign bit and o(u) = ~u otherwise, so +0 and -0
+ *     are one unit apart and "bits differ" equals "nonzero ULP distance".
+ *   - Bitwise error norms are taken over positions where both values are
+ *     finite; non-finite elements are counted per side.
+ *   - Margin bins are half-open [e_{j-1}, e_j) with e_{-1} = 0; a flip at
+ *     margin strictly above the big-margin threshold is a big-margin flip.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+/* dtype codes of the oracle's own interface */
+#define ORC_F32 0
+#define ORC_BF16 1
+
+#define ORC_ROW_NONFINITE 1
+#define ORC_ROW_EMPTY 2
+
+/* ------------------------------------------------------------------ decoding */
+
+static uint32_t pattern32(const void *row, int dtype, int64_t i) {
+  if (dtype == ORC_BF16) return (uint32_t)((const uint16_t *)row)[i] << 16;
+  return ((const uint32_t *)row)[i];
+}
+
+/* exact widening of an element to double */
+static double value(const void *row, int dtype, int64_t i) {
+  uint32_t u = pattern32(row, dtype, i);
+  float f;
+  memcpy(&f, &u, 4);
+  return (double)f;
+}
+
+/* -------------------------------------------------------- softmax statistics */
+
+/* log of the softmax normaliser: m + log(sum_i exp(x_i - m)), summed in index
+ * order ([logits] 怎么比两个分布: p_i is the softmax of the logits). */
+static double log_normaliser(const double *x, int64_t v) {
+  double m = -INFINITY;
+  for (int64_t i = 0; i < v; i++)
+    if (x[i] > m) m = x[i];
+  if (m == -INFINITY) return -INFINITY;
+  double s = 0.0;
+  for (int64_t i = 0; i < v; i++) s += exp(x[i] - m);
+  return m + log(s);
+}
+
+/* ------------------------------------------------------------ top-k ordering */
+
+typedef struct {
+  double x;
+  int64_t i;
+} keyed;
+
+/* value descending, index ascending */
+static int by_value_desc(const void *pa, const void *pb) {
+  const keyed *a = (const keyed *)pa, *b = (const keyed *)pb;
+  if (a->x > b->x) return -1;
+  if (a->x < b->x) return 1;
+  return (a->i < b->i) ? -1 : (a->i > b->i);
+}
+
+/* ------------------------------------------------------------ one row compare */
+
+typedef struct {
+  double kl_topk, kl_full, margin, lse_base, lse_cand;
+  int32_t top1_base, top2_base, top1_cand;
+  uint8_t flip, status;
+} orc_row;
+
+static void flag_row(orc_row *o, uint8_t status, int32_t *topk_idx, int k) {
+  o->kl_topk = o->kl_full = o->margin = o->lse_base = o->lse_cand = NAN;
+  o->top1_base = o->top2_base = o->top1_cand = -1;
+  o->flip = 0;
+  o->status = status;
+  for (int j = 0; j < k; j++) topk_idx[j] = -1;
+}
+
+static void compare_row(const double *x, const double *y, int64_t v, int k, keyed *order,
+                        orc_row *o, int32_t *topk_idx) {
+  /* the finite check of the ladder in [dcu] §1 / §7 */
+  int bad = 0, x_any = 0, y_any = 0;
+  for (int64_t i = 0; i < v; i++) {
+    if (isnan(x[i]) || isnan(y[i]) || x[i] == INFINITY || y[i] == INFINITY) bad = 1;
+    if (x[i] > -INFINITY) x_any = 1;
+    if (y[i] > -INFINITY) y_any = 1;
+  }
+  if (bad) {
+    flag_row(o, ORC_ROW_NONFINITE, topk_idx, k);
+    return;
+  }
+  if (!x_any || !y_any) {
+    flag_row(o, ORC_ROW_EMPTY, topk_idx, k);
+    return;
+  }
+  const int64_t keff = (int64_t)k < v ? (int64_t)k : v;
+
+  const double lse_a = log_normaliser(x, v);
+  const double lse_b = log_normaliser(y, v);
+  o->lse_base = lse_a;
+  o->lse_cand = lse_b;
+
+  /* full KL(P||Q) = sum_i p_i (ln p_i - ln q_i) ([logits] 怎么比两个分布, KL equation).
+   * Tokens with p_i = 0 add nothing; p_i > 0 with q_i = 0 makes it infinite. */
+  double kl = 0.0;
+  int inf_full = 0;
+  for (int64_t i = 0; i < v; i++) {
+    if (x[i] == -INFINITY) continue;
+    if (y[i] == -INFINITY) {
+      inf_full = 1;
+      continue;
+    }
+    const double lp = x[i] - lse_a, lq = y[i] - lse_b;
+    kl += exp(lp) * (lp - lq);
+  }
+  o->kl_full = inf_full ? INFINITY : kl;
+
+  /* baseline top-k by a full sort ([logits] 怎么比两个分布, top-20 + "other") */
+  for (int64_t i = 0; i < v; i++) {
+    order[i].x = x[i];
+    order[i].i = i;
+  }
+  qsort(order, (size_t)v, sizeof(keyed), by_value_desc);
+  for (int j = 0; j < k; j++) topk_idx[j] = j < keff ? (int32_t)order[j].i : -1;
+
+  /* top-k + other KL: head tokens term by term, the rest merged into one bucket
+   * on each side. */
+  double klk = 0.0;
+  int inf_k = 0;
+  for (int64_t j = 0; j < keff; j++) {
+    const int64_t i = order[j].i;
+    if (x[i] == -INFINITY) continue;
+    if (y[i] == -INFINITY) {
+      inf_k = 1;
+      continue;
+    }
+    const double lp = x[i] - lse_a, lq = y[i] - lse_b;
+    klk += exp(lp) * (lp - lq);
+  }
+  /* bucket masses in log form: log p_o = log sum_{i not in S} exp(x_i - lse_a) */
+  double mo_x = -INFINITY, mo_y = -INFINITY;
+  for (int64_t j = keff; j < v; j++) {
+    const int64_t i = order[j].i;
+    if (x[i] > mo_x) mo_x = x[i];
+    if (y[i] > mo_y) mo_y = y[i];
+  }
+  if (mo_x > -INFINITY) {
+    if (mo_y == -INFINITY) {
+      inf_k = 1; /* baseline mass in the bucket, none on the candidate side */
+    } else {
+      double sx = 0.0, sy = 0.0;
+      for (int64_t j = keff; j < v; j++) {
+        const int64_t i = order[j].i;
+        sx += exp(x[i] - mo_x);
+        sy += exp(y[i] - mo_y);
+      }
+      const double lpo = mo_x - lse_a + log(sx), lqo = mo_y - lse_b + log(sy);
+      klk += exp(lpo) * (lpo - lqo);
+    }
+  }
+  o->kl_topk = inf_k ? INFINITY : klk;
+
+  /* margin: baseline top-1 logit minus top-2 logit ([logits] 怎么比两个分布, margin) */
+  o->top1_base = (int32_t)order[0].i;
+  o->top2_base = (int32_t)order[1].i;
+  o->margin = order[0].x - order[1].x;
+
+  /* candidate top-1 (lowest index among the maxima) and the flip
+   * ([logits] 怎么比两个分布, top-1 翻转) */
+  int64_t best = 0;
+  for (int64_t i = 1; i < v; i++)
+    if (y[i] > y[best]) best = i;
+  o->top1_cand = (int32_t)best;
+  o->flip = (uint8_t)(best != order[0].i);
+  o->status = 0;
+}
+
+/*
+ * Compare n rows.  base/cand: row-major with leading dimensions in elements.
+ * Any output pointer may be NULL.  topk_idx is [n, k].  Returns 0, or -1 on
+ * a bad argument or allocation failure.
+ */
+int orc_compare(const void *base, int tb, int64_t ld_base, const void *cand, int tc,
+                int64_t ld_cand, int64_t n, int64_t v, int k, double *kl_topk, double *kl_full,
+                double *margin, double *lse_base, double *lse_cand, int32_t *top1_base,
+                int32_t *top2_base, int32_t *top1_cand, uint8_t *flip, int32_t *topk_idx,
+                uint8_t *status, int nthreads) {
+  if (!base || !cand || n < 0 || v < 2 || k < 1 || ld_base < v || ld_cand < v) return -1;
+  if ((tb != ORC_F32 && tb != ORC_BF16) || (tc != ORC_F32 && tc != ORC_BF16)) return -1;
+  const size_t eb = tb == ORC_BF16 ? 2 : 4, ec = tc == ORC_BF16 ? 2 : 4;
+  int failed = 0;
+#ifdef _OPENMP
+  if (nthreads > 0) omp_set_num_threads(nthreads);
+#else
+  (void)nthreads;
+#endif
+#pragma omp parallel
+  {
+    double *x = (double *)malloc((size_t)v * sizeof(double));
+    double *y = (double *)malloc((size_t)v * sizeof(double));
+    keyed *order = (keyed *)malloc((size_t)v * sizeof(keyed));
+    int32_t *idx = (int32_t *)malloc((size_t)k * sizeof(int32_t));
+    if (!x || !y || !order || !idx) {
+#pragma omp atomic write
+      failed = 1;
+    }
+#pragma omp for schedule(dynamic, 1)
+    for (int64_t r = 0; r < n; r++) {
+      if (!x || !y || !order || !idx) continue;
+      const void *br = (const char *)base + (size_t)r * (size_t)ld_base * eb;
+      const void *cr = (const char *)cand + (size_t)r * (size_t)ld_cand * ec;
+      for (int64_t i = 0; i < v; i++) {
+        x[i] = value(br, tb, i);
+        y[i] = value(cr, tc, i);
+      }
+      orc_row o;
+      compare_row(x, y, v, k, order, &o, idx);
+      if (kl_topk) kl_topk[r] = o.kl_topk;
+      if (kl_full) kl_full[r] = o.kl_full;
+      if (margin) margin[r] = o.margin;
+      if (lse_base) lse_base[r] = o.lse_base;
+      if (lse_cand) lse_cand[r] = o.lse_cand;
+      if (top1_base) top1_base[r] = o.top1_base;
+      if (top2_base) top2_base[r] = o.top2_base;
+      if (top1_cand) top1_cand[r] = o.top1_cand;
+      if (flip) flip[r] = o.flip;
+      if (status) status[r] = o.status;
+      if (topk_idx) memcpy(topk_idx + (size_t)r * (size_t)k, idx, (size_t)k * sizeof(int32_t));
+    }
+    free(x);
+    free(y);
+    free(order);
+    free(idx);
+  }
+  return failed ? -1 : 0;
+}
+
+/* ------------------------------------------------------------ bitwise / ULP */
+
+typedef struct {
+  int64_t ndiff, first_diff, nonfinite_a, nonfinite_b;
+  uint32_t max_ulp, pad_;
+  double max_abs, sum_abs, sum_sq_diff, sum_sq_base, mean_abs, rel_l2;
+} orc_bitdiff_row;
+
+/* monotone integer image of a bit pattern of the given width (16 or 32) */
+static uint32_t ordered(uint32_t u, int width) {
+  const uint32_t sign = width == 16 ? 0x8000u : 0x80000000u;
+  const uint32_t all = width == 16 ? 0xffffu : 0xffffffffu;
+  return (u & sign) ? (~u & all) : (u | sign);
+}
+
+/*
+ * Per-row bitwise statistics between a and b ([bitexact] 二: full-logit
+ * compare as integers, count of differing elements and first differing
+ * position; [dcu] §1 and §7: finite check, max abs, mean abs, relative L2).
+ * Same dtype: patterns compared at that width.  Mixed dtypes: both sides
+ * widened to fp32 patterns (bf16 -> bits << 16), compared at width 32.
+ */
+int orc_bitdiff(const void *a, int ta, int64_t lda, const void *b, int tb, int64_t ldb,
+                int64_t rows, int64_t cols, orc_bitdiff_row *out, int nthreads) {
+  if (!a || !b || !out || rows < 0 || cols < 1 || lda < cols || ldb < cols) return -1;
+  if ((ta != ORC_F32 && ta != ORC_BF16) || (tb != ORC_F32 && tb != ORC_BF16)) return -1;
+  const int width = (ta == ORC_BF16 && tb == ORC_BF16) ? 16 : 32;
+  const size_t ea = ta == ORC_BF16 ? 2 : 4, eb = tb == ORC_BF16 ? 2 : 4;
+#ifdef _OPENMP
+  if (nthreads > 0) omp_set_num_threads(nthreads);
+#else
+  (void)nthreads;
+#endif
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int64_t r = 0; r < rows; r++) {
+    const void *ar = (const char *)a + (size_t)r * (size_t)lda * ea;
+    const void *br = (const char *)b + (size_t)r * (size_t)ldb * eb;
+    orc_bitdiff_row o;
+    memset(&o, 0, sizeof o);
+    o.first_diff = -1;
+    for (int64_t i = 0; i < cols; i++) {
+      uint32_t ua = pattern32(ar, ta, i), ub = pattern32(br, tb, i);
+      if (width == 16) {
+        ua >>= 16;
+        ub >>= 16;
+      }
+      if (ua != ub) {
+        o.ndiff++;
+        if (o.first_diff < 0) o.first_diff = i;
+      }
+      const int64_t d = (int64_t)ordered(ua, width) - (int64_t)ordered(ub, width);
+      const uint32_t ulp = (uint32_t)(d < 0 ? -d : d);
+      if (ulp > o.max_ulp) o.max_ulp = ulp;
+      const double x = value(ar, ta, i), y = value(br, tb, i);
+      const int fx = isfinite(x), fy = isfinite(y);
+      if (!fx) o.nonfinite_a++;
+      if (!fy) o.nonfinite_b++;
+      if (fx && fy) {
+        const double e = x - y;
+        if (fabs(e) > o.max_abs) o.max_abs = fabs(e);
+        o.sum_abs += fabs(e);
+        o.sum_sq_diff += e * e;
+        o.sum_sq_base += x * x;
+      }
+    }
+    o.mean_abs = o.sum_abs / (double)cols;
+    if (o.sum_sq_base > 0.0)
+      o.rel_l2 = sqrt(o.sum_sq_diff / o.sum_sq_base);
+    else
+      o.rel_l2 = o.sum_sq_diff > 0.0 ? INFINITY : 0.0;
+    out[r] = o;
+  }
+  return 0;
+}
+
+/* ------------------------------------------------------------ margin bins */
+
+typedef struct {
+  int64_t count, flips, ties, tie_flips;
+  double sum_kl_topk, sum_kl_full, max_kl_topk;
+} orc_bin;
+
+typedef struct {
+  int64_t big_margin_flips, excluded, unbinned;
+} orc_group_summary;
+
+/*
+ * Flip rates by margin bin ([logits] 三者联合起来验证精度问题: count flips per
+ * margin bin and compare each bin with the normal difference; a flip at a
+ * margin above 1 calls for a stop).  Rows are taken in ascending order.
+ * group may be NULL (one group); rows whose group id is outside
+ * [0, n_groups) are skipped; rows with a nonzero status are counted as
+ * excluded in their group.  bins is [n_groups, n_edges].
+ */
+int orc_bin_report(const double *margin, const uint8_t *flip, const double *kl_topk,
+                   const double *kl_full, const uint8_t *status, const int32_t *group,
+                   int n_groups, int64_t n, const double *edges, int n_edges, double big_margin,
+                   orc_bin *bins, orc_group_summary *summary) {
+  if (!margin || !flip || !kl_topk || !kl_full || !edges || !bins || !summary) return -1;
+  if (n_groups < 1 || n_edges < 1 || n < 0) return -1;
+  for (int j = 0; j < n_edges; j++) {
+    if (isnan(edges[j]) || edges[j] <= 0.0) return -1;
+    if (j > 0 && !(edges[j] > edges[j - 1])) return -1;
+  }
+  for (int64_t t = 0; t < (int64_t)n_groups * n_edges; t++) {
+    memset(&bins[t], 0, sizeof(orc_bin));
+    bins[t].max_kl_topk = -INFINITY;
+  }
+  memset(summary, 0, (size_t)n_groups * sizeof(orc_group_summary));
+  for (int64_t r = 0; r < n; r++) {
+    const int g = group ? group[r] : 0;
+    if (g < 0 || g >= n_groups) continue;
+    if (status && status[r] != 0) {
+      summary[g].excluded++;
+      continue;
+    }
+    const double m = margin[r];
+    if (flip[r] && m > big_margin) summary[g].big_margin_flips++;
+    int j = 0;
+    while (j < n_edges && !(m < edges[j])) j++;
+    if (j == n_edges) {
+      summary[g].unbinned++;
+      continue;
+    }
+    orc_bin *bn = &bins[(int64_t)g * n_edges + j];
+    bn->count++;
+    bn->flips += flip[r] ? 1 : 0;
+    if (m == 0.0) {
+      bn->ties++;
+      bn->tie_flips += flip[r] ? 1 : 0;
+    }
+    bn->sum_kl_topk += kl_topk[r];
+    bn->sum_kl_full += kl_full[r];
+    if (kl_topk[r] > bn->max_kl_topk) bn->max_kl_topk = kl_topk[r];
+  }
+  return 0;
+}
