@@ -47,7 +47,8 @@ extern "C" {
 #define LCMP_ABI_VERSION 1
 #define LCMP_MAX_K 64       /* largest top-k */
 #define LCMP_MAX_EDGES 32   /* largest number of margin-bin edges */
-#define LCMP_MAX_GROUPS 4096
+#define LCMP_MAX_GROUPS 256 /* largest number of row groups in lcmp_bin_report */
+#define LCMP_MAX_BINS 256   /* largest n_groups * n_edges */
 
 typedef enum { LCMP_F32 = 0, LCMP_BF16 = 1 } lcmp_dtype;
 
@@ -55,7 +56,7 @@ typedef enum {
   LCMP_OK = 0,
   LCMP_EINVAL = -1,     /* NULL required pointer, negative count, bad flag, misaligned workspace */
   LCMP_EDTYPE = -2,     /* unknown element type */
-  LCMP_ESHAPE = -3,     /* v < 2, k out of [1, LCMP_MAX_K], ld < columns, sizes too large */
+  LCMP_ESHAPE = -3,     /* v < 2, k out of [1, LCMP_MAX_K], ld < columns, sizes or bin counts too large */
   LCMP_EWORKSPACE = -4, /* workspace NULL or smaller than the matching *_workspace_bytes() */
   LCMP_EHIP = -5,       /* a HIP launch or runtime call failed */
   LCMP_EEDGES = -6      /* edges not strictly ascending, not positive, NaN, or too many */

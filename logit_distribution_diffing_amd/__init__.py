@@ -1,0 +1,254 @@
+"""Teacher-forced logit comparison on AMD MI355X (gfx950): Python binding.
+
+Thin ctypes layer over ``liblcmp.so`` (see ``include/lcmp.h`` for the C ABI).
+It only marshals arguments: torch is used for device memory and streams, and
+every step of the comparison runs in the library's HIP kernels.  There is no
+CPU fallback: importing this module raises if the library has not been built
+(``python -m logit_distribution_diffing_amd.build``).
+
+Entry points (same names as the C ABI):
+  lcmp_compare_logits(base, cand, k=20, with_bitdiff=False)  -> dict of tensors
+  lcmp_bitdiff(a, b)                                         -> structured tensor
+  lcmp_bin_report(margin, flip, kl_topk, kl_full, edges, ...) -> (bins, summary)
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "liblcmp.so")
+
+LCMP_F32, LCMP_BF16 = 0, 1
+LCMP_WITH_BITDIFF = 1
+LCMP_ROW_NONFINITE, LCMP_ROW_EMPTY = 1, 2
+LCMP_MAX_K = 64
+STATUS_NAMES = {0: "LCMP_OK", -1: "LCMP_EINVAL", -2: "LCMP_EDTYPE", -3: "LCMP_ESHAPE",
+                -4: "LCMP_EWORKSPACE", -5: "LCMP_EHIP", -6: "LCMP_EEDGES"}
+
+EXPORTED = ("lcmp_abi_version", "lcmp_strerror", "lcmp_compare_workspace_bytes",
+            "lcmp_compare_logits", "lcmp_bitdiff_workspace_bytes", "lcmp_bitdiff",
+            "lcmp_bin_workspace_bytes", "lcmp_bin_report")
+
+
+class LcmpError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        msg = _lib.lcmp_strerror(status).decode() if _lib is not None else ""
+        super().__init__(f"{where}: {STATUS_NAMES.get(status, status)} ({msg})")
+
+
+class RowOut(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in (
+        "kl_topk", "kl_full", "margin", "lse_base", "lse_cand", "top1_base", "top2_base",
+        "top1_cand", "flip", "status", "topk_idx")]
+
+
+# record sizes of the C structs (int64 x4, uint32 x2, double x6) etc.
+BITDIFF_ROW_BYTES = 4 * 8 + 2 * 4 + 6 * 8
+BIN_BYTES = 4 * 8 + 3 * 8
+GROUP_SUMMARY_BYTES = 3 * 8
+
+_lib = None
+
+
+def _load():
+    global _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            f"{LIB_PATH} is missing; build it with `python -m logit_distribution_diffing_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, i64, ci, u32, sz = (ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_uint32,
+                            ctypes.c_size_t)
+    lib.lcmp_abi_version.restype = ci
+    lib.lcmp_abi_version.argtypes = []
+    lib.lcmp_strerror.restype = ctypes.c_char_p
+    lib.lcmp_strerror.argtypes = [ci]
+    lib.lcmp_compare_workspace_bytes.restype = sz
+    lib.lcmp_compare_workspace_bytes.argtypes = [i64, i64, ci, u32]
+    lib.lcmp_compare_logits.restype = ci
+    lib.lcmp_compare_logits.argtypes = [vp, ci, i64, vp, ci, i64, i64, i64, ci, u32,
+                                        ctypes.POINTER(RowOut), vp, vp, sz, vp]
+    lib.lcmp_bitdiff_workspace_bytes.restype = sz
+    lib.lcmp_bitdiff_workspace_bytes.argtypes = [i64, i64]
+    lib.lcmp_bitdiff.restype = ci
+    lib.lcmp_bitdiff.argtypes = [vp, ci, i64, vp, ci, i64, i64, i64, vp, vp, sz, vp]
+    lib.lcmp_bin_workspace_bytes.restype = sz
+    lib.lcmp_bin_workspace_bytes.argtypes = [i64, ci, ci]
+    lib.lcmp_bin_report.restype = ci
+    lib.lcmp_bin_report.argtypes = [vp, vp, vp, vp, vp, vp, ci, i64,
+                                    ctypes.POINTER(ctypes.c_double), ci, ctypes.c_double,
+                                    vp, vp, vp, sz, vp]
+    _lib = lib
+    return lib
+
+
+_load()
+
+
+def lib() -> ctypes.CDLL:
+    return _lib
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return LCMP_F32
+    if t.dtype == torch.bfloat16:
+        return LCMP_BF16
+    raise TypeError(f"unsupported dtype {t.dtype}: float32 or bfloat16")
+
+
+def _ld(t: torch.Tensor) -> int:
+    if t.dim() != 2 or t.stride(1) != 1:
+        raise ValueError("expected a 2-D tensor with unit stride along the vocabulary")
+    return t.stride(0) if t.size(0) > 1 else max(t.stride(0), t.size(1))
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _check(rc: int, where: str):
+    if rc != 0:
+        raise LcmpError(rc, where)
+
+
+def compare_workspace_bytes(n: int, v: int, k: int = 20, with_bitdiff: bool = False) -> int:
+    return int(_lib.lcmp_compare_workspace_bytes(n, v, k, LCMP_WITH_BITDIFF if with_bitdiff else 0))
+
+
+def alloc_compare_outputs(n: int, k: int, device, with_bitdiff: bool = False) -> dict:
+    f64 = dict(dtype=torch.float64, device=device)
+    i32 = dict(dtype=torch.int32, device=device)
+    u8 = dict(dtype=torch.uint8, device=device)
+    out = dict(kl_topk=torch.empty(n, **f64), kl_full=torch.empty(n, **f64),
+               margin=torch.empty(n, **f64), lse_base=torch.empty(n, **f64),
+               lse_cand=torch.empty(n, **f64), top1_base=torch.empty(n, **i32),
+               top2_base=torch.empty(n, **i32), top1_cand=torch.empty(n, **i32),
+               flip=torch.empty(n, **u8), status=torch.empty(n, **u8),
+               topk_idx=torch.empty((n, k), **i32))
+    if with_bitdiff:
+        out["bitdiff"] = torch.empty((n, BITDIFF_ROW_BYTES), **u8)
+    return out
+
+
+def lcmp_compare_logits(base: torch.Tensor, cand: torch.Tensor, k: int = 20,
+                        with_bitdiff: bool = False, v: int | None = None, out: dict | None = None,
+                        workspace: torch.Tensor | None = None, stream=None) -> dict:
+    """Compare baseline and candidate logits row by row (device tensors [n, >=v]).
+
+    Returns a dict of device tensors (kl_topk, kl_full, margin, lse_base, lse_cand,
+    top1_base, top2_base, top1_cand, flip, status, topk_idx and, with
+    with_bitdiff, a raw [n, 88] uint8 `bitdiff` record tensor; see unpack_bitdiff)."""
+    n = base.size(0)
+    if cand.size(0) != n:
+        raise ValueError("baseline and candidate need the same number of rows")
+    v = base.size(1) if v is None else v
+    flags = LCMP_WITH_BITDIFF if with_bitdiff else 0
+    if out is None:
+        out = alloc_compare_outputs(n, k, base.device, with_bitdiff)
+    ws_bytes = int(_lib.lcmp_compare_workspace_bytes(n, v, k, flags))
+    if ws_bytes == 0:
+        raise LcmpError(-3, "lcmp_compare_workspace_bytes")
+    if workspace is None or workspace.numel() < ws_bytes:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=base.device)
+    ro = RowOut(*[_ptr(out.get(f)) for f in (
+        "kl_topk", "kl_full", "margin", "lse_base", "lse_cand", "top1_base", "top2_base",
+        "top1_cand", "flip", "status", "topk_idx")])
+    rc = _lib.lcmp_compare_logits(
+        base.data_ptr(), _dtype_code(base), _ld(base), cand.data_ptr(), _dtype_code(cand),
+        _ld(cand), n, v, k, flags, ctypes.byref(ro), _ptr(out.get("bitdiff")),
+        workspace.data_ptr(), workspace.numel(), _stream(stream))
+    _check(rc, "lcmp_compare_logits")
+    return out
+
+
+def lcmp_bitdiff(a: torch.Tensor, b: torch.Tensor, cols: int | None = None,
+                 out: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
+                 stream=None) -> torch.Tensor:
+    """Per-row bitwise / ULP statistics; returns a raw [rows, 88] uint8 record tensor."""
+    rows = a.size(0)
+    cols = a.size(1) if cols is None else cols
+    if out is None:
+        out = torch.empty((rows, BITDIFF_ROW_BYTES), dtype=torch.uint8, device=a.device)
+    ws_bytes = int(_lib.lcmp_bitdiff_workspace_bytes(rows, cols))
+    if ws_bytes == 0:
+        raise LcmpError(-3, "lcmp_bitdiff_workspace_bytes")
+    if workspace is None or workspace.numel() < ws_bytes:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=a.device)
+    rc = _lib.lcmp_bitdiff(a.data_ptr(), _dtype_code(a), _ld(a), b.data_ptr(), _dtype_code(b),
+                           _ld(b), rows, cols, out.data_ptr(), workspace.data_ptr(),
+                           workspace.numel(), _stream(stream))
+    _check(rc, "lcmp_bitdiff")
+    return out
+
+
+def lcmp_bin_report(margin, flip, kl_topk, kl_full, edges, status=None, group=None,
+                    n_groups: int = 1, big_margin: float = 1.0, workspace=None, stream=None):
+    """Margin-bin report; returns raw (bins [n_groups*n_edges, 56] uint8,
+    summary [n_groups, 24] uint8) device tensors (see unpack_bins)."""
+    n = margin.numel()
+    edges = [float(e) for e in edges]
+    ne = len(edges)
+    dev = margin.device
+    bins = torch.empty((n_groups * ne, BIN_BYTES), dtype=torch.uint8, device=dev)
+    summ = torch.empty((n_groups, GROUP_SUMMARY_BYTES), dtype=torch.uint8, device=dev)
+    ws_bytes = int(_lib.lcmp_bin_workspace_bytes(n, n_groups, ne))
+    if ws_bytes == 0:
+        raise LcmpError(-3, "lcmp_bin_workspace_bytes")
+    if workspace is None or workspace.numel() < ws_bytes:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    e_arr = (ctypes.c_double * ne)(*edges)
+    rc = _lib.lcmp_bin_report(_ptr(margin), _ptr(flip), _ptr(kl_topk), _ptr(kl_full),
+                              _ptr(status), _ptr(group), n_groups, n, e_arr, ne, big_margin,
+                              bins.data_ptr(), summ.data_ptr(), workspace.data_ptr(),
+                              workspace.numel(), _stream(stream))
+    _check(rc, "lcmp_bin_report")
+    return bins, summ
+
+
+# ----------------------------------------------------------------------------- unpacking
+def _np():
+    import numpy as np
+    return np
+
+
+def bitdiff_dtype():
+    np = _np()
+    return np.dtype([("ndiff", np.int64), ("first_diff", np.int64), ("nonfinite_a", np.int64),
+                     ("nonfinite_b", np.int64), ("max_ulp", np.uint32), ("pad_", np.uint32),
+                     ("max_abs", np.float64), ("sum_abs", np.float64),
+                     ("sum_sq_diff", np.float64), ("sum_sq_base", np.float64),
+                     ("mean_abs", np.float64), ("rel_l2", np.float64)])
+
+
+def bin_dtype():
+    np = _np()
+    return np.dtype([("count", np.int64), ("flips", np.int64), ("ties", np.int64),
+                     ("tie_flips", np.int64), ("sum_kl_topk", np.float64),
+                     ("sum_kl_full", np.float64), ("max_kl_topk", np.float64)])
+
+
+def summary_dtype():
+    np = _np()
+    return np.dtype([("big_margin_flips", np.int64), ("excluded", np.int64),
+                     ("unbinned", np.int64)])
+
+
+def unpack_bitdiff(raw: torch.Tensor):
+    """[rows, 88] uint8 device/host tensor -> numpy structured array."""
+    return raw.cpu().numpy().reshape(-1).view(bitdiff_dtype())
+
+
+def unpack_bins(bins: torch.Tensor, summ: torch.Tensor, n_groups: int = 1):
+    b = bins.cpu().numpy().reshape(-1).view(bin_dtype()).reshape(n_groups, -1)
+    s = summ.cpu().numpy().reshape(-1).view(summary_dtype())
+    return b, s

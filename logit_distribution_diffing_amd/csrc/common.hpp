@@ -1,0 +1,173 @@
+// common.hpp -- device-side helpers and workspace records of liblcmp (gfx950).
+//
+// Layout decisions for CDNA4: one wave64 owns one (row, chunk) work item and
+// streams it with 16-byte non-temporal loads; a 256-thread block is only a
+// container of four independent waves, so the streaming kernel needs no
+// barrier.  Per-lane accumulators are float for runs of 8 elements and
+// double across runs; every cross-lane and cross-chunk reduction has a fixed
+// order, so results are bit-identical from run to run.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace lcmp {
+
+constexpr int kWave = 64;
+constexpr int kBlock = 256;
+constexpr int kWavesPerBlock = kBlock / kWave;
+constexpr int kMaxK = 64;
+constexpr int kSpan = kWave * 8;       // elements one wave covers per step (8 per lane)
+constexpr int kCap = 256;              // per-wave top-k candidate buffer (entries)
+constexpr int kMaxChunks = 64;         // chunks per row (one lane of the merge each)
+
+// exp(x) is evaluated as exp2(x * kL2E - r2) with a wave-uniform reference r2
+// (log2 units).  The finalize uses the same float constant, so the reference
+// of the streamed sums and of the top-k terms agree exactly.
+constexpr float kL2E = 1.44269504088896340736f;
+constexpr double kLn2 = 0.69314718055994530942;
+// lazily move the reference when a logit exceeds it by 2^24 (in exp2 units)
+constexpr float kRescaleLog2 = 24.0f;
+// |delta| bound of the polynomial for phi(d) = d + expm1(-d)
+constexpr float kPolyMax = 0.125f;
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// --------------------------------------------------------------------- records
+
+// One per (row, chunk): streamed softmax sums and counters.  s, d, f are
+// sum e_i, sum e_i*delta_i and sum e_i*phi(delta_i) with e_i = 2^(a_i*kL2E - r2).
+struct ChunkStats {
+  double s, d, f;
+  double r2;     // reference in log2 units; -inf when the chunk held no finite logit
+  float bmax;    // candidate maximum (-inf if none)
+  int32_t bidx;  // lowest index of bmax, -1 if none
+  int32_t cnt;   // top-k entries stored for this chunk
+  int32_t n_bad, n_ainf, n_binf, n_qzero;
+  int32_t pad_;
+};
+
+// One per (row, chunk) when bitwise statistics are requested.
+struct ChunkBits {
+  int64_t ndiff, first;  // first differing column, -1 if none
+  int64_t nfa, nfb;
+  uint32_t max_ulp, pad_;
+  double max_abs;
+  double sum_abs, ssd, ssb;
+};
+
+// Public per-row record (mirrors lcmp_bitdiff_row).
+struct BitdiffRow {
+  int64_t ndiff, first_diff, nonfinite_a, nonfinite_b;
+  uint32_t max_ulp, pad_;
+  double max_abs, sum_abs, sum_sq_diff, sum_sq_base, mean_abs, rel_l2;
+};
+
+// --------------------------------------------------------------------- lanes
+
+__device__ __forceinline__ int lane_id() {
+  return __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+}
+
+__device__ __forceinline__ uint64_t ballot(bool p) { return __builtin_amdgcn_ballot_w64(p); }
+
+// lanes below this one whose bit is set in m
+__device__ __forceinline__ int prefix_count(uint64_t m) {
+  return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+}
+
+template <typename T>
+__device__ __forceinline__ T uniform(T x) {
+  return __builtin_amdgcn_readfirstlane(x);
+}
+__device__ __forceinline__ float uniform(float x) {
+  return __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(x)));
+}
+
+// Butterfly reductions: lane l combines with lane l^m, so every lane ends with
+// the same bit pattern (the combine is commutative) and the order is fixed.
+__device__ __forceinline__ double wave_sum(double x) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) x += __shfl_xor(x, m, kWave);
+  return x;
+}
+__device__ __forceinline__ int64_t wave_sum(int64_t x) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) x += __shfl_xor(x, m, kWave);
+  return x;
+}
+__device__ __forceinline__ int wave_sum(int x) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) x += __shfl_xor(x, m, kWave);
+  return x;
+}
+__device__ __forceinline__ double wave_max(double x) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) x = fmax(x, __shfl_xor(x, m, kWave));
+  return x;
+}
+__device__ __forceinline__ float wave_max(float x) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) x = fmaxf(x, __shfl_xor(x, m, kWave));
+  return x;
+}
+__device__ __forceinline__ uint32_t wave_max(uint32_t x) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) x = max(x, (uint32_t)__shfl_xor((int)x, m, kWave));
+  return x;
+}
+__device__ __forceinline__ int wave_min(int x) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) x = min(x, __shfl_xor(x, m, kWave));
+  return x;
+}
+__device__ __forceinline__ int64_t wave_min(int64_t x) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) x = min(x, (int64_t)__shfl_xor(x, m, kWave));
+  return x;
+}
+__device__ __forceinline__ int wave_max(int x) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) x = max(x, __shfl_xor(x, m, kWave));
+  return x;
+}
+
+// --------------------------------------------------------------------- values
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// Monotone unsigned image of a float for ranking: -0 is first folded onto +0
+// (they compare equal), then positive patterns get the sign bit set and
+// negative ones are inverted.
+__device__ __forceinline__ uint32_t rank_key(float x) {
+  uint32_t u = __float_as_uint(x + 0.0f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ float rank_key_inv(uint32_t o) {
+  return __uint_as_float((o & 0x80000000u) ? (o & 0x7fffffffu) : ~o);
+}
+
+// Ordered image used for ULP distances (no folding of -0: +0 and -0 are one
+// unit apart).  Width 32 on fp32 patterns.
+__device__ __forceinline__ uint32_t ulp_order32(uint32_t u) {
+  return u ^ ((uint32_t)((int32_t)u >> 31) | 0x80000000u);
+}
+// Width 16 on a bf16 pattern held in the low half.
+__device__ __forceinline__ uint32_t ulp_order16(uint32_t h) {
+  return (h & 0x8000u) ? (~h & 0xffffu) : (h | 0x8000u);
+}
+
+// phi(d) / d^2 = 1/2 - d/6 + d^2/24 - d^3/120 + ..., truncated after d^3; the
+// dropped terms are below 7e-7 relative for |d| <= 1/8.
+__device__ __forceinline__ float phi_over_d2(float d) {
+  float p = fmaf(d, -1.0f / 120.0f, 1.0f / 24.0f);
+  p = fmaf(d, p, -1.0f / 6.0f);
+  return fmaf(d, p, 0.5f);
+}
+
+// psi(x) = x - log1p(x), the second-order remainder of log1p (x >= -1).
+__device__ __forceinline__ double psi(double x) { return x - log1p(x); }
+
+}  // namespace lcmp

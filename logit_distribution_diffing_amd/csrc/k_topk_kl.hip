@@ -1,0 +1,215 @@
+// k_topk_kl.hip -- per-row merge of the streamed chunk records and the final
+// comparison quantities, in double precision (one wave per row).
+//
+// With u = E/s (E = f - d = sum e*expm1(-delta)), L = lse_cand - lse_base =
+// log1p(u), and p_i = e_i/s:
+//   full KL    = sum_i p_i (delta_i + L)                 = f/s - psi(u)
+//   top-k KL   = sum_S p_i phi_i + p_o psi(E_o/p_o) - psi(u)
+// where psi(x) = x - log1p(x), phi_i = delta_i + expm1(-delta_i), S the
+// baseline's top-k set, p_o its complement mass and E_o = u - sum_S p_i g_i
+// (g_i = expm1(-delta_i)).  Both are the KL of the page "在 agent 时代如何快速验证
+// kernel 对精度的影响" (section 怎么比两个分布: the KL equation and the top-20 +
+// "other" bucket) rewritten so that only second-order quantities are summed:
+// no difference of two nearly equal log-normalisers is ever formed.
+#include "common.hpp"
+#include "launch.hpp"
+#include "merge.hpp"
+
+#include <math.h>
+
+namespace lcmp {
+
+__device__ __forceinline__ void wave_fence2() {
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+}
+
+__global__ __launch_bounds__(kWave) void k_topk_kl(FinalArgs a) {
+  extern __shared__ uint32_t smem[];
+  const int lane = lane_id();
+  const int64_t row = blockIdx.x;
+  const int C = a.nchunks;
+  const int kint = a.kint;
+  const int mcap = C * kint;
+  uint32_t *e_key = smem;                          // [mcap]
+  int32_t *e_idx = (int32_t *)(e_key + mcap);      // [mcap]
+  float *e_b = (float *)(e_idx + mcap);            // [mcap]
+  float *s_a = (float *)(e_b + mcap);              // [kMaxK] sorted
+  float *s_b = s_a + kMaxK;
+  int32_t *s_i = (int32_t *)(s_b + kMaxK);
+
+  if (a.bd) merge_bits(a.bits + row * C, C, a.v, a.bd + row);
+
+  // ---- chunk sums, rescaled to the largest reference
+  const bool has = lane < C;
+  ChunkStats cs;
+  if (has) cs = a.stats[row * C + lane];
+  const double r2 = has ? cs.r2 : -INFINITY;
+  const double M2 = wave_max(r2);
+  const int nb = wave_sum(has ? cs.n_bad : 0);
+  const int na = wave_sum(has ? cs.n_ainf : 0);
+  const int nbi = wave_sum(has ? cs.n_binf : 0);
+  const int nq = wave_sum(has ? cs.n_qzero : 0);
+  uint8_t status = 0;
+  if (nb > 0)
+    status = 1;  // LCMP_ROW_NONFINITE
+  else if ((int64_t)na == a.v || (int64_t)nbi == a.v)
+    status = 2;  // LCMP_ROW_EMPTY
+  if (status) {
+    if (lane == 0) {
+      if (a.kl_topk) a.kl_topk[row] = NAN;
+      if (a.kl_full) a.kl_full[row] = NAN;
+      if (a.margin) a.margin[row] = NAN;
+      if (a.lse_base) a.lse_base[row] = NAN;
+      if (a.lse_cand) a.lse_cand[row] = NAN;
+      if (a.top1_base) a.top1_base[row] = -1;
+      if (a.top2_base) a.top2_base[row] = -1;
+      if (a.top1_cand) a.top1_cand[row] = -1;
+      if (a.flip) a.flip[row] = 0;
+      if (a.status) a.status[row] = status;
+    }
+    if (a.topk_idx)
+      for (int j = lane; j < a.k; j += kWave) a.topk_idx[row * a.k + j] = -1;
+    return;
+  }
+  const double sc = (has && r2 > -INFINITY) ? exp2(r2 - M2) : 0.0;
+  const double S = wave_sum(has ? cs.s * sc : 0.0);
+  const double D = wave_sum(has ? cs.d * sc : 0.0);
+  const double F = wave_sum(has ? cs.f * sc : 0.0);
+
+  // ---- candidate argmax across chunks: value descending, index ascending
+  const float bm = has ? cs.bmax : -INFINITY;
+  const float BM = uniform(wave_max(bm));
+  const int bx = wave_min((has && cs.bidx >= 0 && bm == BM) ? cs.bidx : 0x7fffffff);
+  const int top1_cand = bx == 0x7fffffff ? -1 : bx;
+
+  // ---- gather the chunk top-k sets
+  int off = 0, m = 0;
+  for (int c = 0; c < C; ++c) {
+    const int cc = __shfl(has ? cs.cnt : 0, c, kWave);
+    if (c < lane) off += cc;
+    m += cc;
+  }
+  for (int c = 0; c < C; ++c) {
+    const int cc = __shfl(has ? cs.cnt : 0, c, kWave);
+    const int oc = __shfl(off, c, kWave);
+    const int64_t src = (row * C + c) * kint;
+    for (int j = lane; j < cc; j += kWave) {
+      e_key[oc + j] = rank_key(a.ta[src + j]);
+      e_idx[oc + j] = a.ti[src + j];
+      e_b[oc + j] = a.tb[src + j];
+    }
+  }
+  for (int j = lane; j < kMaxK; j += kWave) {
+    s_a[j] = -INFINITY;
+    s_b[j] = -INFINITY;
+    s_i[j] = -1;
+  }
+  wave_fence2();
+  // rank of each entry among all entries (keys are distinct through the index)
+  for (int e = lane; e < m; e += kWave) {
+    const uint32_t ke = e_key[e];
+    const int ie = e_idx[e];
+    int rank = 0;
+    for (int f = 0; f < m; ++f) {
+      const uint32_t kf = e_key[f];
+      rank += (kf > ke || (kf == ke && e_idx[f] < ie)) ? 1 : 0;
+    }
+    if (rank < kint) {
+      s_a[rank] = rank_key_inv(ke);
+      s_b[rank] = e_b[e];
+      s_i[rank] = ie;
+    }
+  }
+  wave_fence2();
+
+  // ---- head terms (lanes j < k_eff)
+  const int keff = (int)min((int64_t)a.k, a.v);
+  const bool in_head = lane < keff;
+  const float ha = in_head ? s_a[lane] : -INFINITY;
+  const float hb = in_head ? s_b[lane] : -INFINITY;
+  const bool ainf = ha == -INFINITY, binf = hb == -INFINITY;
+  double e = 0.0, tphi = 0.0, tg = 0.0;
+  int head_inf = 0;
+  if (in_head && !ainf) {
+    e = exp2((double)ha * (double)kL2E - M2);
+    const double p = e / S;
+    if (binf) {
+      head_inf = 1;
+      tg = -p;
+    } else {
+      const double dl = (double)ha - (double)hb;
+      const double g = expm1(-dl);
+      tphi = p * (dl + g);
+      tg = p * g;
+    }
+  }
+  const double sum_e = wave_sum(e), sum_pphi = wave_sum(tphi), sum_pg = wave_sum(tg);
+  const int n_sa = wave_sum((in_head && ainf) ? 1 : 0);
+  const int n_sb = wave_sum((in_head && binf) ? 1 : 0);
+  const int any_head_inf = wave_max(head_inf);
+
+  if (a.topk_idx)
+    for (int j = lane; j < a.k; j += kWave) a.topk_idx[row * a.k + j] = j < keff ? s_i[j] : -1;
+
+  if (lane == 0) {
+    double u = (F - D) / S;
+    if (!(u > -1.0)) u = -1.0 + 0x1p-52;
+    const double lse_b = M2 * kLn2 + log(S);
+    const double kl_full = nq > 0 ? INFINITY : F / S - psi(u);
+    double klk;
+    if (any_head_inf) {
+      klk = INFINITY;
+    } else {
+      klk = sum_pphi - psi(u);
+      const int64_t n_other = a.v - keff;
+      const int64_t o_fin_a = n_other - ((int64_t)na - n_sa);
+      const int64_t o_fin_b = n_other - ((int64_t)nbi - n_sb);
+      if (o_fin_a > 0) {
+        if (o_fin_b == 0) {
+          klk = INFINITY;
+        } else {
+          const double p_o = fmax(0.0, (S - sum_e) / S);
+          if (p_o > 0.0) {
+            double x = (u - sum_pg) / p_o;
+            if (!(x > -1.0)) x = -1.0 + 0x1p-52;
+            klk += p_o * psi(x);
+          }
+        }
+      }
+    }
+    if (a.kl_topk) a.kl_topk[row] = klk;
+    if (a.kl_full) a.kl_full[row] = kl_full;
+    if (a.margin) a.margin[row] = (double)s_a[0] - (double)s_a[1];
+    if (a.lse_base) a.lse_base[row] = lse_b;
+    if (a.lse_cand) a.lse_cand[row] = lse_b + log1p(u);
+    if (a.top1_base) a.top1_base[row] = s_i[0];
+    if (a.top2_base) a.top2_base[row] = s_i[1];
+    if (a.top1_cand) a.top1_cand[row] = top1_cand;
+    if (a.flip) a.flip[row] = (uint8_t)(top1_cand != s_i[0]);
+    if (a.status) a.status[row] = 0;
+  }
+}
+
+hipError_t launch_topk_kl(const FinalArgs &a, hipStream_t stream) {
+  if (a.n == 0) return hipSuccess;
+  const size_t mcap = (size_t)a.nchunks * a.kint;
+  const size_t shmem = mcap * 12 + (size_t)kMaxK * 12;
+  hipLaunchKernelGGL(k_topk_kl, dim3((unsigned)a.n), dim3(kWave), shmem, stream, a);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------- bitwise-only rows
+
+__global__ __launch_bounds__(kWave) void k_bitdiff_final(BitsFinalArgs a) {
+  const int64_t row = blockIdx.x;
+  merge_bits(a.bits + row * a.nchunks, a.nchunks, a.cols, a.out + row);
+}
+
+hipError_t launch_bitdiff_final(const BitsFinalArgs &a, hipStream_t stream) {
+  if (a.rows == 0) return hipSuccess;
+  hipLaunchKernelGGL(k_bitdiff_final, dim3((unsigned)a.rows), dim3(kWave), 0, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace lcmp

@@ -1,0 +1,84 @@
+// launch.hpp -- argument records and host-side launchers shared by the
+// translation units of liblcmp (internal; not part of the C ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "common.hpp"
+
+namespace lcmp {
+
+// streaming pass (k_row_stats): one wave per (row, chunk)
+struct StreamArgs {
+  const void *a, *b;
+  int64_t lda, ldb;  // elements
+  int64_t n, v;      // rows, columns used
+  int64_t chunk;     // chunk length in elements, a multiple of kSpan
+  int32_t nchunks;   // chunks per row
+  int32_t kint;      // top-k entries kept per chunk
+  ChunkStats *stats;  // [n * nchunks]  (compare)
+  ChunkBits *bits;    // [n * nchunks]  (bitwise)
+  float *ta, *tb;     // [n * nchunks * kint]
+  int32_t *ti;
+};
+
+// per-row merge and finalize (k_topk_kl)
+struct FinalArgs {
+  const ChunkStats *stats;
+  const ChunkBits *bits;  // NULL: no bitwise output
+  const float *ta, *tb;
+  const int32_t *ti;
+  int64_t n, v;
+  int32_t nchunks, kint, k;
+  double *kl_topk, *kl_full, *margin, *lse_base, *lse_cand;
+  int32_t *top1_base, *top2_base, *top1_cand;
+  uint8_t *flip, *status;
+  int32_t *topk_idx;
+  BitdiffRow *bd;
+};
+
+// per-row merge of bitwise chunks (k_bitdiff)
+struct BitsFinalArgs {
+  const ChunkBits *bits;
+  int64_t rows, cols;
+  int32_t nchunks;
+  BitdiffRow *out;
+};
+
+// one margin bin of one group, plus per-group counters (k_bin_reduce)
+struct BinAcc {
+  int64_t count, flips, ties, tie_flips;
+  double sum_kl_topk, sum_kl_full, max_kl_topk;
+};
+struct GroupAcc {
+  int64_t big_margin_flips, excluded, unbinned;
+};
+
+constexpr int kBinRowsPerBlock = 2048;  // rows of one level-1 block (one wave)
+constexpr int kMaxBins = 256;           // n_groups * n_edges
+constexpr int kMaxGroups = 256;
+constexpr int kMaxEdges = 32;
+
+struct BinArgs {
+  const double *margin, *kl_topk, *kl_full;
+  const uint8_t *flip, *status;
+  const int32_t *group;
+  int64_t n;
+  int32_t n_groups, n_edges;
+  double edges[kMaxEdges];
+  double big_margin;
+  BinAcc *part_bins;      // [nblk * n_groups * n_edges]
+  GroupAcc *part_groups;  // [nblk * n_groups]
+  int32_t nblk;
+  BinAcc *bins;           // [n_groups * n_edges]
+  GroupAcc *groups;       // [n_groups]
+};
+
+hipError_t launch_row_stats(const StreamArgs &a, int ta, int tb, bool cmp, bool bits, bool vec,
+                            hipStream_t stream);
+hipError_t launch_topk_kl(const FinalArgs &a, hipStream_t stream);
+hipError_t launch_bitdiff_final(const BitsFinalArgs &a, hipStream_t stream);
+hipError_t launch_bin_reduce(const BinArgs &a, hipStream_t stream);
+
+}  // namespace lcmp

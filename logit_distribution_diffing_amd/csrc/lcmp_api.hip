@@ -1,0 +1,282 @@
+// lcmp_api.hip -- the C ABI of liblcmp: argument checks, workspace layout,
+// chunking, launches.  Declarations and the contract live in include/lcmp.h.
+#include "../../include/lcmp.h"
+
+#include <math.h>
+#include <string.h>
+
+#include "common.hpp"
+#include "launch.hpp"
+
+using namespace lcmp;
+
+static_assert(sizeof(lcmp_bitdiff_row) == sizeof(BitdiffRow), "bitdiff row layout");
+static_assert(sizeof(lcmp_bin) == sizeof(BinAcc), "bin layout");
+static_assert(sizeof(lcmp_group_summary) == sizeof(GroupAcc), "group summary layout");
+static_assert(kMaxGroups == LCMP_MAX_GROUPS && kMaxBins == LCMP_MAX_BINS &&
+                  kMaxEdges == LCMP_MAX_EDGES && kMaxK == LCMP_MAX_K,
+              "limits of the header and of the kernels agree");
+
+namespace {
+
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+bool dtype_ok(int t) { return t == LCMP_F32 || t == LCMP_BF16; }
+size_t esize(int t) { return t == LCMP_BF16 ? 2 : 4; }
+
+// Chunks per row: enough (row, chunk) waves to fill the GPU several times over
+// (256 CUs x 16 waves, four times), without cutting a row into pieces shorter
+// than 16 wave steps.  A function of the sizes only, so the summation order,
+// and hence every result bit, does not depend on the device or the stream.
+struct Chunking {
+  int64_t chunk;
+  int32_t nchunks;
+};
+
+Chunking choose_chunks(int64_t n, int64_t v) {
+  const int64_t steps = (v + kSpan - 1) / kSpan;
+  const int64_t target_items = 4 * 256 * 16;
+  int64_t c = n > 0 ? (target_items + n - 1) / n : 1;
+  const int64_t cmax = steps / 16 > 1 ? steps / 16 : 1;
+  if (c > cmax) c = cmax;
+  if (c > 16) c = 16;
+  if (c < 1) c = 1;
+  const int64_t per = (steps + c - 1) / c;
+  Chunking ch;
+  ch.chunk = per * kSpan;
+  ch.nchunks = (int32_t)((v + ch.chunk - 1) / ch.chunk);
+  return ch;
+}
+
+int kint_of(int64_t v, int k) {
+  const int64_t keff = (int64_t)k < v ? (int64_t)k : v;
+  return (int)(keff < 2 ? 2 : keff);
+}
+
+struct CompareLayout {
+  Chunking ch;
+  int kint;
+  size_t off_stats, off_bits, off_ta, off_tb, off_ti, total;
+};
+
+CompareLayout compare_layout(int64_t n, int64_t v, int k, uint32_t flags) {
+  CompareLayout L;
+  L.ch = choose_chunks(n, v);
+  L.kint = kint_of(v, k);
+  const size_t items = (size_t)n * (size_t)L.ch.nchunks;
+  size_t o = 0;
+  L.off_stats = o;
+  o = align_up(o + items * sizeof(ChunkStats));
+  L.off_bits = o;
+  if (flags & LCMP_WITH_BITDIFF) o = align_up(o + items * sizeof(ChunkBits));
+  L.off_ta = o;
+  o = align_up(o + items * (size_t)L.kint * sizeof(float));
+  L.off_tb = o;
+  o = align_up(o + items * (size_t)L.kint * sizeof(float));
+  L.off_ti = o;
+  o = align_up(o + items * (size_t)L.kint * sizeof(int32_t));
+  L.total = o;
+  return L;
+}
+
+// 16-byte loads need every row start of both tensors 16-byte aligned
+bool vector_ok(const void *a, int ta, int64_t lda, const void *b, int tb, int64_t ldb) {
+  const uintptr_t pa = (uintptr_t)a, pb = (uintptr_t)b;
+  return pa % 16 == 0 && pb % 16 == 0 && ((size_t)lda * esize(ta)) % 16 == 0 &&
+         ((size_t)ldb * esize(tb)) % 16 == 0;
+}
+
+constexpr int64_t kMaxCols = 0x7fffffffLL - 4096;  // indices are 32-bit in the kernels
+constexpr int64_t kMaxRows = (int64_t)1 << 40;
+
+}  // namespace
+
+extern "C" {
+
+int lcmp_abi_version(void) { return LCMP_ABI_VERSION; }
+
+const char *lcmp_strerror(int status) {
+  switch (status) {
+    case LCMP_OK: return "ok";
+    case LCMP_EINVAL: return "invalid argument (null pointer, negative count, unknown flag or misaligned workspace)";
+    case LCMP_EDTYPE: return "unknown element type";
+    case LCMP_ESHAPE: return "invalid shape (v < 2, k outside [1, LCMP_MAX_K], ld < columns, or too large)";
+    case LCMP_EWORKSPACE: return "workspace missing or too small";
+    case LCMP_EHIP: return "HIP launch or runtime error";
+    case LCMP_EEDGES: return "margin-bin edges invalid (must be positive, strictly ascending, at most LCMP_MAX_EDGES)";
+    default: return "unknown status";
+  }
+}
+
+size_t lcmp_compare_workspace_bytes(int64_t n, int64_t v, int k, uint32_t flags) {
+  if (n < 0 || v < 2 || v > kMaxCols || n > kMaxRows || k < 1 || k > LCMP_MAX_K) return 0;
+  if (n == 0) return kAlign;
+  return compare_layout(n, v, k, flags).total;
+}
+
+int lcmp_compare_logits(const void *base, int tb, int64_t ld_base, const void *cand, int tc,
+                        int64_t ld_cand, int64_t n, int64_t v, int k, uint32_t flags,
+                        const lcmp_row_out *out, lcmp_bitdiff_row *bd, void *workspace,
+                        size_t ws_bytes, void *stream) {
+  if (!dtype_ok(tb) || !dtype_ok(tc)) return LCMP_EDTYPE;
+  if (n < 0 || (flags & ~LCMP_WITH_BITDIFF) != 0 || !out) return LCMP_EINVAL;
+  if (v < 2 || v > kMaxCols || n > kMaxRows || k < 1 || k > LCMP_MAX_K || ld_base < v ||
+      ld_cand < v)
+    return LCMP_ESHAPE;
+  const bool with_bits = (flags & LCMP_WITH_BITDIFF) != 0;
+  if (with_bits && !bd) return LCMP_EINVAL;
+  if (n == 0) return LCMP_OK;
+  if (!base || !cand) return LCMP_EINVAL;
+  const CompareLayout L = compare_layout(n, v, k, flags);
+  if (!workspace || ws_bytes < L.total) return LCMP_EWORKSPACE;
+  if ((uintptr_t)workspace % 16 != 0) return LCMP_EINVAL;
+
+  char *ws = (char *)workspace;
+  StreamArgs sa;
+  sa.a = base;
+  sa.b = cand;
+  sa.lda = ld_base;
+  sa.ldb = ld_cand;
+  sa.n = n;
+  sa.v = v;
+  sa.chunk = L.ch.chunk;
+  sa.nchunks = L.ch.nchunks;
+  sa.kint = L.kint;
+  sa.stats = (ChunkStats *)(ws + L.off_stats);
+  sa.bits = with_bits ? (ChunkBits *)(ws + L.off_bits) : nullptr;
+  sa.ta = (float *)(ws + L.off_ta);
+  sa.tb = (float *)(ws + L.off_tb);
+  sa.ti = (int32_t *)(ws + L.off_ti);
+  hipStream_t s = (hipStream_t)stream;
+  if (launch_row_stats(sa, tb, tc, true, with_bits, vector_ok(base, tb, ld_base, cand, tc, ld_cand),
+                       s) != hipSuccess)
+    return LCMP_EHIP;
+
+  FinalArgs fa;
+  fa.stats = sa.stats;
+  fa.bits = sa.bits;
+  fa.ta = sa.ta;
+  fa.tb = sa.tb;
+  fa.ti = sa.ti;
+  fa.n = n;
+  fa.v = v;
+  fa.nchunks = L.ch.nchunks;
+  fa.kint = L.kint;
+  fa.k = k;
+  fa.kl_topk = out->kl_topk;
+  fa.kl_full = out->kl_full;
+  fa.margin = out->margin;
+  fa.lse_base = out->lse_base;
+  fa.lse_cand = out->lse_cand;
+  fa.top1_base = out->top1_base;
+  fa.top2_base = out->top2_base;
+  fa.top1_cand = out->top1_cand;
+  fa.flip = out->flip;
+  fa.status = out->status;
+  fa.topk_idx = out->topk_idx;
+  fa.bd = with_bits ? (BitdiffRow *)bd : nullptr;
+  if (launch_topk_kl(fa, s) != hipSuccess) return LCMP_EHIP;
+  return LCMP_OK;
+}
+
+size_t lcmp_bitdiff_workspace_bytes(int64_t rows, int64_t cols) {
+  if (rows < 0 || cols < 1 || cols > kMaxCols || rows > kMaxRows) return 0;
+  if (rows == 0) return kAlign;
+  const Chunking ch = choose_chunks(rows, cols);
+  return align_up((size_t)rows * (size_t)ch.nchunks * sizeof(ChunkBits));
+}
+
+int lcmp_bitdiff(const void *a, int ta, int64_t lda, const void *b, int tb, int64_t ldb,
+                 int64_t rows, int64_t cols, lcmp_bitdiff_row *out, void *workspace,
+                 size_t ws_bytes, void *stream) {
+  if (!dtype_ok(ta) || !dtype_ok(tb)) return LCMP_EDTYPE;
+  if (rows < 0) return LCMP_EINVAL;
+  if (cols < 1 || cols > kMaxCols || rows > kMaxRows || lda < cols || ldb < cols)
+    return LCMP_ESHAPE;
+  if (rows == 0) return LCMP_OK;
+  if (!a || !b || !out) return LCMP_EINVAL;
+  const Chunking ch = choose_chunks(rows, cols);
+  const size_t need = align_up((size_t)rows * (size_t)ch.nchunks * sizeof(ChunkBits));
+  if (!workspace || ws_bytes < need) return LCMP_EWORKSPACE;
+  if ((uintptr_t)workspace % 16 != 0) return LCMP_EINVAL;
+  StreamArgs sa;
+  memset(&sa, 0, sizeof sa);
+  sa.a = a;
+  sa.b = b;
+  sa.lda = lda;
+  sa.ldb = ldb;
+  sa.n = rows;
+  sa.v = cols;
+  sa.chunk = ch.chunk;
+  sa.nchunks = ch.nchunks;
+  sa.kint = 2;
+  sa.bits = (ChunkBits *)workspace;
+  hipStream_t s = (hipStream_t)stream;
+  if (launch_row_stats(sa, ta, tb, false, true, vector_ok(a, ta, lda, b, tb, ldb), s) !=
+      hipSuccess)
+    return LCMP_EHIP;
+  BitsFinalArgs fa;
+  fa.bits = sa.bits;
+  fa.rows = rows;
+  fa.cols = cols;
+  fa.nchunks = ch.nchunks;
+  fa.out = (BitdiffRow *)out;
+  if (launch_bitdiff_final(fa, s) != hipSuccess) return LCMP_EHIP;
+  return LCMP_OK;
+}
+
+size_t lcmp_bin_workspace_bytes(int64_t n, int n_groups, int n_edges) {
+  if (n < 0 || n_groups < 1 || n_groups > kMaxGroups || n_edges < 1 || n_edges > kMaxEdges ||
+      n_groups * n_edges > kMaxBins)
+    return 0;
+  const int64_t nblk = (n + kBinRowsPerBlock - 1) / kBinRowsPerBlock;
+  return align_up((size_t)nblk * (size_t)n_groups * n_edges * sizeof(BinAcc)) +
+         align_up((size_t)nblk * (size_t)n_groups * sizeof(GroupAcc)) + kAlign;
+}
+
+int lcmp_bin_report(const double *margin, const uint8_t *flip, const double *kl_topk,
+                    const double *kl_full, const uint8_t *status, const int32_t *group,
+                    int n_groups, int64_t n, const double *edges, int n_edges, double big_margin,
+                    lcmp_bin *bins, lcmp_group_summary *summary, void *workspace,
+                    size_t ws_bytes, void *stream) {
+  if (n < 0 || !bins || !summary || !edges) return LCMP_EINVAL;
+  if (n_groups < 1 || n_groups > kMaxGroups || n_edges < 1 || n_edges > kMaxEdges ||
+      n_groups * n_edges > kMaxBins)
+    return LCMP_ESHAPE;
+  for (int j = 0; j < n_edges; ++j) {
+    if (isnan(edges[j]) || !(edges[j] > 0.0)) return LCMP_EEDGES;
+    if (j > 0 && !(edges[j] > edges[j - 1])) return LCMP_EEDGES;
+  }
+  if (isnan(big_margin)) return LCMP_EINVAL;
+  if (n > 0 && (!margin || !flip || !kl_topk || !kl_full)) return LCMP_EINVAL;
+  const size_t need = lcmp_bin_workspace_bytes(n, n_groups, n_edges);
+  if (!workspace || ws_bytes < need) return LCMP_EWORKSPACE;
+  if ((uintptr_t)workspace % 16 != 0) return LCMP_EINVAL;
+  const int64_t nblk = (n + kBinRowsPerBlock - 1) / kBinRowsPerBlock;
+  BinArgs ba;
+  memset(&ba, 0, sizeof ba);
+  ba.margin = margin;
+  ba.kl_topk = kl_topk;
+  ba.kl_full = kl_full;
+  ba.flip = flip;
+  ba.status = status;
+  ba.group = group;
+  ba.n = n;
+  ba.n_groups = n_groups;
+  ba.n_edges = n_edges;
+  for (int j = 0; j < n_edges; ++j) ba.edges[j] = edges[j];
+  ba.big_margin = big_margin;
+  char *ws = (char *)workspace;
+  ba.part_bins = (BinAcc *)ws;
+  ba.part_groups =
+      (GroupAcc *)(ws + align_up((size_t)nblk * (size_t)n_groups * n_edges * sizeof(BinAcc)));
+  ba.nblk = (int32_t)nblk;
+  ba.bins = (BinAcc *)bins;
+  ba.groups = (GroupAcc *)summary;
+  if (launch_bin_reduce(ba, (hipStream_t)stream) != hipSuccess) return LCMP_EHIP;
+  return LCMP_OK;
+}
+
+}  // extern "C"

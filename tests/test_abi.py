@@ -1,0 +1,145 @@
+"""The C-ABI library loads, exports every declared entry point, and rejects bad
+arguments on the host before any launch (CPU only: no call here reaches a GPU)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "lcmp.h")
+
+
+@pytest.fixture(scope="module")
+def L():
+    from logit_distribution_diffing_amd import build
+    build.build()
+    import logit_distribution_diffing_amd as mod
+    return mod
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(lcmp_[a-z_]+)\s*\(", text)))
+
+
+def test_every_declared_symbol_is_exported(L):
+    names = declared_functions()
+    assert len(names) >= 8
+    lib = ctypes.CDLL(L.LIB_PATH)
+    for name in names:
+        assert hasattr(lib, name), name
+    assert set(names) == set(L.EXPORTED)
+
+
+def test_version_and_strerror(L):
+    lib = L.lib()
+    assert lib.lcmp_abi_version() == 1
+    for st in (0, -1, -2, -3, -4, -5, -6):
+        assert len(lib.lcmp_strerror(st)) > 0
+    assert lib.lcmp_strerror(-99) == b"unknown status"
+
+
+def test_workspace_queries(L):
+    lib = L.lib()
+    assert lib.lcmp_compare_workspace_bytes(10240, 151936, 20, 0) > 0
+    a = lib.lcmp_compare_workspace_bytes(512, 151936, 20, 0)
+    b = lib.lcmp_compare_workspace_bytes(512, 151936, 20, 1)
+    assert b > a
+    assert lib.lcmp_compare_workspace_bytes(10, 1, 20, 0) == 0      # v < 2
+    assert lib.lcmp_compare_workspace_bytes(10, 100, 0, 0) == 0     # k < 1
+    assert lib.lcmp_compare_workspace_bytes(10, 100, 65, 0) == 0    # k > 64
+    assert lib.lcmp_compare_workspace_bytes(-1, 100, 20, 0) == 0
+    assert lib.lcmp_bitdiff_workspace_bytes(4096, 5120) > 0
+    assert lib.lcmp_bitdiff_workspace_bytes(4, 0) == 0
+    assert lib.lcmp_bin_workspace_bytes(65536, 1, 6) > 0
+    assert lib.lcmp_bin_workspace_bytes(10, 0, 6) == 0
+    assert lib.lcmp_bin_workspace_bytes(10, 16, 17) == 0            # more than 256 bins
+
+
+FAKE = 0x10000  # a non-null address that is never dereferenced: every call below fails validation
+
+
+def _compare(L, **kw):
+    args = dict(base=FAKE, tb=0, ld_base=100, cand=FAKE, tc=0, ld_cand=100, n=4, v=100, k=20,
+                flags=0, out=L.RowOut(), bd=None, ws=FAKE, ws_bytes=1 << 30, stream=None)
+    args.update(kw)
+    out = args["out"]
+    return L.lib().lcmp_compare_logits(args["base"], args["tb"], args["ld_base"], args["cand"],
+                                       args["tc"], args["ld_cand"], args["n"], args["v"], args["k"],
+                                       args["flags"], None if out is None else ctypes.byref(out),
+                                       args["bd"], args["ws"], args["ws_bytes"], args["stream"])
+
+
+def test_compare_argument_errors(L):
+    assert _compare(L, tb=7) == -2
+    assert _compare(L, tc=-1) == -2
+    assert _compare(L, n=-1) == -1
+    assert _compare(L, flags=2) == -1
+    assert _compare(L, out=None) == -1
+    assert _compare(L, v=1) == -3
+    assert _compare(L, k=0) == -3
+    assert _compare(L, k=65) == -3
+    assert _compare(L, ld_base=99) == -3
+    assert _compare(L, ld_cand=50) == -3
+    assert _compare(L, flags=1, bd=None) == -1          # bitwise stats need a destination
+    assert _compare(L, base=None) == -1
+    assert _compare(L, ws=None) == -4
+    assert _compare(L, ws_bytes=16) == -4
+    assert _compare(L, ws=FAKE + 4) == -1                # misaligned workspace
+    assert _compare(L, n=0) == 0                         # empty batch: nothing to do
+
+
+def test_bitdiff_argument_errors(L):
+    lib = L.lib()
+
+    def call(**kw):
+        a = dict(a=FAKE, ta=1, lda=10, b=FAKE, tb=1, ldb=10, rows=2, cols=10, out=FAKE, ws=FAKE,
+                 ws_bytes=1 << 20, stream=None)
+        a.update(kw)
+        return lib.lcmp_bitdiff(a["a"], a["ta"], a["lda"], a["b"], a["tb"], a["ldb"], a["rows"],
+                                a["cols"], a["out"], a["ws"], a["ws_bytes"], a["stream"])
+
+    assert call(ta=3) == -2
+    assert call(rows=-2) == -1
+    assert call(cols=0) == -3
+    assert call(lda=9) == -3
+    assert call(out=None) == -1
+    assert call(ws=None) == -4
+    assert call(ws_bytes=1) == -4
+    assert call(rows=0) == 0
+
+
+def test_bin_report_argument_errors(L):
+    lib = L.lib()
+
+    def call(edges=(0.1, 0.5, float("inf")), **kw):
+        e = (ctypes.c_double * len(edges))(*edges)
+        a = dict(margin=FAKE, flip=FAKE, kt=FAKE, kf=FAKE, status=None, group=None, ng=1, n=10,
+                 ne=len(edges), big=1.0, bins=FAKE, summ=FAKE, ws=FAKE, ws_bytes=1 << 20)
+        a.update(kw)
+        return lib.lcmp_bin_report(a["margin"], a["flip"], a["kt"], a["kf"], a["status"], a["group"],
+                                   a["ng"], a["n"], e, a["ne"], a["big"], a["bins"], a["summ"],
+                                   a["ws"], a["ws_bytes"], None)
+
+    assert call(edges=(0.5, 0.1)) == -6                    # not ascending
+    assert call(edges=(0.0, 1.0)) == -6                    # not positive
+    assert call(edges=(0.1, float("nan"))) == -6
+    assert call(edges=(0.1, 0.1)) == -6
+    assert call(ng=0) == -3
+    assert call(ng=300) == -3
+    assert call(ng=100, edges=(0.1, 0.5, 1.0)) == -3       # 300 bins
+    assert call(n=-1) == -1
+    assert call(bins=None) == -1
+    assert call(margin=None) == -1
+    assert call(ws=None) == -4
+    assert call(big=float("nan")) == -1
+
+
+def test_binding_rejects_unsupported_dtype(L):
+    """Only float32 and bfloat16 tensors are accepted."""
+    import torch
+    with pytest.raises(TypeError):
+        L.lcmp_compare_logits(torch.zeros(2, 4, dtype=torch.float64),
+                              torch.zeros(2, 4, dtype=torch.float64))

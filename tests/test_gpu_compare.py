@@ -1,0 +1,171 @@
+"""GPU parity of lcmp_compare_logits against the oracle (small and edge inputs)."""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from helpers import assert_bitdiff_equal, assert_compare_equal, gpu_compare
+
+pytestmark = pytest.mark.gpu
+
+
+def _case(msg):
+    print(f"[case] {msg}", flush=True)
+
+
+def test_tiny_workload_parity():
+    w = synth.WORKLOADS["tiny"]
+    _case("tiny 64x1024 f32/f32")
+    a, b = synth.tiny(w["seed"], 0, w["n"], w["v"])
+    g = gpu_compare(a, b, k=w["k"], with_bitdiff=True)
+    o = oracle.compare(a, b, k=w["k"])
+    assert_compare_equal(g, o)
+    assert_bitdiff_equal(g["bitdiff"], oracle.bitdiff(a, b))
+
+
+@pytest.mark.parametrize("v", [2, 3, 19, 20, 21, 511, 512, 513, 1023, 1024, 1025, 4097, 20001])
+@pytest.mark.parametrize("k", [1, 2, 20, 64])
+def test_ragged_vocab_sizes(v, k):
+    _case(f"ragged v={v} k={k}")
+    rng = np.random.default_rng(v * 100 + k)
+    n = 7
+    a = (1.5 * rng.standard_normal((n, v))).astype(np.float32)
+    b = (a + 0.05 * rng.standard_normal((n, v))).astype(np.float32)
+    g = gpu_compare(a, b, k=k, with_bitdiff=True)
+    assert_compare_equal(g, oracle.compare(a, b, k=k))
+    assert_bitdiff_equal(g["bitdiff"], oracle.bitdiff(a, b))
+
+
+@pytest.mark.parametrize("tb,tc", [("f32", "f32"), ("f32", "bf16"), ("bf16", "f32"),
+                                   ("bf16", "bf16")])
+def test_dtype_combinations(tb, tc):
+    _case(f"dtypes {tb}/{tc}")
+    rng = np.random.default_rng(5)
+    n, v = 33, 5000
+    x = (1.5 * rng.standard_normal((n, v))).astype(np.float32)
+    y = (x + 0.02 * rng.standard_normal((n, v))).astype(np.float32)
+
+    def conv(t, arr):
+        if t == "f32":
+            return arr
+        import torch
+        return torch.from_numpy(arr).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+
+    a, b = conv(tb, x), conv(tc, y)
+    g = gpu_compare(a, b, k=20, with_bitdiff=True)
+    assert_compare_equal(g, oracle.compare(a, b, k=20))
+    assert_bitdiff_equal(g["bitdiff"], oracle.bitdiff(a, b))
+
+
+def test_ties_and_signed_zeros():
+    _case("ties")
+    rng = np.random.default_rng(9)
+    n, v = 12, 3000
+    a = rng.integers(-3, 3, (n, v)).astype(np.float32)  # heavy ties everywhere
+    b = rng.integers(-3, 3, (n, v)).astype(np.float32)
+    a[0] = 0.0  # all equal
+    a[1] = -0.0
+    a[1, ::2] = 0.0  # +0 / -0 interleaved: equal values, index order decides
+    b[2] = 5.0  # candidate all tied
+    g = gpu_compare(a, b, k=64)
+    assert_compare_equal(g, oracle.compare(a, b, k=64))
+
+
+@pytest.mark.parametrize("order", ["ascending", "descending", "clustered"])
+def test_adversarial_orders_for_topk(order):
+    _case(f"order {order}")
+    rng = np.random.default_rng(3)
+    n, v = 4, 151936
+    base = np.sort(rng.standard_normal((n, v)).astype(np.float32), axis=1)
+    if order == "descending":
+        base = base[:, ::-1].copy()
+    elif order == "clustered":
+        base = rng.standard_normal((n, v)).astype(np.float32)
+        base[:, 70000:70100] += 20.0  # the whole top sits in one lane's neighbourhood
+    cand = (base + 0.01 * rng.standard_normal((n, v))).astype(np.float32)
+    g = gpu_compare(base, cand, k=64)
+    assert_compare_equal(g, oracle.compare(base, cand, k=64))
+
+
+def test_special_values_and_flags():
+    _case("special values")
+    v = 2000
+    a = np.zeros((8, v), np.float32)
+    b = np.zeros((8, v), np.float32)
+    rng = np.random.default_rng(1)
+    a[:] = rng.standard_normal((8, v))
+    b[:] = a + 0.01 * rng.standard_normal((8, v))
+    a[0, 17] = np.nan                      # NONFINITE
+    b[1, 1999] = np.inf                    # NONFINITE
+    a[2, :] = -np.inf                      # EMPTY
+    b[3, 10] = -np.inf                     # q = 0 where p > 0: infinite KL
+    a[4, 100:] = -np.inf                   # baseline excludes most tokens
+    a[5, :1990] = -np.inf                  # ten finite tokens only
+    b[5, :] = -np.inf
+    b[5, 1990:] = 1.0
+    a[6] = 1e30                            # huge equal logits
+    b[6] = 1e30
+    b[7, :] = a[7] + 3.0                   # large deltas (exact shift)
+    b[7, 5] = a[7, 5] - 4.0
+    g = gpu_compare(a, b, k=20, with_bitdiff=True)
+    o = oracle.compare(a, b, k=20)
+    assert list(o["status"]) == [1, 1, 2, 0, 0, 0, 0, 0]
+    assert_compare_equal(g, o)
+    assert_bitdiff_equal(g["bitdiff"], oracle.bitdiff(a, b))
+
+
+def test_identical_inputs_exact_zero():
+    _case("identical")
+    a, _ = synth.tiny(synth.SEED_BASE, 0, 16, 1024)
+    g = gpu_compare(a, a.copy(), k=20, with_bitdiff=True)
+    assert np.all(g["kl_full"] == 0.0) and np.all(g["kl_topk"] == 0.0)
+    assert np.all(g["flip"] == 0)
+    assert np.all(g["bitdiff"]["ndiff"] == 0) and np.all(g["bitdiff"]["first_diff"] == -1)
+
+
+def test_leading_dimension_and_unaligned_rows():
+    import torch
+    import logit_distribution_diffing_amd as L
+    _case("ld > v, unaligned")
+    rng = np.random.default_rng(4)
+    n, v, ld = 9, 3001, 3009
+    full_a = (1.5 * rng.standard_normal((n, ld))).astype(np.float32)
+    full_b = (full_a + 0.03 * rng.standard_normal((n, ld))).astype(np.float32)
+    o = oracle.compare(full_a[:, :v].copy(), full_b[:, :v].copy(), k=20)
+    ta = torch.from_numpy(full_a).cuda()
+    tb = torch.from_numpy(full_b).cuda()
+    out = L.lcmp_compare_logits(ta, tb, k=20, v=v)  # ld = 3009: rows not 16-byte aligned
+    g = {kk: vv.cpu().numpy() for kk, vv in out.items()}
+    assert_compare_equal(g, o)
+    # base pointer one element past an aligned address
+    ta2 = torch.from_numpy(np.ascontiguousarray(full_a[:, 1:v + 1])).cuda()
+    flat = torch.empty(n * v + 1, dtype=torch.float32, device="cuda")
+    flat[1:].copy_(ta2.reshape(-1))
+    tb2 = torch.from_numpy(np.ascontiguousarray(full_b[:, 1:v + 1])).cuda()
+    out = L.lcmp_compare_logits(flat[1:].view(n, v), tb2, k=20)
+    g = {kk: vv.cpu().numpy() for kk, vv in out.items()}
+    assert_compare_equal(g, oracle.compare(full_a[:, 1:v + 1].copy(), full_b[:, 1:v + 1].copy(), k=20))
+
+
+def test_single_row_and_empty_batch():
+    import torch
+    import logit_distribution_diffing_amd as L
+    _case("n=1, n=0")
+    a, b = synth.segment(synth.SEED_BASE + 1, 0, 1, 151936)
+    g = gpu_compare(a, b, k=20, with_bitdiff=True)
+    assert_compare_equal(g, oracle.compare(a, b, k=20))
+    e = torch.empty((0, 100), dtype=torch.float32, device="cuda")
+    out = L.lcmp_compare_logits(e, e, k=20)
+    assert out["kl_full"].numel() == 0
+
+
+def test_repeated_runs_bit_identical():
+    _case("determinism")
+    a, b = synth.segment(synth.SEED_BASE + 1, 0, 64, 151936)
+    g1 = gpu_compare(a, b, k=20, with_bitdiff=True)
+    g2 = gpu_compare(a, b, k=20, with_bitdiff=True)
+    for key in g1:
+        if key == "bitdiff":
+            assert g1[key].tobytes() == g2[key].tobytes()
+        else:
+            assert np.array_equal(g1[key].view(np.uint8), g2[key].view(np.uint8)), key
