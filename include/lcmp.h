@@ -161,6 +161,17 @@ int lcmp_compare_logits(const void *base, int tb, int64_t ld_base, const void *c
                         const lcmp_row_out *out, lcmp_bitdiff_row *bd, void *workspace,
                         size_t ws_bytes, void *stream);
 
+/*
+ * Instrumented form of lcmp_compare_logits for measuring the streaming pass:
+ * when ev_before / ev_after (hipEvent_t) are non-NULL they are recorded on
+ * `stream` immediately before and after the streaming kernel, so their
+ * elapsed time is that kernel's duration.  Everything else is identical.
+ */
+int lcmp_compare_logits_timed(const void *base, int tb, int64_t ld_base, const void *cand, int tc,
+                              int64_t ld_cand, int64_t n, int64_t v, int k, uint32_t flags,
+                              const lcmp_row_out *out, lcmp_bitdiff_row *bd, void *workspace,
+                              size_t ws_bytes, void *stream, void *ev_before, void *ev_after);
+
 /* ---------------------------------------------------------------- bitwise */
 
 size_t lcmp_bitdiff_workspace_bytes(int64_t rows, int64_t cols);

@@ -29,8 +29,8 @@ STATUS_NAMES = {0: "LCMP_OK", -1: "LCMP_EINVAL", -2: "LCMP_EDTYPE", -3: "LCMP_ES
                 -4: "LCMP_EWORKSPACE", -5: "LCMP_EHIP", -6: "LCMP_EEDGES"}
 
 EXPORTED = ("lcmp_abi_version", "lcmp_strerror", "lcmp_compare_workspace_bytes",
-            "lcmp_compare_logits", "lcmp_bitdiff_workspace_bytes", "lcmp_bitdiff",
-            "lcmp_bin_workspace_bytes", "lcmp_bin_report")
+            "lcmp_compare_logits", "lcmp_compare_logits_timed", "lcmp_bitdiff_workspace_bytes",
+            "lcmp_bitdiff", "lcmp_bin_workspace_bytes", "lcmp_bin_report")
 
 
 class LcmpError(RuntimeError):
@@ -71,6 +71,8 @@ def _load():
     lib.lcmp_compare_logits.restype = ci
     lib.lcmp_compare_logits.argtypes = [vp, ci, i64, vp, ci, i64, i64, i64, ci, u32,
                                         ctypes.POINTER(RowOut), vp, vp, sz, vp]
+    lib.lcmp_compare_logits_timed.restype = ci
+    lib.lcmp_compare_logits_timed.argtypes = lib.lcmp_compare_logits.argtypes + [vp, vp]
     lib.lcmp_bitdiff_workspace_bytes.restype = sz
     lib.lcmp_bitdiff_workspace_bytes.argtypes = [i64, i64]
     lib.lcmp_bitdiff.restype = ci
@@ -142,12 +144,14 @@ def alloc_compare_outputs(n: int, k: int, device, with_bitdiff: bool = False) ->
 
 def lcmp_compare_logits(base: torch.Tensor, cand: torch.Tensor, k: int = 20,
                         with_bitdiff: bool = False, v: int | None = None, out: dict | None = None,
-                        workspace: torch.Tensor | None = None, stream=None) -> dict:
+                        workspace: torch.Tensor | None = None, stream=None,
+                        events: tuple | None = None) -> dict:
     """Compare baseline and candidate logits row by row (device tensors [n, >=v]).
 
     Returns a dict of device tensors (kl_topk, kl_full, margin, lse_base, lse_cand,
     top1_base, top2_base, top1_cand, flip, status, topk_idx and, with
-    with_bitdiff, a raw [n, 88] uint8 `bitdiff` record tensor; see unpack_bitdiff)."""
+    with_bitdiff, a raw [n, 88] uint8 `bitdiff` record tensor; see unpack_bitdiff).
+    `events`, a pair of raw hipEvent_t handles, selects lcmp_compare_logits_timed."""
     n = base.size(0)
     if cand.size(0) != n:
         raise ValueError("baseline and candidate need the same number of rows")
@@ -163,10 +167,13 @@ def lcmp_compare_logits(base: torch.Tensor, cand: torch.Tensor, k: int = 20,
     ro = RowOut(*[_ptr(out.get(f)) for f in (
         "kl_topk", "kl_full", "margin", "lse_base", "lse_cand", "top1_base", "top2_base",
         "top1_cand", "flip", "status", "topk_idx")])
-    rc = _lib.lcmp_compare_logits(
-        base.data_ptr(), _dtype_code(base), _ld(base), cand.data_ptr(), _dtype_code(cand),
-        _ld(cand), n, v, k, flags, ctypes.byref(ro), _ptr(out.get("bitdiff")),
-        workspace.data_ptr(), workspace.numel(), _stream(stream))
+    args = (base.data_ptr(), _dtype_code(base), _ld(base), cand.data_ptr(), _dtype_code(cand),
+            _ld(cand), n, v, k, flags, ctypes.byref(ro), _ptr(out.get("bitdiff")),
+            workspace.data_ptr(), workspace.numel(), _stream(stream))
+    if events is None:
+        rc = _lib.lcmp_compare_logits(*args)
+    else:
+        rc = _lib.lcmp_compare_logits_timed(*args, events[0], events[1])
     _check(rc, "lcmp_compare_logits")
     return out
 
@@ -192,15 +199,19 @@ def lcmp_bitdiff(a: torch.Tensor, b: torch.Tensor, cols: int | None = None,
 
 
 def lcmp_bin_report(margin, flip, kl_topk, kl_full, edges, status=None, group=None,
-                    n_groups: int = 1, big_margin: float = 1.0, workspace=None, stream=None):
+                    n_groups: int = 1, big_margin: float = 1.0, workspace=None, stream=None,
+                    bins=None, summary=None):
     """Margin-bin report; returns raw (bins [n_groups*n_edges, 56] uint8,
     summary [n_groups, 24] uint8) device tensors (see unpack_bins)."""
     n = margin.numel()
     edges = [float(e) for e in edges]
     ne = len(edges)
     dev = margin.device
-    bins = torch.empty((n_groups * ne, BIN_BYTES), dtype=torch.uint8, device=dev)
-    summ = torch.empty((n_groups, GROUP_SUMMARY_BYTES), dtype=torch.uint8, device=dev)
+    if bins is None:
+        bins = torch.empty((n_groups * ne, BIN_BYTES), dtype=torch.uint8, device=dev)
+    if summary is None:
+        summary = torch.empty((n_groups, GROUP_SUMMARY_BYTES), dtype=torch.uint8, device=dev)
+    summ = summary
     ws_bytes = int(_lib.lcmp_bin_workspace_bytes(n, n_groups, ne))
     if ws_bytes == 0:
         raise LcmpError(-3, "lcmp_bin_workspace_bytes")

@@ -18,7 +18,6 @@ constexpr int kBlock = 256;
 constexpr int kWavesPerBlock = kBlock / kWave;
 constexpr int kMaxK = 64;
 constexpr int kSpan = kWave * 8;       // elements one wave covers per step (8 per lane)
-constexpr int kCap = 256;              // per-wave top-k candidate buffer (entries)
 constexpr int kMaxChunks = 64;         // chunks per row (one lane of the merge each)
 
 // exp(x) is evaluated as exp2(x * kL2E - r2) with a wave-uniform reference r2

@@ -17,6 +17,11 @@
 // fp32, lane l takes elements [4l, 4l+4) and [256+4l, 256+4l+4), so each load
 // instruction of the wave covers one contiguous run; when both sides are bf16,
 // lane l takes [8l, 8l+8) with one 16-byte load per side.
+//
+// Code shape: the per-step work is instantiated once for the streaming loop
+// and once for the ragged last step.  Rare work (moving the exp2 reference,
+// exact treatment of special values, top-k buffer flushes, argmax updates)
+// sits behind wave-uniform branches so the common step is straight-line code.
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -24,7 +29,18 @@
 
 namespace lcmp {
 
-constexpr int kFlushAt = 192;  // flush the candidate buffer once it holds this many
+// The candidate buffer holds kCapW = kCapPerLane * 64 entries (value, index).
+// A step appends at most 8 entries per lane whose group maximum passes the
+// threshold; when that bound could overflow the buffer it is first reduced to
+// kint <= 64 entries (64 + 512 <= kCapW), and after a step it is reduced
+// whenever it holds more than kFlushAt.
+constexpr int kCapPerLane = 9;
+constexpr int kCapW = kCapPerLane * kWave;  // 576
+constexpr int kFlushAt = 256;
+// threshold index meaning "no index bound yet": every element at or above
+// the threshold value passes
+constexpr int kTauOpen = 0x7fffffff;
+constexpr int kTauLaneMax = 0x7ffffffe;  // same, after the lane-maxima bound was taken
 
 struct WaveState {
   // softmax sums (per lane, double across 8-element runs)
@@ -33,18 +49,16 @@ struct WaveState {
   // (|r2h| >= 2^28) that one float cannot hold the reference within a unit;
   // such chunks take the exact path throughout
   float r2h, r2l, gate;
-  bool huge;
   // candidate argmax (uniform)
   float bmax;
   int bidx;
   // top-k threshold key (uniform) and buffer fill
   float tau_a;
   int tau_i, cnt;
-  bool tau_set;
   // counters (per lane)
   int n_bad, n_ainf, n_binf, n_qzero;
   // bitwise statistics
-  int64_t ndiff, first;  // uniform
+  int ndiff, first;  // uniform (a chunk holds fewer than 2^31 elements)
   uint32_t max_ulp;
   float max_abs;
   double max_abs_d, sab, ssd, ssb;
@@ -56,82 +70,105 @@ __device__ __forceinline__ void wave_fence() {
   __builtin_amdgcn_wave_barrier();
 }
 
+// v_max3_f32 without the NaN canonicalisation the compiler adds around fmaxf
+// on loaded values (a NaN in a row flags it through the sums anyway).
+__device__ __forceinline__ float max3f(float a, float b, float c) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
+__device__ __forceinline__ float max3abs(float a, float b, float c) {
+  float r;
+  asm("v_max3_f32 %0, |%1|, |%2|, |%3|" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
+__device__ __forceinline__ float max8(const float (&x)[8]) {
+  return max3f(max3f(max3f(x[0], x[1], x[2]), x[3], x[4]), max3f(x[5], x[6], x[7]), x[7]);
+}
+__device__ __forceinline__ float max8abs(const float (&x)[8]) {
+  return max3abs(max3abs(max3abs(x[0], x[1], x[2]), x[3], x[4]), max3abs(x[5], x[6], x[7]), x[7]);
+}
+__device__ __forceinline__ uint32_t sad_u32(uint32_t a, uint32_t b) {
+  uint32_t r;
+  asm("v_sad_u32 %0, %1, %2, 0" : "=v"(r) : "v"(a), "v"(b));
+  return r;
+}
+
 // ---------------------------------------------------------------- top-k buffer
 
-// Reduce the wave's candidate buffer to exactly `kint` entries (the largest
-// keys: value descending, index ascending) and raise the threshold to the
-// kint-th key.  Called with the whole wave active; cnt > kint.
-__device__ void flush_candidates(float *ba, float *bb, int *bi, WaveState &st, int kint) {
+// Reduce the wave's candidate buffer (cnt > kint entries of value ba[] and
+// index bi[] in LDS) to exactly the kint largest keys -- value descending,
+// index ascending -- and raise the threshold to the kint-th key.  Whole wave,
+// uniform control flow.  Written for size, not speed: it runs rarely.
+__device__ __forceinline__ void flush_candidates(float *ba, int *bi, WaveState &st, int kint) {
   wave_fence();
   const int lane = lane_id();
-  const int per = (st.cnt + kWave - 1) / kWave;  // 1..4, uniform
-  float va[4], vb[4];
-  int ix[4];
-  uint32_t key[4];
-  bool ok[4];
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const int e = lane + kWave * q;
-    ok[q] = q < per && e < st.cnt;
-    va[q] = ok[q] ? ba[e] : 0.0f;
-    vb[q] = ok[q] ? bb[e] : 0.0f;
-    ix[q] = ok[q] ? bi[e] : 0;
-    key[q] = rank_key(va[q]);
-  }
+  const int cnt = st.cnt;
+  const int per = (cnt + kWave - 1) / kWave;
   // kint-th largest value key, one bit at a time from the top
   uint32_t T = 0;
+#pragma unroll 1
   for (int bit = 31; bit >= 0; --bit) {
     const uint32_t c = T | (1u << bit);
     int n = 0;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) n += __popcll(ballot(ok[q] && key[q] >= c));
+#pragma unroll 1
+    for (int q = 0; q < per; ++q) {
+      const int e = lane + kWave * q;
+      n += __popcll(ballot(e < cnt && rank_key(ba[e]) >= c));
+    }
     if (n >= kint) T = c;
   }
   int ngt = 0, neq = 0;
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    ngt += __popcll(ballot(ok[q] && key[q] > T));
-    neq += __popcll(ballot(ok[q] && key[q] == T));
+#pragma unroll 1
+  for (int q = 0; q < per; ++q) {
+    const int e = lane + kWave * q;
+    const uint32_t k = e < cnt ? rank_key(ba[e]) : 0u;
+    ngt += __popcll(ballot(e < cnt && k > T));
+    neq += __popcll(ballot(e < cnt && k == T));
   }
   const int need = kint - ngt;  // >= 1 entries taken among the ties at T
   int isel = 0x7fffffff;
   if (neq > need) {
     // need-th smallest index among the ties
     uint32_t I = 0;
+#pragma unroll 1
     for (int bit = 30; bit >= 0; --bit) {
       const uint32_t c = I | (1u << bit);
       int n = 0;
-#pragma unroll
-      for (int q = 0; q < 4; ++q) n += __popcll(ballot(ok[q] && key[q] == T && (uint32_t)ix[q] < c));
+#pragma unroll 1
+      for (int q = 0; q < per; ++q) {
+        const int e = lane + kWave * q;
+        n += __popcll(ballot(e < cnt && rank_key(ba[e]) == T && (uint32_t)bi[e] < c));
+      }
       if (n < need) I = c;
     }
     isel = (int)I;
   }
-  bool keep[4];
-  int tie_hi = -1;
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    keep[q] = ok[q] && (key[q] > T || (key[q] == T && ix[q] <= isel));
-    if (keep[q] && key[q] == T) tie_hi = max(tie_hi, ix[q]);
-  }
-  wave_fence();
-  int fill = 0;
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const uint64_t m = ballot(keep[q]);
-    const int pos = fill + prefix_count(m);
-    if (keep[q]) {
-      ba[pos] = va[q];
-      bb[pos] = vb[q];
-      bi[pos] = ix[q];
+  // in-place compaction in entry order: every entry of round q is read before
+  // any lane writes, and round q writes only below 64 * (q + 1)
+  int fill = 0, tie_hi = -1;
+#pragma unroll 1
+  for (int q = 0; q < per; ++q) {
+    const int e = lane + kWave * q;
+    const bool in = e < cnt;
+    const float va = in ? ba[e] : 0.0f;
+    const int ix = in ? bi[e] : 0;
+    const uint32_t k = rank_key(va);
+    const bool keep = in && (k > T || (k == T && ix <= isel));
+    if (keep && k == T) tie_hi = max(tie_hi, ix);
+    const uint64_t m = ballot(keep);
+    wave_fence();
+    if (keep) {
+      const int pos = fill + prefix_count(m);
+      ba[pos] = va;
+      bi[pos] = ix;
     }
     fill += __popcll(m);
+    wave_fence();
   }
-  wave_fence();
   st.cnt = fill;
   st.tau_a = rank_key_inv(T);
-  st.tau_i = wave_max(tie_hi);
-  st.tau_set = true;
+  st.tau_i = uniform(wave_max(tie_hi));
 }
 
 // ---------------------------------------------------------------- element mapping
@@ -143,75 +180,76 @@ __device__ __forceinline__ int lane_offset(int lane, int j) {
 }
 
 template <int T>
-__device__ __forceinline__ uint32_t load_pattern(const char *row, int64_t i) {
+__device__ __forceinline__ uint32_t load_pattern(const char *row, int i) {
   if (T == 1) return (uint32_t)(*(const uint16_t *)(row + 2 * i)) << 16;
   return *(const uint32_t *)(row + 4 * i);
 }
 
-// Raw registers of one wave step (one lane's 8 elements of each side).
-template <int TA, int TB>
-struct Raw {
-  static constexpr bool MAPB = (TA == 1 && TB == 1);
-  u32x4 a0, a1, b0, b1;  // fp32: two 16-byte pieces; bf16 map A: .xy used; map B: a0 only
-};
-
-template <int TA, int TB>
-__device__ __forceinline__ void load_vec(Raw<TA, TB> &r, const char *ra, const char *rb, int64_t base,
-                                         int lane) {
-  if (Raw<TA, TB>::MAPB) {
-    r.a0 = __builtin_nontemporal_load((const u32x4 *)(ra + 2 * (base + 8 * lane)));
-    r.b0 = __builtin_nontemporal_load((const u32x4 *)(rb + 2 * (base + 8 * lane)));
-    return;
-  }
-  const int64_t o0 = base + 4 * lane, o1 = base + 256 + 4 * lane;
-  if (TA == 0) {
-    r.a0 = __builtin_nontemporal_load((const u32x4 *)(ra + 4 * o0));
-    r.a1 = __builtin_nontemporal_load((const u32x4 *)(ra + 4 * o1));
-  } else {
-    u32x2 w0 = __builtin_nontemporal_load((const u32x2 *)(ra + 2 * o0));
-    u32x2 w1 = __builtin_nontemporal_load((const u32x2 *)(ra + 2 * o1));
-    r.a0 = u32x4{w0.x, w0.y, 0u, 0u};
-    r.a1 = u32x4{w1.x, w1.y, 0u, 0u};
-  }
-  if (TB == 0) {
-    r.b0 = __builtin_nontemporal_load((const u32x4 *)(rb + 4 * o0));
-    r.b1 = __builtin_nontemporal_load((const u32x4 *)(rb + 4 * o1));
-  } else {
-    u32x2 w0 = __builtin_nontemporal_load((const u32x2 *)(rb + 2 * o0));
-    u32x2 w1 = __builtin_nontemporal_load((const u32x2 *)(rb + 2 * o1));
-    r.b0 = u32x4{w0.x, w0.y, 0u, 0u};
-    r.b1 = u32x4{w1.x, w1.y, 0u, 0u};
-  }
-}
-
-// fp32-space bit patterns of the 8 elements of one side
+// Raw registers of one wave step: one lane's 8 elements of each side, as
+// 16-byte (fp32, or bf16 when both sides are bf16) or 8-byte (bf16) pieces.
+// `p` is the wave's step pointer; each lane adds its own byte offset.
 template <int T, bool MAPB>
-__device__ __forceinline__ void decode(const u32x4 &p0, const u32x4 &p1, uint32_t (&u)[8]) {
-  if (MAPB) {
-    u[0] = p0.x << 16; u[1] = p0.x & 0xffff0000u;
-    u[2] = p0.y << 16; u[3] = p0.y & 0xffff0000u;
-    u[4] = p0.z << 16; u[5] = p0.z & 0xffff0000u;
-    u[6] = p0.w << 16; u[7] = p0.w & 0xffff0000u;
-  } else if (T == 0) {
+struct Side;
+template <bool MAPB>
+struct Side<0, MAPB> {
+  u32x4 p0, p1;
+  __device__ __forceinline__ void load(const char *p, uint32_t lane) {
+    p0 = __builtin_nontemporal_load((const u32x4 *)(p + 16u * lane));
+    p1 = __builtin_nontemporal_load((const u32x4 *)(p + 1024u + 16u * lane));
+  }
+  __device__ __forceinline__ void decode(uint32_t (&u)[8]) const {
     u[0] = p0.x; u[1] = p0.y; u[2] = p0.z; u[3] = p0.w;
     u[4] = p1.x; u[5] = p1.y; u[6] = p1.z; u[7] = p1.w;
-  } else {
+  }
+};
+template <>
+struct Side<1, false> {
+  u32x2 p0, p1;
+  __device__ __forceinline__ void load(const char *p, uint32_t lane) {
+    p0 = __builtin_nontemporal_load((const u32x2 *)(p + 8u * lane));
+    p1 = __builtin_nontemporal_load((const u32x2 *)(p + 512u + 8u * lane));
+  }
+  __device__ __forceinline__ void decode(uint32_t (&u)[8]) const {
     u[0] = p0.x << 16; u[1] = p0.x & 0xffff0000u;
     u[2] = p0.y << 16; u[3] = p0.y & 0xffff0000u;
     u[4] = p1.x << 16; u[5] = p1.x & 0xffff0000u;
     u[6] = p1.y << 16; u[7] = p1.y & 0xffff0000u;
   }
-}
+};
+template <>
+struct Side<1, true> {
+  u32x4 p0;
+  __device__ __forceinline__ void load(const char *p, uint32_t lane) {
+    p0 = __builtin_nontemporal_load((const u32x4 *)(p + 16u * lane));
+  }
+  __device__ __forceinline__ void decode(uint32_t (&u)[8]) const {
+    u[0] = p0.x << 16; u[1] = p0.x & 0xffff0000u;
+    u[2] = p0.y << 16; u[3] = p0.y & 0xffff0000u;
+    u[4] = p0.z << 16; u[5] = p0.z & 0xffff0000u;
+    u[6] = p0.w << 16; u[7] = p0.w & 0xffff0000u;
+  }
+};
+
+template <int TA, int TB>
+struct Raw {
+  static constexpr bool MAPB = (TA == 1 && TB == 1);
+  Side<TA, MAPB> a;
+  Side<TB, MAPB> b;
+  __device__ __forceinline__ void load(const char *pa, const char *pb, uint32_t lane) {
+    a.load(pa, lane);
+    b.load(pb, lane);
+  }
+};
 
 // Bounds-checked element loads (ragged tail, unaligned rows); positions past
 // `hi` read as -inf on both sides and are masked out of every statistic.
 template <int TA, int TB, bool MAPB>
 __device__ __forceinline__ uint32_t load_checked(uint32_t (&ua)[8], uint32_t (&ub)[8], const char *ra,
-                                                 const char *rb, int64_t base, int64_t hi, int lane) {
+                                                 const char *rb, int base, int hi, int lane) {
   uint32_t valid = 0;
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
-    const int64_t i = base + lane_offset<MAPB>(lane, j);
+    const int i = base + lane_offset<MAPB>(lane, j);
     if (i < hi) {
       ua[j] = load_pattern<TA>(ra, i);
       ub[j] = load_pattern<TB>(rb, i);
@@ -224,65 +262,70 @@ __device__ __forceinline__ uint32_t load_checked(uint32_t (&ua)[8], uint32_t (&u
   return valid;
 }
 
+// ---------------------------------------------------------------- rare work
+
+// Move the exp2 reference when a logit outgrows it (rare after the first step).
+__device__ __forceinline__ void rescale(WaveState &st, float gm) {
+  const float wm = uniform(wave_max(gm));
+  const float nh = wm * kL2E;
+  const bool huge = fabsf(nh) >= 268435456.0f && isfinite(nh);
+  const float nl = huge ? fmaf(wm, kL2E, -nh) : 0.0f;
+  if (st.r2h > -INFINITY) {
+    const double sc = exp2(((double)st.r2h + (double)st.r2l) - ((double)nh + (double)nl));
+    st.s *= sc;
+    st.d *= sc;
+    st.f *= sc;
+  }
+  st.r2h = nh;
+  st.r2l = nl;
+  st.gate = (nh + kRescaleLog2) * (1.0f / kL2E);
+}
+
 // ---------------------------------------------------------------- one wave step
 
 template <bool CMP, bool BITS, bool W16, bool MAPB>
 __device__ __forceinline__ void process_step(const uint32_t (&ua)[8], const uint32_t (&ub)[8],
-                                             uint32_t valid, bool force_slow, int64_t base,
-                                             int lane, int kint, WaveState &st, float *ba,
-                                             float *bb, int *bi) {
+                                             uint32_t valid, bool tail, int base, int lane,
+                                             int kint, WaveState &st, float *ba, int *bi) {
   float xa[8], xb[8];
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
     xa[j] = __uint_as_float(ua[j]);
     xb[j] = __uint_as_float(ub[j]);
   }
-  const float ga = fmaxf(fmaxf(fmaxf(xa[0], xa[1]), fmaxf(xa[2], xa[3])),
-                         fmaxf(fmaxf(xa[4], xa[5]), fmaxf(xa[6], xa[7])));
-  const float gb = fmaxf(fmaxf(fmaxf(xb[0], xb[1]), fmaxf(xb[2], xb[3])),
-                         fmaxf(fmaxf(xb[4], xb[5]), fmaxf(xb[6], xb[7])));
-
+  float ga = 0.0f, gb = 0.0f;
   if (CMP) {
-    // move the exp2 reference when a logit outgrows it (rare after the first step)
-    const float gm = fmaxf(ga, gb);
-    if (ballot(gm > st.gate)) {
-      const float wm = uniform(wave_max(gm));
-      const float nh = wm * kL2E;
-      const bool huge = fabsf(nh) >= 268435456.0f && isfinite(nh);
-      const float nl = huge ? fmaf(wm, kL2E, -nh) : 0.0f;
-      if (st.r2h > -INFINITY) {
-        const double sc = exp2(((double)st.r2h + (double)st.r2l) - ((double)nh + (double)nl));
-        st.s *= sc;
-        st.d *= sc;
-        st.f *= sc;
-      }
-      st.r2h = nh;
-      st.r2l = nl;
-      st.huge = st.huge || huge;
-      st.gate = (nh + kRescaleLog2) * (1.0f / kL2E);
-    }
+    ga = max8(xa);
+    gb = max8(xb);
+    const float gm = max3f(ga, gb, gb);
+    if (ballot(gm > st.gate)) rescale(st, gm);
   }
 
   // fast path: every element finite, |delta| <= 1/8
   float d[8];
 #pragma unroll
   for (int j = 0; j < 8; ++j) d[j] = xa[j] - xb[j];
+  const float dmax = max8abs(d);
   float sg = 0.0f, dg = 0.0f, fg = 0.0f;
-  float sab = 0.0f, ssd = 0.0f, ssb = 0.0f, dmax = 0.0f;
+  float sab = 0.0f, ssd = 0.0f, ssb = 0.0f;
   if (CMP) {
-    float e[8], ed[8], ef[8];
+    float s0 = 0.0f, s1 = 0.0f, d0 = 0.0f, d1 = 0.0f, f0 = 0.0f, f1 = 0.0f;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      e[j] = __builtin_amdgcn_exp2f(fmaf(xa[j], kL2E, -st.r2h));
-      ed[j] = e[j] * d[j];
-      ef[j] = (ed[j] * d[j]) * phi_over_d2(d[j]);
+    for (int j = 0; j < 8; j += 2) {
+      const float e0 = __builtin_amdgcn_exp2f(fmaf(xa[j], kL2E, -st.r2h));
+      const float e1 = __builtin_amdgcn_exp2f(fmaf(xa[j + 1], kL2E, -st.r2h));
+      const float ed0 = e0 * d[j], ed1 = e1 * d[j + 1];
+      s0 += e0;
+      s1 += e1;
+      d0 += ed0;
+      d1 += ed1;
+      f0 = fmaf(ed0 * d[j], phi_over_d2(d[j]), f0);
+      f1 = fmaf(ed1 * d[j + 1], phi_over_d2(d[j + 1]), f1);
     }
-    sg = ((e[0] + e[1]) + (e[2] + e[3])) + ((e[4] + e[5]) + (e[6] + e[7]));
-    dg = ((ed[0] + ed[1]) + (ed[2] + ed[3])) + ((ed[4] + ed[5]) + (ed[6] + ed[7]));
-    fg = ((ef[0] + ef[1]) + (ef[2] + ef[3])) + ((ef[4] + ef[5]) + (ef[6] + ef[7]));
+    sg = s0 + s1;
+    dg = d0 + d1;
+    fg = f0 + f1;
   }
-#pragma unroll
-  for (int j = 0; j < 8; ++j) dmax = fmaxf(dmax, fabsf(d[j]));
   if (BITS) {
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
@@ -291,8 +334,8 @@ __device__ __forceinline__ void process_step(const uint32_t (&ua)[8], const uint
       ssb = fmaf(xa[j], xa[j], ssb);
     }
   }
-  bool ok = !force_slow;
-  if (CMP) ok = ok && !st.huge && (dmax <= kPolyMax) && (dg == dg);
+  bool ok = !tail;
+  if (CMP) ok = ok && st.r2l == 0.0f && (dmax <= kPolyMax) && (dg == dg);
   if (BITS) ok = ok && isfinite(sab) && isfinite(ssd) && isfinite(ssb);
 
   if (ok) {
@@ -305,10 +348,11 @@ __device__ __forceinline__ void process_step(const uint32_t (&ua)[8], const uint
       st.sab += (double)sab;
       st.ssd += (double)ssd;
       st.ssb += (double)ssb;
-      st.max_abs = fmaxf(st.max_abs, dmax);
+      st.max_abs = max3f(st.max_abs, dmax, dmax);
     }
   } else {
-    // exact element-by-element path: special values and large differences
+    // exact element-by-element path: special values, large differences,
+    // huge logits, ragged tails
     float s2 = 0.0f, d2 = 0.0f, f2 = 0.0f;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
@@ -363,48 +407,38 @@ __device__ __forceinline__ void process_step(const uint32_t (&ua)[8], const uint
     }
   }
 
-  int idx[8];
-#pragma unroll
-  for (int j = 0; j < 8; ++j) idx[j] = (int)(base + lane_offset<MAPB>(lane, j));
-
   if (CMP) {
-    // threshold from the first full step: the kint-th largest of the 64 lane maxima
-    // (a full step has all 8 elements of every lane valid; the test is wave-uniform)
-    if (!st.tau_set && !force_slow) {
-      const uint32_t kg = rank_key(ga);
-      uint32_t T = 0;
-      for (int bit = 31; bit >= 0; --bit) {
-        const uint32_t c = T | (1u << bit);
-        if (__popcll(ballot(kg >= c)) >= kint) T = c;
-      }
-      st.tau_a = rank_key_inv(T);
-      st.tau_i = 0x7fffffff;
-      st.tau_set = true;
-    }
     // top-k candidates: keys above the threshold go to the LDS buffer
     if (ballot(ga >= st.tau_a)) {
+      // first full step: the kint-th largest of the 64 lane maxima bounds the
+      // chunk's kint-th key from below
+      if (st.tau_i == kTauOpen && !tail) {
+        const uint32_t kg = rank_key(ga);
+        uint32_t T = 0;
+#pragma unroll 1
+        for (int bit = 31; bit >= 0; --bit) {
+          const uint32_t c = T | (1u << bit);
+          if (__popcll(ballot(kg >= c)) >= kint) T = c;
+        }
+        st.tau_a = rank_key_inv(T);
+        st.tau_i = kTauLaneMax;
+      }
+      // at most 8 appends per passing lane: make room first if that could overflow
+      if (st.cnt + 8 * __popcll(ballot(ga >= st.tau_a)) > kCapW) flush_candidates(ba, bi, st, kint);
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        bool pass = ((valid >> j) & 1u) &&
-                    (xa[j] > st.tau_a || (xa[j] == st.tau_a && idx[j] < st.tau_i));
-        uint64_t m = ballot(pass);
-        if (!m) continue;
-        if (st.cnt + __popcll(m) > kCap) {
-          flush_candidates(ba, bb, bi, st, kint);
-          pass = ((valid >> j) & 1u) &&
-                 (xa[j] > st.tau_a || (xa[j] == st.tau_a && idx[j] < st.tau_i));
-          m = ballot(pass);
-          if (!m) continue;
-        }
-        const int pos = st.cnt + prefix_count(m);
+        const int idx = base + lane_offset<MAPB>(lane, j);
+        const bool pass = ((valid >> j) & 1u) &&
+                          (xa[j] > st.tau_a || (xa[j] == st.tau_a && idx < st.tau_i));
+        const uint64_t m = ballot(pass);
         if (pass) {
+          const int pos = st.cnt + prefix_count(m);
           ba[pos] = xa[j];
-          bb[pos] = xb[j];
-          bi[pos] = idx[j];
+          bi[pos] = idx;
         }
         st.cnt += __popcll(m);
       }
-      if (st.cnt >= kFlushAt) flush_candidates(ba, bb, bi, st, kint);
+      if (st.cnt > kFlushAt) flush_candidates(ba, bi, st, kint);
     }
     // candidate argmax, lowest index on ties (steps of a wave ascend in index)
     if (ballot(gb > st.bmax)) {
@@ -412,34 +446,32 @@ __device__ __forceinline__ void process_step(const uint32_t (&ua)[8], const uint
       int li = 0x7fffffff;
 #pragma unroll
       for (int j = 7; j >= 0; --j)
-        if (((valid >> j) & 1u) && xb[j] == wm) li = idx[j];
+        if (((valid >> j) & 1u) && xb[j] == wm) li = base + lane_offset<MAPB>(lane, j);
       st.bmax = wm;
       st.bidx = uniform(wave_min(li));
     }
   }
 
   if (BITS) {
+    // distance in the ordered integer image: |ua - ub| when the signs agree,
+    // ma + mb + 1 (through zero) when they differ; bf16 patterns sit in the
+    // upper half, so the same formula yields the bf16 distance << 16
     uint64_t any = 0;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      const uint64_t m = ballot(ua[j] != ub[j]);
+      const uint32_t x = ua[j] ^ ub[j];
+      const uint64_t m = ballot(x != 0u);
       st.ndiff += __popcll(m);
       any |= m;
-      uint32_t oa, ob;
-      if (W16) {
-        oa = ulp_order16(ua[j] >> 16);
-        ob = ulp_order16(ub[j] >> 16);
-      } else {
-        oa = ulp_order32(ua[j]);
-        ob = ulp_order32(ub[j]);
-      }
-      st.max_ulp = max(st.max_ulp, max(oa, ob) - min(oa, ob));
+      const uint32_t same = sad_u32(ua[j], ub[j]);
+      const uint32_t cross = ua[j] + ub[j] + (W16 ? 0x80010000u : 0x80000001u);
+      st.max_ulp = max(st.max_ulp, (int32_t)x < 0 ? cross : same);
     }
     if (st.first < 0 && any) {
       int li = 0x7fffffff;
 #pragma unroll
       for (int j = 7; j >= 0; --j)
-        if (ua[j] != ub[j]) li = idx[j];
+        if (ua[j] != ub[j]) li = base + lane_offset<MAPB>(lane, j);
       st.first = uniform(wave_min(li));
     }
   }
@@ -452,23 +484,22 @@ __global__ __launch_bounds__(kBlock) void k_row_stats(StreamArgs args) {
   constexpr bool MAPB = (TA == 1 && TB == 1);
   constexpr bool W16 = (TA == 1 && TB == 1);
   constexpr int SA = TA == 1 ? 2 : 4, SB = TB == 1 ? 2 : 4;
-  __shared__ float s_ba[kWavesPerBlock][CMP ? kCap : 1];
-  __shared__ float s_bb[kWavesPerBlock][CMP ? kCap : 1];
-  __shared__ int s_bi[kWavesPerBlock][CMP ? kCap : 1];
+  __shared__ float s_ba[kWavesPerBlock][CMP ? kCapW : 1];
+  __shared__ int s_bi[kWavesPerBlock][CMP ? kCapW : 1];
 
-  const int wid = threadIdx.x / kWave;
+  // every quantity derived from the wave id is uniform: keep it scalar
+  const int wid = __builtin_amdgcn_readfirstlane((int)(threadIdx.x / kWave));
   const int lane = lane_id();
   const int64_t item = (int64_t)blockIdx.x * kWavesPerBlock + wid;
-  const int64_t items = args.n * args.nchunks;
-  if (item >= items) return;
+  if (item >= args.n * args.nchunks) return;
   const int64_t row = item / args.nchunks;
   const int chunk = (int)(item - row * args.nchunks);
-  const int64_t lo = (int64_t)chunk * args.chunk;
-  const int64_t hi = min(args.v, lo + args.chunk);
+  // column indices fit in 32 bits (the vocabulary is below 2^31)
+  const int lo = (int)((int64_t)chunk * args.chunk);
+  const int hi = (int)min(args.v, (int64_t)lo + args.chunk);
   const char *ra = (const char *)args.a + row * args.lda * SA;
   const char *rb = (const char *)args.b + row * args.ldb * SB;
   float *ba = s_ba[wid];
-  float *bb = s_bb[wid];
   int *bi = s_bi[wid];
   const int kint = args.kint;
 
@@ -476,14 +507,12 @@ __global__ __launch_bounds__(kBlock) void k_row_stats(StreamArgs args) {
   st.s = st.d = st.f = 0.0;
   st.r2h = -INFINITY;
   st.r2l = 0.0f;
-  st.huge = false;
   st.gate = -INFINITY;
   st.bmax = -INFINITY;
   st.bidx = -1;
   st.tau_a = -INFINITY;
-  st.tau_i = 0x7fffffff;
+  st.tau_i = kTauOpen;
   st.cnt = 0;
-  st.tau_set = false;
   st.n_bad = st.n_ainf = st.n_binf = st.n_qzero = 0;
   st.ndiff = 0;
   st.first = -1;
@@ -493,45 +522,52 @@ __global__ __launch_bounds__(kBlock) void k_row_stats(StreamArgs args) {
   st.sab = st.ssd = st.ssb = 0.0;
   st.nfa = st.nfb = 0;
 
-  const int64_t nfull = (hi - lo) / kSpan;
+  const int nfull = (hi - lo) / kSpan;
   if (VEC) {
-    if (nfull > 0) {
-      Raw<TA, TB> cur, nxt;
-      load_vec<TA, TB>(cur, ra, rb, lo, lane);
-      for (int64_t sp = 0; sp < nfull; ++sp) {
-        const int64_t base = lo + sp * kSpan;
-        if (sp + 1 < nfull) load_vec<TA, TB>(nxt, ra, rb, base + kSpan, lane);
-        uint32_t ua[8], ub[8];
-        decode<TA, MAPB>(cur.a0, cur.a1, ua);
-        decode<TB, MAPB>(cur.b0, cur.b1, ub);
-        process_step<CMP, BITS, W16, MAPB>(ua, ub, 0xffu, false, base, lane, kint, st, ba, bb, bi);
-        cur = nxt;
-      }
+    // Two register sets: while one step is processed the next one's loads are
+    // in flight.  The prefetch is unconditional (the last step is fetched
+    // twice): a load under a branch makes the wait before the current step's
+    // use a full drain of the memory counter.
+    const char *pa = ra + (int64_t)lo * SA, *pb = rb + (int64_t)lo * SB;
+    Raw<TA, TB> cur, nxt;
+    if (nfull > 0) cur.load(pa, pb, (uint32_t)lane);
+#pragma unroll 1
+    for (int sp = 0; sp < nfull; ++sp) {
+      const int sn = sp + 1 < nfull ? sp + 1 : sp;
+      nxt.load(pa + (int64_t)sn * kSpan * SA, pb + (int64_t)sn * kSpan * SB, (uint32_t)lane);
+      uint32_t ua[8], ub[8];
+      cur.a.decode(ua);
+      cur.b.decode(ub);
+      process_step<CMP, BITS, W16, MAPB>(ua, ub, 0xffu, false, lo + sp * kSpan, lane, kint, st, ba,
+                                         bi);
+      cur = nxt;
     }
   } else {
-    for (int64_t sp = 0; sp < nfull; ++sp) {
-      const int64_t base = lo + sp * kSpan;
+#pragma unroll 1
+    for (int sp = 0; sp < nfull; ++sp) {
+      const int base = lo + sp * kSpan;
       uint32_t ua[8], ub[8];
       const uint32_t valid = load_checked<TA, TB, MAPB>(ua, ub, ra, rb, base, hi, lane);
-      process_step<CMP, BITS, W16, MAPB>(ua, ub, valid, false, base, lane, kint, st, ba, bb, bi);
+      process_step<CMP, BITS, W16, MAPB>(ua, ub, valid, false, base, lane, kint, st, ba, bi);
     }
   }
   if (lo + nfull * kSpan < hi) {
-    const int64_t base = lo + nfull * kSpan;
+    const int base = lo + nfull * kSpan;
     uint32_t ua[8], ub[8];
     const uint32_t valid = load_checked<TA, TB, MAPB>(ua, ub, ra, rb, base, hi, lane);
-    process_step<CMP, BITS, W16, MAPB>(ua, ub, valid, true, base, lane, kint, st, ba, bb, bi);
+    process_step<CMP, BITS, W16, MAPB>(ua, ub, valid, true, base, lane, kint, st, ba, bi);
   }
 
-  // ---- wave totals, fixed order
+  // ---- wave totals, fixed order.  The output pointers are read from the
+  // argument segment here rather than held in scalar registers through the loop.
+  const StreamArgs &late = *(const StreamArgs *)__builtin_amdgcn_kernarg_segment_ptr();
   if (CMP) {
-    if (st.cnt > kint) flush_candidates(ba, bb, bi, st, kint);
+    if (st.cnt > kint) flush_candidates(ba, bi, st, kint);
     wave_fence();
     const int64_t tk = item * kint;
     if (lane < st.cnt) {
-      args.ta[tk + lane] = ba[lane];
-      args.tb[tk + lane] = bb[lane];
-      args.ti[tk + lane] = bi[lane];
+      late.ta[tk + lane] = ba[lane];
+      late.ti[tk + lane] = bi[lane];
     }
     const double S = wave_sum(st.s), D = wave_sum(st.d), F = wave_sum(st.f);
     const int nb = wave_sum(st.n_bad), na = wave_sum(st.n_ainf), nbi = wave_sum(st.n_binf),
@@ -550,13 +586,13 @@ __global__ __launch_bounds__(kBlock) void k_row_stats(StreamArgs args) {
       cs.n_binf = nbi;
       cs.n_qzero = nq;
       cs.pad_ = 0;
-      args.stats[item] = cs;
+      late.stats[item] = cs;
     }
   }
   if (BITS) {
     const double sab = wave_sum(st.sab), ssd = wave_sum(st.ssd), ssb = wave_sum(st.ssb);
     const int nfa = wave_sum(st.nfa), nfb = wave_sum(st.nfb);
-    const uint32_t mu = wave_max(st.max_ulp);
+    const uint32_t mu = wave_max(st.max_ulp) >> (W16 ? 16 : 0);
     const double ma = wave_max(fmax((double)st.max_abs, st.max_abs_d));
     if (lane == 0) {
       ChunkBits cb;
@@ -570,7 +606,7 @@ __global__ __launch_bounds__(kBlock) void k_row_stats(StreamArgs args) {
       cb.sum_abs = sab;
       cb.ssd = ssd;
       cb.ssb = ssb;
-      args.bits[item] = cb;
+      late.bits[item] = cb;
     }
   }
 }

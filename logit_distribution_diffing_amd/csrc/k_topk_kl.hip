@@ -33,10 +33,8 @@ __global__ __launch_bounds__(kWave) void k_topk_kl(FinalArgs a) {
   const int mcap = C * kint;
   uint32_t *e_key = smem;                          // [mcap]
   int32_t *e_idx = (int32_t *)(e_key + mcap);      // [mcap]
-  float *e_b = (float *)(e_idx + mcap);            // [mcap]
-  float *s_a = (float *)(e_b + mcap);              // [kMaxK] sorted
-  float *s_b = s_a + kMaxK;
-  int32_t *s_i = (int32_t *)(s_b + kMaxK);
+  float *s_a = (float *)(e_idx + mcap);            // [kMaxK] sorted
+  int32_t *s_i = (int32_t *)(s_a + kMaxK);
 
   if (a.bd) merge_bits(a.bits + row * C, C, a.v, a.bd + row);
 
@@ -97,12 +95,10 @@ __global__ __launch_bounds__(kWave) void k_topk_kl(FinalArgs a) {
     for (int j = lane; j < cc; j += kWave) {
       e_key[oc + j] = rank_key(a.ta[src + j]);
       e_idx[oc + j] = a.ti[src + j];
-      e_b[oc + j] = a.tb[src + j];
     }
   }
   for (int j = lane; j < kMaxK; j += kWave) {
     s_a[j] = -INFINITY;
-    s_b[j] = -INFINITY;
     s_i[j] = -1;
   }
   wave_fence2();
@@ -117,7 +113,6 @@ __global__ __launch_bounds__(kWave) void k_topk_kl(FinalArgs a) {
     }
     if (rank < kint) {
       s_a[rank] = rank_key_inv(ke);
-      s_b[rank] = e_b[e];
       s_i[rank] = ie;
     }
   }
@@ -127,7 +122,13 @@ __global__ __launch_bounds__(kWave) void k_topk_kl(FinalArgs a) {
   const int keff = (int)min((int64_t)a.k, a.v);
   const bool in_head = lane < keff;
   const float ha = in_head ? s_a[lane] : -INFINITY;
-  const float hb = in_head ? s_b[lane] : -INFINITY;
+  // gather the candidate logit at each head index
+  float hb = -INFINITY;
+  if (in_head) {
+    const int64_t off = row * a.ldc + s_i[lane];
+    hb = a.tc == 1 ? __uint_as_float((uint32_t)((const uint16_t *)a.cand)[off] << 16)
+                   : ((const float *)a.cand)[off];
+  }
   const bool ainf = ha == -INFINITY, binf = hb == -INFINITY;
   double e = 0.0, tphi = 0.0, tg = 0.0;
   int head_inf = 0;
@@ -194,7 +195,7 @@ __global__ __launch_bounds__(kWave) void k_topk_kl(FinalArgs a) {
 hipError_t launch_topk_kl(const FinalArgs &a, hipStream_t stream) {
   if (a.n == 0) return hipSuccess;
   const size_t mcap = (size_t)a.nchunks * a.kint;
-  const size_t shmem = mcap * 12 + (size_t)kMaxK * 12;
+  const size_t shmem = mcap * 8 + (size_t)kMaxK * 8;
   hipLaunchKernelGGL(k_topk_kl, dim3((unsigned)a.n), dim3(kWave), shmem, stream, a);
   return hipGetLastError();
 }

@@ -19,7 +19,7 @@ struct StreamArgs {
   int32_t kint;      // top-k entries kept per chunk
   ChunkStats *stats;  // [n * nchunks]  (compare)
   ChunkBits *bits;    // [n * nchunks]  (bitwise)
-  float *ta, *tb;     // [n * nchunks * kint]
+  float *ta;          // [n * nchunks * kint] top-k candidate values and indices
   int32_t *ti;
 };
 
@@ -27,8 +27,11 @@ struct StreamArgs {
 struct FinalArgs {
   const ChunkStats *stats;
   const ChunkBits *bits;  // NULL: no bitwise output
-  const float *ta, *tb;
+  const float *ta;
   const int32_t *ti;
+  const void *cand;  // candidate logits, read at the top-k indices
+  int32_t tc;
+  int64_t ldc;
   int64_t n, v;
   int32_t nchunks, kint, k;
   double *kl_topk, *kl_full, *margin, *lse_base, *lse_cand;

@@ -58,7 +58,7 @@ int kint_of(int64_t v, int k) {
 struct CompareLayout {
   Chunking ch;
   int kint;
-  size_t off_stats, off_bits, off_ta, off_tb, off_ti, total;
+  size_t off_stats, off_bits, off_ta, off_ti, total;
 };
 
 CompareLayout compare_layout(int64_t n, int64_t v, int k, uint32_t flags) {
@@ -72,8 +72,6 @@ CompareLayout compare_layout(int64_t n, int64_t v, int k, uint32_t flags) {
   L.off_bits = o;
   if (flags & LCMP_WITH_BITDIFF) o = align_up(o + items * sizeof(ChunkBits));
   L.off_ta = o;
-  o = align_up(o + items * (size_t)L.kint * sizeof(float));
-  L.off_tb = o;
   o = align_up(o + items * (size_t)L.kint * sizeof(float));
   L.off_ti = o;
   o = align_up(o + items * (size_t)L.kint * sizeof(int32_t));
@@ -116,10 +114,12 @@ size_t lcmp_compare_workspace_bytes(int64_t n, int64_t v, int k, uint32_t flags)
   return compare_layout(n, v, k, flags).total;
 }
 
-int lcmp_compare_logits(const void *base, int tb, int64_t ld_base, const void *cand, int tc,
+}  // extern "C"
+
+static int compare_impl(const void *base, int tb, int64_t ld_base, const void *cand, int tc,
                         int64_t ld_cand, int64_t n, int64_t v, int k, uint32_t flags,
                         const lcmp_row_out *out, lcmp_bitdiff_row *bd, void *workspace,
-                        size_t ws_bytes, void *stream) {
+                        size_t ws_bytes, void *stream, void *ev_before, void *ev_after) {
   if (!dtype_ok(tb) || !dtype_ok(tc)) return LCMP_EDTYPE;
   if (n < 0 || (flags & ~LCMP_WITH_BITDIFF) != 0 || !out) return LCMP_EINVAL;
   if (v < 2 || v > kMaxCols || n > kMaxRows || k < 1 || k > LCMP_MAX_K || ld_base < v ||
@@ -147,19 +147,22 @@ int lcmp_compare_logits(const void *base, int tb, int64_t ld_base, const void *c
   sa.stats = (ChunkStats *)(ws + L.off_stats);
   sa.bits = with_bits ? (ChunkBits *)(ws + L.off_bits) : nullptr;
   sa.ta = (float *)(ws + L.off_ta);
-  sa.tb = (float *)(ws + L.off_tb);
   sa.ti = (int32_t *)(ws + L.off_ti);
   hipStream_t s = (hipStream_t)stream;
+  if (ev_before && hipEventRecord((hipEvent_t)ev_before, s) != hipSuccess) return LCMP_EHIP;
   if (launch_row_stats(sa, tb, tc, true, with_bits, vector_ok(base, tb, ld_base, cand, tc, ld_cand),
                        s) != hipSuccess)
     return LCMP_EHIP;
+  if (ev_after && hipEventRecord((hipEvent_t)ev_after, s) != hipSuccess) return LCMP_EHIP;
 
   FinalArgs fa;
   fa.stats = sa.stats;
   fa.bits = sa.bits;
   fa.ta = sa.ta;
-  fa.tb = sa.tb;
   fa.ti = sa.ti;
+  fa.cand = cand;
+  fa.tc = tc;
+  fa.ldc = ld_cand;
   fa.n = n;
   fa.v = v;
   fa.nchunks = L.ch.nchunks;
@@ -179,6 +182,24 @@ int lcmp_compare_logits(const void *base, int tb, int64_t ld_base, const void *c
   fa.bd = with_bits ? (BitdiffRow *)bd : nullptr;
   if (launch_topk_kl(fa, s) != hipSuccess) return LCMP_EHIP;
   return LCMP_OK;
+}
+
+extern "C" {
+
+int lcmp_compare_logits(const void *base, int tb, int64_t ld_base, const void *cand, int tc,
+                        int64_t ld_cand, int64_t n, int64_t v, int k, uint32_t flags,
+                        const lcmp_row_out *out, lcmp_bitdiff_row *bd, void *workspace,
+                        size_t ws_bytes, void *stream) {
+  return compare_impl(base, tb, ld_base, cand, tc, ld_cand, n, v, k, flags, out, bd, workspace,
+                      ws_bytes, stream, nullptr, nullptr);
+}
+
+int lcmp_compare_logits_timed(const void *base, int tb, int64_t ld_base, const void *cand, int tc,
+                              int64_t ld_cand, int64_t n, int64_t v, int k, uint32_t flags,
+                              const lcmp_row_out *out, lcmp_bitdiff_row *bd, void *workspace,
+                              size_t ws_bytes, void *stream, void *ev_before, void *ev_after) {
+  return compare_impl(base, tb, ld_base, cand, tc, ld_cand, n, v, k, flags, out, bd, workspace,
+                      ws_bytes, stream, ev_before, ev_after);
 }
 
 size_t lcmp_bitdiff_workspace_bytes(int64_t rows, int64_t cols) {

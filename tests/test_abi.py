@@ -12,8 +12,8 @@ HEADER = os.path.join(ROOT, "include", "lcmp.h")
 
 @pytest.fixture(scope="module")
 def L():
-    from logit_distribution_diffing_amd import build
-    build.build()
+    import runpy
+    runpy.run_path(os.path.join(ROOT, "logit_distribution_diffing_amd", "build.py"))["build"]()
     import logit_distribution_diffing_amd as mod
     return mod
 
