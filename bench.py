@@ -41,7 +41,7 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0
 METRIC = "logit positions/sec at V=151936 + achieved HBM GB/s vs MI355X peak"
 COUNTERS_FILE = os.path.join(ROOT, "profiles", "k_row_stats_corpus_counters.md")
-KERNEL_SOURCES = ("k_row_stats.hip", "common.hpp", "launch.hpp")
+KERNEL_SOURCES = ("k_row_stats.hip", "common.hpp")
 
 
 def log(*a):
@@ -101,7 +101,7 @@ def make_inputs(workload: str, w: dict, torch):
     dt = {"f32": torch.float32, "bf16": torch.bfloat16}
     base = torch.empty((n, v), dtype=dt[w["base"]], device="cuda")
     cand = torch.empty((n, v), dtype=dt[w["cand"]], device="cuda")
-    keep = min(n, 4096)
+    keep = min(n, 16384)
     host_a = host_b = None
     blk = 1024
     t0 = time.time()

@@ -3,12 +3,12 @@
 // flips are judged per margin bin, and a flip at a large margin is a stop).
 //
 // Two levels with a fixed order, so repeated calls are bit-identical:
-//   level 1: one wave per block of 2048 rows; each 64-row batch is split by
+//   level 1: one wave per block of 256 rows; each 64-row batch is split by
 //            bin, every bin's values are summed with a fixed butterfly and
 //            added to the block's LDS accumulator in batch order; integer
 //            counts go through LDS atomics (exact, order-free).
-//   level 2: one thread per bin (and per group) adds the block partials in
-//            block order.
+//   level 2: one wave per bin (and per group) adds the block partials in a
+//            fixed lane-then-butterfly order.
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -106,31 +106,48 @@ __global__ __launch_bounds__(kWave) void k_bin_partial(BinArgs a) {
   }
 }
 
-__global__ __launch_bounds__(kBlock) void k_bin_final(BinArgs a) {
+// One wave per bin (then per group): lane l adds partials l, l+64, ... in order,
+// then the butterfly combines the lanes.
+__global__ __launch_bounds__(kWave) void k_bin_final(BinArgs a) {
+  const int lane = lane_id();
   const int nbins = a.n_groups * a.n_edges;
-  for (int t = threadIdx.x; t < nbins; t += kBlock) {
-    BinAcc o = {0, 0, 0, 0, 0.0, 0.0, -INFINITY};
-    for (int b = 0; b < a.nblk; ++b) {
+  const int t = blockIdx.x;
+  if (t < nbins) {
+    int64_t c0 = 0, c1 = 0, c2 = 0, c3 = 0;
+    double s0 = 0.0, s1 = 0.0, mx = -INFINITY;
+    for (int b = lane; b < a.nblk; b += kWave) {
       const BinAcc p = a.part_bins[(int64_t)b * nbins + t];
-      o.count += p.count;
-      o.flips += p.flips;
-      o.ties += p.ties;
-      o.tie_flips += p.tie_flips;
-      o.sum_kl_topk += p.sum_kl_topk;
-      o.sum_kl_full += p.sum_kl_full;
-      o.max_kl_topk = fmax(o.max_kl_topk, p.max_kl_topk);
+      c0 += p.count;
+      c1 += p.flips;
+      c2 += p.ties;
+      c3 += p.tie_flips;
+      s0 += p.sum_kl_topk;
+      s1 += p.sum_kl_full;
+      mx = fmax(mx, p.max_kl_topk);
     }
-    a.bins[t] = o;
-  }
-  for (int g = threadIdx.x; g < a.n_groups; g += kBlock) {
-    GroupAcc o = {0, 0, 0};
-    for (int b = 0; b < a.nblk; ++b) {
+    BinAcc o;
+    o.count = wave_sum(c0);
+    o.flips = wave_sum(c1);
+    o.ties = wave_sum(c2);
+    o.tie_flips = wave_sum(c3);
+    o.sum_kl_topk = wave_sum(s0);
+    o.sum_kl_full = wave_sum(s1);
+    o.max_kl_topk = wave_max(mx);
+    if (lane == 0) a.bins[t] = o;
+  } else {
+    const int g = t - nbins;
+    int64_t c0 = 0, c1 = 0, c2 = 0;
+    for (int b = lane; b < a.nblk; b += kWave) {
       const GroupAcc p = a.part_groups[(int64_t)b * a.n_groups + g];
-      o.big_margin_flips += p.big_margin_flips;
-      o.excluded += p.excluded;
-      o.unbinned += p.unbinned;
+      c0 += p.big_margin_flips;
+      c1 += p.excluded;
+      c2 += p.unbinned;
     }
-    a.groups[g] = o;
+    GroupAcc o;
+    o.big_margin_flips = wave_sum(c0);
+    o.excluded = wave_sum(c1);
+    o.unbinned = wave_sum(c2);
+    if (lane == 0) a.groups[g] = o;
   }
 }
 
@@ -140,7 +157,8 @@ hipError_t launch_bin_reduce(const BinArgs &a, hipStream_t stream) {
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL(k_bin_final, dim3(1), dim3(kBlock), 0, stream, a);
+  hipLaunchKernelGGL(k_bin_final, dim3((unsigned)(a.n_groups * a.n_edges + a.n_groups)),
+                     dim3(kWave), 0, stream, a);
   return hipGetLastError();
 }
 

@@ -58,7 +58,7 @@ struct GroupAcc {
   int64_t big_margin_flips, excluded, unbinned;
 };
 
-constexpr int kBinRowsPerBlock = 2048;  // rows of one level-1 block (one wave)
+constexpr int kBinRowsPerBlock = 256;  // rows of one level-1 block (one wave)
 constexpr int kMaxBins = 256;           // n_groups * n_edges
 constexpr int kMaxGroups = 256;
 constexpr int kMaxEdges = 32;
