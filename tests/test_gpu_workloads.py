@@ -1,0 +1,304 @@
+"""GPU parity at the workloads' full sizes, in the launch configuration that
+bench.py times (compare with fused bitwise statistics, then the margin-bin
+report), plus the margin-bin reduction on its own.
+
+Full-size rows are checked against the oracle on a sample of positions the
+oracle computes one by one; properties that hold at any size (bin totals, the
+constructed big-margin flips, identical outputs for identical rows, bitwise
+repeatability) are checked on every row.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from helpers import assert_bitdiff_equal, assert_compare_equal, to_device
+
+pytestmark = pytest.mark.gpu
+
+BIN_SUM_REL = 1e-12  # fp64 sums of up to 1e6 non-negative terms in another order
+
+
+def _case(msg):
+    print(f"[case] {msg}", flush=True)
+
+
+def _gen(workload, w, r0, nr):
+    if workload == "segment":
+        return synth.segment(w["seed"], r0, nr, w["v"])
+    if workload == "corpus":
+        return synth.corpus(w["seed"], r0, nr, w["v"], w["n"], w["swap_frac"])
+    if workload == "stream":
+        return synth.stream(w["seed"], r0, nr, w["v"])
+    raise ValueError(workload)
+
+
+def _upload(workload, w, rows_kept, n_gen=None, blk=1024):
+    """Generate rows [0, n_gen) block by block into device tensors of shape
+    [n, v]; keep host copies of `rows_kept` (must lie below n_gen)."""
+    import torch
+    n, v = w["n"], w["v"]
+    n_gen = n if n_gen is None else n_gen
+    dt = {"f32": torch.float32, "bf16": torch.bfloat16}
+    base = torch.empty((n, v), dtype=dt[w["base"]], device="cuda")
+    cand = torch.empty((n, v), dtype=dt[w["cand"]], device="cuda")
+    kept_a, kept_b = {}, {}
+    for r0 in range(0, n_gen, blk):
+        nr = min(blk, n_gen - r0)
+        a, b = _gen(workload, w, r0, nr)
+        for r in rows_kept:
+            if r0 <= r < r0 + nr:
+                kept_a[r] = a[r - r0].copy()
+                kept_b[r] = b[r - r0].copy()
+        base[r0:r0 + nr].copy_(to_device(a))
+        cand[r0:r0 + nr].copy_(to_device(b))
+        print(f"[gen] {workload} rows {r0 + nr}/{n_gen}", flush=True)
+    rows = sorted(rows_kept)
+    ha = np.stack([kept_a[r] for r in rows])
+    hb = np.stack([kept_b[r] for r in rows])
+    return base, cand, np.array(rows, dtype=np.int64), ha, hb
+
+
+def _bench_step(base, cand, k, edges):
+    """The timed step of bench.py: compare with bitwise statistics, then bins."""
+    import torch
+    import logit_distribution_diffing_amd as L
+    n = base.size(0)
+    out = L.alloc_compare_outputs(n, k, base.device, with_bitdiff=True)
+    ws = torch.empty(L.compare_workspace_bytes(n, base.size(1), k, True), dtype=torch.uint8,
+                     device="cuda")
+    L.lcmp_compare_logits(base, cand, k=k, with_bitdiff=True, out=out, workspace=ws)
+    bins, summ = L.lcmp_bin_report(out["margin"], out["flip"], out["kl_topk"], out["kl_full"],
+                                   edges, status=out["status"])
+    torch.cuda.synchronize()
+    g = {key: val.cpu().numpy() for key, val in out.items() if key != "bitdiff"}
+    g["bitdiff"] = L.unpack_bitdiff(out["bitdiff"])
+    gb, gs = L.unpack_bins(bins, summ)
+    return g, gb, gs
+
+
+def _select(g, rows):
+    s = {key: val[rows] for key, val in g.items() if key != "bitdiff"}
+    s["bitdiff"] = g["bitdiff"][rows]
+    return s
+
+
+def _check_rows(g, rows, ha, hb, k):
+    sub = _select(g, rows)
+    assert_compare_equal(sub, oracle.compare(ha, hb, k=k))
+    assert_bitdiff_equal(sub["bitdiff"], oracle.bitdiff(ha, hb))
+
+
+def _bins_total(gb, gs):
+    return int(gb["count"].sum() + gs["excluded"].sum() + gs["unbinned"].sum())
+
+
+def test_segment_all_rows():
+    """512 x 151936 fp32/fp32, every row against the oracle, bins included."""
+    w = synth.WORKLOADS["segment"]
+    _case("segment 512x151936 f32/f32, all rows")
+    base, cand, rows, ha, hb = _upload("segment", w, range(w["n"]))
+    g, gb, gs = _bench_step(base, cand, w["k"], synth.DEFAULT_EDGES)
+    _check_rows(g, rows, ha, hb, w["k"])
+    o = oracle.compare(ha, hb, k=w["k"])
+    ob, os_ = oracle.bin_report(o["margin"], o["flip"], o["kl_topk"], o["kl_full"],
+                                synth.DEFAULT_EDGES, status=o["status"])
+    for f in ("count", "flips", "ties", "tie_flips"):
+        assert np.array_equal(gb[f], ob[f]), f
+    for f in ("big_margin_flips", "excluded", "unbinned"):
+        assert np.array_equal(gs[f], os_[f]), f
+    # KL sums of GPU and oracle rows agree as the rows do
+    for f in ("sum_kl_topk", "sum_kl_full"):
+        tol = 1e-7 * gb["count"] + 1e-4 * ob[f]
+        assert np.all(np.abs(gb[f] - ob[f]) <= tol), f
+
+
+@pytest.fixture(scope="module")
+def corpus_run():
+    """Corpus scale, 10240 x 151936 fp32/bf16, generated in full on the device."""
+    w = synth.WORKLOADS["corpus"]
+    swaps = synth.swap_rows(w["seed"], w["n"], w["swap_frac"])
+    rng = np.random.default_rng(20240)
+    extra = rng.choice(w["n"], 192, replace=False)
+    edge_rows = [0, 1, 511, 512, 2047, 2048, 4095, 4096, w["n"] - 2, w["n"] - 1]
+    kept = set(int(r) for r in np.concatenate([swaps, extra, edge_rows]))
+    base, cand, rows, ha, hb = _upload("corpus", w, kept)
+    g, gb, gs = _bench_step(base, cand, w["k"], synth.DEFAULT_EDGES)
+    g2, gb2, gs2 = _bench_step(base, cand, w["k"], synth.DEFAULT_EDGES)
+    del base, cand
+    import torch
+    torch.cuda.empty_cache()
+    return dict(w=w, swaps=swaps, rows=rows, ha=ha, hb=hb, g=g, gb=gb, gs=gs, g2=g2, gb2=gb2,
+                gs2=gs2)
+
+
+def test_corpus_sampled_rows(corpus_run):
+    c = corpus_run
+    _case(f"corpus 10240x151936 f32/bf16, {len(c['rows'])} sampled rows")
+    _check_rows(c["g"], c["rows"], c["ha"], c["hb"], c["w"]["k"])
+
+
+def test_corpus_big_margin_flips_by_construction(corpus_run):
+    """51 rows carry a top-1/top-2 exchange at a margin above 1; the noise of
+    sd 0.02 cannot flip any other row at such a margin."""
+    c = corpus_run
+    _case("corpus big-margin flips")
+    w, g, swaps = c["w"], c["g"], c["swaps"]
+    assert swaps.size == 51
+    assert int(c["gs"]["big_margin_flips"][0]) == 51
+    assert np.all(g["flip"][swaps] == 1) and np.all(g["margin"][swaps] > 1.0)
+    assert _bins_total(c["gb"], c["gs"]) == w["n"]
+    assert int(c["gs"]["excluded"][0]) == 0
+    assert int(c["gb"]["flips"].sum()) == int(g["flip"].sum())
+    assert int(c["gb"]["count"].sum()) + int(c["gs"]["unbinned"][0]) == w["n"]
+
+
+def test_corpus_repeatable_bit_for_bit(corpus_run):
+    c = corpus_run
+    _case("corpus determinism")
+    for key in c["g"]:
+        if key == "bitdiff":
+            assert c["g"][key].tobytes() == c["g2"][key].tobytes()
+        else:
+            assert np.array_equal(c["g"][key].view(np.uint8), c["g2"][key].view(np.uint8)), key
+    assert c["gb"].tobytes() == c["gb2"].tobytes()
+    assert c["gs"].tobytes() == c["gs2"].tobytes()
+
+
+def test_stream_full_size_tiled():
+    """65536 x 151936 bf16/bf16 (about 2 x 19.9 GB resident).  The first 1024
+    seeded rows are generated on the host and tiled over all positions, so
+    every position with the same row index mod 1024 must give bit-identical
+    outputs; sampled positions across the whole range are checked against the
+    oracle.  Row offsets pass 2^32 elements, so 64-bit addressing is exercised."""
+    import torch
+    w = synth.WORKLOADS["stream"]
+    _case("stream 65536x151936 bf16/bf16 (1024 seeded rows tiled)")
+    blk = 1024
+    base, cand, rows0, ha0, hb0 = _upload("stream", w, range(blk), n_gen=blk)
+    for r0 in range(blk, w["n"], blk):
+        base[r0:r0 + blk].copy_(base[:blk])
+        cand[r0:r0 + blk].copy_(cand[:blk])
+    g, gb, gs = _bench_step(base, cand, w["k"], synth.DEFAULT_EDGES)
+    del base, cand
+    torch.cuda.empty_cache()
+    pos = np.array([0, 1, 1023, 1024, 28270, 28271, 28272, 32768, 50000, 65534, 65535]
+                   + list(np.random.default_rng(7).choice(w["n"], 53, replace=False)))
+    pos = np.unique(pos)
+    _check_rows(g, pos, ha0[pos % blk], hb0[pos % blk], w["k"])
+    src = np.arange(w["n"]) % blk
+    for key in g:
+        if key == "bitdiff":
+            assert g[key].tobytes() == g[key][src].tobytes(), key
+        else:
+            assert np.array_equal(g[key].view(np.uint8).reshape(w["n"], -1),
+                                  g[key][src].view(np.uint8).reshape(w["n"], -1)), key
+    assert _bins_total(gb, gs) == w["n"]
+
+
+@pytest.mark.parametrize("t", synth.WORKLOADS["sweep"]["t_list"])
+def test_sweep_bf16_shapes(t):
+    """bf16 [T, 5120] with 0.1% of elements moved by +-1..3 ULP: the oracle's
+    statistics and the answers known by construction."""
+    import torch
+    import logit_distribution_diffing_amd as L
+    w = synth.WORKLOADS["sweep"]
+    _case(f"sweep bf16 [{t},{w['cols']}]")
+    a = synth.bf16_normal(w["seed"], 0, t, w["cols"])
+    b, pos, steps = synth.inject_ulp(w["seed"], t, a, w["frac"])
+    raw = L.lcmp_bitdiff(to_device(a), to_device(b))
+    torch.cuda.synchronize()
+    g = L.unpack_bitdiff(raw)
+    assert_bitdiff_equal(g, oracle.bitdiff(a, b))
+    _known_answers(g, pos, steps, t, w["cols"])
+
+
+def test_sweep_fp32_logit_rows():
+    import torch
+    import logit_distribution_diffing_amd as L
+    w = synth.WORKLOADS["sweep"]
+    _case(f"sweep fp32 [{w['logit_rows']},{w['v']}]")
+    a = synth.logit_rows(w["seed"], 0, w["logit_rows"], w["v"])
+    b, pos, steps = synth.inject_ulp(w["seed"], 99, a, w["frac"])
+    raw = L.lcmp_bitdiff(to_device(a), to_device(b))
+    torch.cuda.synchronize()
+    g = L.unpack_bitdiff(raw)
+    assert_bitdiff_equal(g, oracle.bitdiff(a, b))
+    _known_answers(g, pos, steps, w["logit_rows"], w["v"])
+
+
+def _known_answers(g, pos, steps, rows, cols):
+    r, c = pos // cols, pos % cols
+    ndiff = np.bincount(r, minlength=rows)
+    first = np.full(rows, -1, np.int64)
+    mx = np.zeros(rows, np.int64)
+    for rr, cc, s in zip(r, c, steps):
+        if first[rr] < 0 or cc < first[rr]:
+            first[rr] = cc
+        mx[rr] = max(mx[rr], abs(int(s)))
+    assert np.array_equal(g["ndiff"], ndiff)
+    assert np.array_equal(g["first_diff"], first)
+    assert np.array_equal(g["max_ulp"].astype(np.int64), mx)
+
+
+# --------------------------------------------------------------------- margin bins
+def _bin_inputs(n, n_groups, edges, seed):
+    rng = np.random.default_rng(seed)
+    special = np.array([0.0, *[e for e in edges if np.isfinite(e)]])
+    pick = rng.integers(0, 5, n)
+    m = rng.uniform(0.0, 3.0, n)
+    sp = special[rng.integers(0, special.size, n)]
+    m = np.where(pick == 0, sp, m)                                     # exactly on an edge
+    m = np.where(pick == 1, np.nextafter(sp, -np.inf).clip(0.0), m)   # just below one
+    m = np.where(rng.random(n) < 0.01, np.inf, m)                      # top-2 at -inf
+    m = np.where(rng.random(n) < 0.01, 50.0 + rng.random(n), m)
+    flip = (rng.random(n) < np.exp(-2.0 * m)).astype(np.uint8)
+    flip[rng.random(n) < 0.002] = 1                                    # big-margin flips
+    kt = rng.exponential(1e-4, n)
+    kf = kt * (1.0 + rng.random(n))
+    kf[rng.random(n) < 0.001] = np.inf                                 # q = 0 somewhere
+    status = np.zeros(n, np.uint8)
+    status[rng.random(n) < 0.005] = 1
+    status[rng.random(n) < 0.002] = 2
+    m[status != 0] = np.nan
+    kt[status != 0] = np.nan
+    kf[status != 0] = np.nan
+    group = rng.integers(0, n_groups, n).astype(np.int32)
+    group[rng.random(n) < 0.01] = -1                                   # rows outside every group
+    group[rng.random(n) < 0.01] = n_groups
+    return m, flip, kt, kf, status, group
+
+
+@pytest.mark.parametrize("n", [0, 1, 63, 64, 65, 255, 256, 257, 10240, 65536, 1 << 20])
+@pytest.mark.parametrize("n_groups,edges", [
+    (1, synth.DEFAULT_EDGES),
+    (5, synth.DEFAULT_EDGES),
+    (8, tuple(0.1 * (j + 1) for j in range(32))),    # 32 finite edges: rows above 3.2 unbinned
+    (256, (1.0,)),
+])
+def test_bin_report_parity(n, n_groups, edges):
+    import torch
+    import logit_distribution_diffing_amd as L
+    _case(f"bins n={n} groups={n_groups} edges={len(edges)}")
+    m, flip, kt, kf, status, group = _bin_inputs(n, n_groups, edges, seed=n * 7 + n_groups)
+    dev = {name: torch.from_numpy(x).cuda() for name, x in
+           (("m", m), ("flip", flip), ("kt", kt), ("kf", kf), ("st", status), ("gr", group))}
+    bins, summ = L.lcmp_bin_report(dev["m"], dev["flip"], dev["kt"], dev["kf"], edges,
+                                   status=dev["st"], group=dev["gr"], n_groups=n_groups)
+    bins2, summ2 = L.lcmp_bin_report(dev["m"], dev["flip"], dev["kt"], dev["kf"], edges,
+                                     status=dev["st"], group=dev["gr"], n_groups=n_groups)
+    torch.cuda.synchronize()
+    gb, gs = L.unpack_bins(bins, summ, n_groups)
+    ob, os_ = oracle.bin_report(m, flip, kt, kf, edges, status=status, group=group,
+                                n_groups=n_groups)
+    for f in ("count", "flips", "ties", "tie_flips"):
+        assert np.array_equal(gb[f], ob[f]), f
+    for f in ("big_margin_flips", "excluded", "unbinned"):
+        assert np.array_equal(gs[f], os_[f]), f
+    assert np.array_equal(gb["max_kl_topk"], ob["max_kl_topk"])
+    for f in ("sum_kl_topk", "sum_kl_full"):
+        inf = np.isinf(ob[f])
+        assert np.array_equal(np.isinf(gb[f]), inf), f
+        assert np.all(np.abs(gb[f][~inf] - ob[f][~inf]) <= BIN_SUM_REL * ob[f][~inf]), f
+    assert bins.cpu().numpy().tobytes() == bins2.cpu().numpy().tobytes()
+    assert summ.cpu().numpy().tobytes() == summ2.cpu().numpy().tobytes()
