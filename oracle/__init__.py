@@ -76,8 +76,13 @@ def build(force: bool = False) -> str:
 def _L():
     global _lib
     if _lib is None:
-        build()
-        lib = ctypes.CDLL(_SO)
+        # ORACLE_LIB names another build of oracle.c (the mutation tests load
+        # deliberately broken copies through it); by default the in-tree build
+        path = os.environ.get("ORACLE_LIB")
+        if not path:
+            build()
+            path = _SO
+        lib = ctypes.CDLL(path)
         vp, i64, ci = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
         lib.orc_compare.restype = ci
         lib.orc_compare.argtypes = [vp, ci, i64, vp, ci, i64, i64, i64, ci] + [vp] * 11 + [ci]
