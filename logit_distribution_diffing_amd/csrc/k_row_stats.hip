@@ -29,14 +29,16 @@
 
 namespace lcmp {
 
-// The candidate buffer holds kCapW = kCapPerLane * 64 entries (value, index).
-// A step appends at most 8 entries per lane whose group maximum passes the
+// The candidate buffer holds kCapW entries (value, index).  Each half of a
+// step appends at most 4 entries per lane whose group maximum passes the
 // threshold; when that bound could overflow the buffer it is first reduced to
-// kint <= 64 entries (64 + 512 <= kCapW), and after a step it is reduced
+// kint <= 64 entries (64 + 256 <= kCapW), and after a step it is reduced
 // whenever it holds more than kFlushAt.
-constexpr int kCapPerLane = 9;
-constexpr int kCapW = kCapPerLane * kWave;  // 576
-constexpr int kFlushAt = 256;
+constexpr int kCapW = 8 * kWave;  // 512
+#ifndef LCMP_FLUSH_AT
+#define LCMP_FLUSH_AT 128
+#endif
+constexpr int kFlushAt = LCMP_FLUSH_AT;
 // threshold index meaning "no index bound yet": every element at or above
 // the threshold value passes
 constexpr int kTauOpen = 0x7fffffff;
@@ -49,6 +51,7 @@ struct WaveState {
   // (|r2h| >= 2^28) that one float cannot hold the reference within a unit;
   // such chunks take the exact path throughout
   float r2h, r2l, gate;
+  float nr2h;  // -r2h, kept where the per-element multiply-add reads it
   // candidate argmax (uniform)
   float bmax;
   int bidx;
@@ -99,32 +102,45 @@ __device__ __forceinline__ uint32_t sad_u32(uint32_t a, uint32_t b) {
 // Reduce the wave's candidate buffer (cnt > kint entries of value ba[] and
 // index bi[] in LDS) to exactly the kint largest keys -- value descending,
 // index ascending -- and raise the threshold to the kint-th key.  Whole wave,
-// uniform control flow.  Written for size, not speed: it runs rarely.
+// uniform control flow.  The entries are read into registers once (lane l
+// holds entries l, l + 64, ...); the selection is a bitwise radix search with
+// one ballot per entry round and bit.
 __device__ __forceinline__ void flush_candidates(float *ba, int *bi, WaveState &st, int kint) {
+  constexpr int kRounds = kCapW / kWave;
   wave_fence();
   const int lane = lane_id();
   const int cnt = st.cnt;
   const int per = (cnt + kWave - 1) / kWave;
+  uint32_t key[kRounds];
+  int idx[kRounds];
+#pragma unroll
+  for (int q = 0; q < kRounds; ++q) {
+    const int e = lane + kWave * q;
+    key[q] = 0u;  // below every stored key (the smallest, -inf, maps to 0x007fffff)
+    idx[q] = 0x7fffffff;
+    if (q < per && e < cnt) {
+      key[q] = rank_key(ba[e]);
+      idx[q] = bi[e];
+    }
+  }
   // kint-th largest value key, one bit at a time from the top
   uint32_t T = 0;
 #pragma unroll 1
   for (int bit = 31; bit >= 0; --bit) {
     const uint32_t c = T | (1u << bit);
     int n = 0;
-#pragma unroll 1
-    for (int q = 0; q < per; ++q) {
-      const int e = lane + kWave * q;
-      n += __popcll(ballot(e < cnt && rank_key(ba[e]) >= c));
-    }
+#pragma unroll
+    for (int q = 0; q < kRounds; ++q)
+      if (q < per) n += __popcll(ballot(key[q] >= c));
     if (n >= kint) T = c;
   }
   int ngt = 0, neq = 0;
-#pragma unroll 1
-  for (int q = 0; q < per; ++q) {
-    const int e = lane + kWave * q;
-    const uint32_t k = e < cnt ? rank_key(ba[e]) : 0u;
-    ngt += __popcll(ballot(e < cnt && k > T));
-    neq += __popcll(ballot(e < cnt && k == T));
+#pragma unroll
+  for (int q = 0; q < kRounds; ++q) {
+    if (q < per) {
+      ngt += __popcll(ballot(key[q] > T));
+      neq += __popcll(ballot(key[q] == T));
+    }
   }
   const int need = kint - ngt;  // >= 1 entries taken among the ties at T
   int isel = 0x7fffffff;
@@ -135,37 +151,32 @@ __device__ __forceinline__ void flush_candidates(float *ba, int *bi, WaveState &
     for (int bit = 30; bit >= 0; --bit) {
       const uint32_t c = I | (1u << bit);
       int n = 0;
-#pragma unroll 1
-      for (int q = 0; q < per; ++q) {
-        const int e = lane + kWave * q;
-        n += __popcll(ballot(e < cnt && rank_key(ba[e]) == T && (uint32_t)bi[e] < c));
-      }
+#pragma unroll
+      for (int q = 0; q < kRounds; ++q)
+        if (q < per) n += __popcll(ballot(key[q] == T && (uint32_t)idx[q] < c));
       if (n < need) I = c;
     }
     isel = (int)I;
   }
-  // in-place compaction in entry order: every entry of round q is read before
-  // any lane writes, and round q writes only below 64 * (q + 1)
+  // compaction in entry order; all entries are in registers, so the buffer
+  // can be overwritten freely
+  wave_fence();
   int fill = 0, tie_hi = -1;
-#pragma unroll 1
-  for (int q = 0; q < per; ++q) {
-    const int e = lane + kWave * q;
-    const bool in = e < cnt;
-    const float va = in ? ba[e] : 0.0f;
-    const int ix = in ? bi[e] : 0;
-    const uint32_t k = rank_key(va);
-    const bool keep = in && (k > T || (k == T && ix <= isel));
-    if (keep && k == T) tie_hi = max(tie_hi, ix);
-    const uint64_t m = ballot(keep);
-    wave_fence();
-    if (keep) {
-      const int pos = fill + prefix_count(m);
-      ba[pos] = va;
-      bi[pos] = ix;
+#pragma unroll
+  for (int q = 0; q < kRounds; ++q) {
+    if (q < per) {
+      const bool keep = key[q] > T || (key[q] == T && idx[q] <= isel);
+      if (keep && key[q] == T) tie_hi = max(tie_hi, idx[q]);
+      const uint64_t m = ballot(keep);
+      if (keep) {
+        const int pos = fill + prefix_count(m);
+        ba[pos] = rank_key_inv(key[q]);
+        bi[pos] = idx[q];
+      }
+      fill += __popcll(m);
     }
-    fill += __popcll(m);
-    wave_fence();
   }
+  wave_fence();
   st.cnt = fill;
   st.tau_a = rank_key_inv(T);
   st.tau_i = uniform(wave_max(tie_hi));
@@ -197,6 +208,10 @@ struct Side<0, MAPB> {
     p0 = __builtin_nontemporal_load((const u32x4 *)(p + 16u * lane));
     p1 = __builtin_nontemporal_load((const u32x4 *)(p + 1024u + 16u * lane));
   }
+  __device__ __forceinline__ void load_lds(const char *p, uint32_t lane) {
+    p0 = *(const u32x4 *)(p + 16u * lane);
+    p1 = *(const u32x4 *)(p + 1024u + 16u * lane);
+  }
   __device__ __forceinline__ void decode(uint32_t (&u)[8]) const {
     u[0] = p0.x; u[1] = p0.y; u[2] = p0.z; u[3] = p0.w;
     u[4] = p1.x; u[5] = p1.y; u[6] = p1.z; u[7] = p1.w;
@@ -208,6 +223,10 @@ struct Side<1, false> {
   __device__ __forceinline__ void load(const char *p, uint32_t lane) {
     p0 = __builtin_nontemporal_load((const u32x2 *)(p + 8u * lane));
     p1 = __builtin_nontemporal_load((const u32x2 *)(p + 512u + 8u * lane));
+  }
+  __device__ __forceinline__ void load_lds(const char *p, uint32_t lane) {
+    p0 = *(const u32x2 *)(p + 8u * lane);
+    p1 = *(const u32x2 *)(p + 512u + 8u * lane);
   }
   __device__ __forceinline__ void decode(uint32_t (&u)[8]) const {
     u[0] = p0.x << 16; u[1] = p0.x & 0xffff0000u;
@@ -221,6 +240,9 @@ struct Side<1, true> {
   u32x4 p0;
   __device__ __forceinline__ void load(const char *p, uint32_t lane) {
     p0 = __builtin_nontemporal_load((const u32x4 *)(p + 16u * lane));
+  }
+  __device__ __forceinline__ void load_lds(const char *p, uint32_t lane) {
+    p0 = *(const u32x4 *)(p + 16u * lane);
   }
   __device__ __forceinline__ void decode(uint32_t (&u)[8]) const {
     u[0] = p0.x << 16; u[1] = p0.x & 0xffff0000u;
@@ -239,7 +261,90 @@ struct Raw {
     a.load(pa, lane);
     b.load(pb, lane);
   }
+  __device__ __forceinline__ void load_lds(const char *pa, const char *pb, uint32_t lane) {
+    a.load_lds(pa, lane);
+    b.load_lds(pb, lane);
+  }
 };
+
+// ---------------------------------------------------------------- LDS staging ring
+
+// Launch shape of one instantiation.  With the LDS ring, the bytes a CU keeps
+// in flight (waves x (ring depth - 1) x step bytes) bound the stream's rate:
+// with a few microseconds of loaded HBM latency, 6 TB/s needs about 100 KB per
+// CU in flight, so the ring is deep and the blocks are small enough that the
+// 160 KB of LDS of a CU holds several of them.
+#ifndef LCMP_RING_FF
+#define LCMP_RING_FF 3  // fp32 / fp32: 4 KiB steps
+#endif
+#ifndef LCMP_RING_FH
+#define LCMP_RING_FH 3  // one fp32 side: 3 KiB steps
+#endif
+#ifndef LCMP_RING_HH
+#define LCMP_RING_HH 3  // bf16 / bf16: 2 KiB steps
+#endif
+#ifndef LCMP_RING_WAVES
+#define LCMP_RING_WAVES 4  // waves per block when staging through LDS
+#endif
+// Which pairs stage through LDS: measured on the corpus (fp32 / bf16) and
+// stream (bf16 / bf16) shapes, the register double buffer is faster when one
+// side is fp32 (more waves fit), the ring when both sides are bf16.
+#ifndef LCMP_RING_MASK
+#define LCMP_RING_MASK 8  // bit 2 * TA + TB set: that pair uses the ring (8: bf16 / bf16 only)
+#endif
+template <int TA, int TB, bool CMP, bool VEC>
+struct Shape {
+  static constexpr bool RING = VEC && CMP && ((LCMP_RING_MASK >> (2 * TA + TB)) & 1);
+  static constexpr int SA = TA == 1 ? 2 : 4, SB = TB == 1 ? 2 : 4;
+  static constexpr int kStepA = kSpan * SA, kStepB = kSpan * SB;
+  static constexpr int kStep = kStepA + kStepB;
+  // ring slots: one step processed, R - 1 in flight
+  static constexpr int R = !RING                  ? 1
+                           : (TA == 1 && TB == 1) ? LCMP_RING_HH
+                           : (TA == 0 && TB == 0) ? LCMP_RING_FF
+                                                  : LCMP_RING_FH;
+  static constexpr int W = RING ? LCMP_RING_WAVES : kWavesPerBlock;  // waves per block
+  static_assert((R - 1) * (kStep / 1024) <= 63, "vector-memory counter range");
+};
+
+// Copy 1 KiB from global memory into LDS without passing through registers:
+// lane l moves bytes [16l, 16l + 16) of `src` to LDS byte address lds + 16l
+// (gfx950 global_load_lds_dwordx4; the LDS base goes in M0, which is restored
+// afterwards).  Completion is tracked by the vector-memory counter only, so
+// the reader waits with wait_vm<N>() before touching the data.
+__device__ __forceinline__ void dma_1k(const char *src, uint32_t voff, uint32_t lds) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %3\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, %2\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(voff), "s"(src), "s"(lds)
+      : "memory");
+}
+
+// Wait until at most N vector-memory operations of this wave are outstanding
+// (they complete in issue order).
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// Wait for the oldest staged step when `ahead` (uniform, <= A) newer steps of
+// D operations each have been issued after it.
+template <int D, int A>
+__device__ __forceinline__ void wait_step(int ahead) {
+  if constexpr (A == 0) {
+    wait_vm<0>();
+  } else {
+    if (ahead >= A)
+      wait_vm<A * D>();
+    else
+      wait_step<D, A - 1>(ahead);
+  }
+}
 
 // Bounds-checked element loads (ragged tail, unaligned rows); positions past
 // `hi` read as -inf on both sides and are masked out of every statistic.
@@ -265,20 +370,29 @@ __device__ __forceinline__ uint32_t load_checked(uint32_t (&ua)[8], uint32_t (&u
 // ---------------------------------------------------------------- rare work
 
 // Move the exp2 reference when a logit outgrows it (rare after the first step).
+// The reference and the gate stay wave-uniform, in scalar registers.
 __device__ __forceinline__ void rescale(WaveState &st, float gm) {
   const float wm = uniform(wave_max(gm));
-  const float nh = wm * kL2E;
+  const float nh = uniform(wm * kL2E);
   const bool huge = fabsf(nh) >= 268435456.0f && isfinite(nh);
-  const float nl = huge ? fmaf(wm, kL2E, -nh) : 0.0f;
-  if (st.r2h > -INFINITY) {
-    const double sc = exp2(((double)st.r2h + (double)st.r2l) - ((double)nh + (double)nl));
-    st.s *= sc;
-    st.d *= sc;
-    st.f *= sc;
-  }
+  const float nl = uniform(huge ? fmaf(wm, kL2E, -nh) : 0.0f);
+  // before the first reference the sums are still 0
+  const double sc =
+      st.r2h > -INFINITY ? exp2(((double)st.r2h + (double)st.r2l) - ((double)nh + (double)nl)) : 0.0;
+  st.s *= sc;
+  st.d *= sc;
+  st.f *= sc;
   st.r2h = nh;
+  st.nr2h = -nh;
   st.r2l = nl;
-  st.gate = (nh + kRescaleLog2) * (1.0f / kL2E);
+  st.gate = uniform((nh + kRescaleLog2) * (1.0f / kL2E));
+}
+
+// Column of element j of a lane inside its step (j may be any value in [0, 8)).
+template <bool MAPB>
+__device__ __forceinline__ int lane_offset_dyn(int lane, int j) {
+  if (MAPB) return 8 * lane + j;
+  return 4 * lane + j + (j >= 4 ? 252 : 0);
 }
 
 // ---------------------------------------------------------------- one wave step
@@ -309,34 +423,58 @@ __device__ __forceinline__ void process_step(const uint32_t (&ua)[8], const uint
   float sg = 0.0f, dg = 0.0f, fg = 0.0f;
   float sab = 0.0f, ssd = 0.0f, ssb = 0.0f;
   if (CMP) {
-    float s0 = 0.0f, s1 = 0.0f, d0 = 0.0f, d1 = 0.0f, f0 = 0.0f, f1 = 0.0f;
+    // e*phi(delta) = (e*delta) * R(delta), R(d) = d/2 - d^2/6 + d^3/24; the
+    // dropped d^4/120 term is below 3.3e-5 of R for |d| <= 1/8
+    float s0, s1, d0, d1, f0, f1;
 #pragma unroll
     for (int j = 0; j < 8; j += 2) {
-      const float e0 = __builtin_amdgcn_exp2f(fmaf(xa[j], kL2E, -st.r2h));
-      const float e1 = __builtin_amdgcn_exp2f(fmaf(xa[j + 1], kL2E, -st.r2h));
+      const float e0 = __builtin_amdgcn_exp2f(fmaf(xa[j], kL2E, st.nr2h));
+      const float e1 = __builtin_amdgcn_exp2f(fmaf(xa[j + 1], kL2E, st.nr2h));
       const float ed0 = e0 * d[j], ed1 = e1 * d[j + 1];
-      s0 += e0;
-      s1 += e1;
-      d0 += ed0;
-      d1 += ed1;
-      f0 = fmaf(ed0 * d[j], phi_over_d2(d[j]), f0);
-      f1 = fmaf(ed1 * d[j + 1], phi_over_d2(d[j + 1]), f1);
+      const float r0 = d[j] * fmaf(d[j], fmaf(d[j], 1.0f / 24.0f, -1.0f / 6.0f), 0.5f);
+      const float r1 = d[j + 1] * fmaf(d[j + 1], fmaf(d[j + 1], 1.0f / 24.0f, -1.0f / 6.0f), 0.5f);
+      if (j == 0) {
+        s0 = e0;
+        s1 = e1;
+        d0 = ed0;
+        d1 = ed1;
+        f0 = ed0 * r0;
+        f1 = ed1 * r1;
+      } else {
+        s0 += e0;
+        s1 += e1;
+        d0 += ed0;
+        d1 += ed1;
+        f0 = fmaf(ed0, r0, f0);
+        f1 = fmaf(ed1, r1, f1);
+      }
     }
     sg = s0 + s1;
     dg = d0 + d1;
     fg = f0 + f1;
   }
   if (BITS) {
+    sab = fabsf(d[0]);
+    ssd = d[0] * d[0];
+    ssb = xa[0] * xa[0];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
+    for (int j = 1; j < 8; ++j) {
       sab += fabsf(d[j]);
       ssd = fmaf(d[j], d[j], ssd);
       ssb = fmaf(xa[j], xa[j], ssb);
     }
   }
+  // Every special value reaches a NaN or an infinity in the checked sums:
+  // with the comparison, a NaN or inf on either side makes delta NaN or
+  // infinite (sab, or dg alone), a huge baseline makes sum a^2 infinite, and
+  // |delta| <= 1/8 bounds sum delta^2.
   bool ok = !tail;
-  if (CMP) ok = ok && st.r2l == 0.0f && (dmax <= kPolyMax) && (dg == dg);
-  if (BITS) ok = ok && isfinite(sab) && isfinite(ssd) && isfinite(ssb);
+  if (CMP && BITS)
+    ok = ok && st.r2l == 0.0f && (dmax <= kPolyMax) && isfinite(sab + ssb);
+  else if (CMP)
+    ok = ok && st.r2l == 0.0f && (dmax <= kPolyMax) && (dg == dg);
+  else if (BITS)
+    ok = ok && isfinite(sab + ssd + ssb);
 
   if (ok) {
     if (CMP) {
@@ -423,30 +561,38 @@ __device__ __forceinline__ void process_step(const uint32_t (&ua)[8], const uint
         st.tau_a = rank_key_inv(T);
         st.tau_i = kTauLaneMax;
       }
-      // at most 8 appends per passing lane: make room first if that could overflow
-      if (st.cnt + 8 * __popcll(ballot(ga >= st.tau_a)) > kCapW) flush_candidates(ba, bi, st, kint);
+      // at most 4 appends per passing lane and half step: make room first if
+      // that could overflow
+      const int npass = __popcll(ballot(ga >= st.tau_a));
+      if (st.cnt + 4 * npass > kCapW) flush_candidates(ba, bi, st, kint);
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        const int idx = base + lane_offset<MAPB>(lane, j);
-        const bool pass = ((valid >> j) & 1u) &&
-                          (xa[j] > st.tau_a || (xa[j] == st.tau_a && idx < st.tau_i));
-        const uint64_t m = ballot(pass);
-        if (pass) {
-          const int pos = st.cnt + prefix_count(m);
-          ba[pos] = xa[j];
-          bi[pos] = idx;
+        if (j == 4 && st.cnt + 4 * npass > kCapW) flush_candidates(ba, bi, st, kint);
+        // value test first; the index test at equal values only when some
+        // lane reaches the threshold with element j
+        if (ballot(((valid >> j) & 1u) && xa[j] >= st.tau_a)) {
+          const int idx = base + lane_offset<MAPB>(lane, j);
+          const bool pass = ((valid >> j) & 1u) &&
+                            (xa[j] > st.tau_a || (xa[j] == st.tau_a && idx < st.tau_i));
+          const uint64_t m = ballot(pass);
+          if (pass) {
+            const int pos = st.cnt + prefix_count(m);
+            ba[pos] = xa[j];
+            bi[pos] = idx;
+          }
+          st.cnt += __popcll(m);
         }
-        st.cnt += __popcll(m);
       }
       if (st.cnt > kFlushAt) flush_candidates(ba, bi, st, kint);
     }
     // candidate argmax, lowest index on ties (steps of a wave ascend in index)
     if (ballot(gb > st.bmax)) {
       const float wm = uniform(wave_max(gb));
-      int li = 0x7fffffff;
+      int js = 8;  // first element of this lane equal to the maximum
 #pragma unroll
       for (int j = 7; j >= 0; --j)
-        if (((valid >> j) & 1u) && xb[j] == wm) li = base + lane_offset<MAPB>(lane, j);
+        if (((valid >> j) & 1u) && xb[j] == wm) js = j;
+      const int li = js < 8 ? base + lane_offset_dyn<MAPB>(lane, js) : 0x7fffffff;
       st.bmax = wm;
       st.bidx = uniform(wave_min(li));
     }
@@ -468,10 +614,11 @@ __device__ __forceinline__ void process_step(const uint32_t (&ua)[8], const uint
       st.max_ulp = max(st.max_ulp, (int32_t)x < 0 ? cross : same);
     }
     if (st.first < 0 && any) {
-      int li = 0x7fffffff;
+      int js = 8;  // first differing element of this lane
 #pragma unroll
       for (int j = 7; j >= 0; --j)
-        if (ua[j] != ub[j]) li = base + lane_offset<MAPB>(lane, j);
+        if (ua[j] != ub[j]) js = j;
+      const int li = js < 8 ? base + lane_offset_dyn<MAPB>(lane, js) : 0x7fffffff;
       st.first = uniform(wave_min(li));
     }
   }
@@ -480,17 +627,23 @@ __device__ __forceinline__ void process_step(const uint32_t (&ua)[8], const uint
 // ---------------------------------------------------------------- kernel
 
 template <int TA, int TB, bool CMP, bool BITS, bool VEC>
-__global__ __launch_bounds__(kBlock) void k_row_stats(StreamArgs args) {
+__global__ __launch_bounds__((Shape<TA, TB, CMP, VEC>::W * kWave)) void k_row_stats(StreamArgs args) {
+  using SH = Shape<TA, TB, CMP, VEC>;
   constexpr bool MAPB = (TA == 1 && TB == 1);
   constexpr bool W16 = (TA == 1 && TB == 1);
-  constexpr int SA = TA == 1 ? 2 : 4, SB = TB == 1 ? 2 : 4;
-  __shared__ float s_ba[kWavesPerBlock][CMP ? kCapW : 1];
-  __shared__ int s_bi[kWavesPerBlock][CMP ? kCapW : 1];
+  constexpr int SA = SH::SA, SB = SH::SB;
+  constexpr int kStepA = SH::kStepA, kStepB = SH::kStepB;
+  constexpr bool RING = SH::RING;
+  constexpr int R = SH::R, W = SH::W;
+  constexpr int kRingBytes = RING ? R * SH::kStep : 16;
+  __shared__ float s_ba[W][CMP ? kCapW : 1];
+  __shared__ int s_bi[W][CMP ? kCapW : 1];
+  __shared__ __attribute__((aligned(16))) char s_ring[W][kRingBytes];
 
   // every quantity derived from the wave id is uniform: keep it scalar
   const int wid = __builtin_amdgcn_readfirstlane((int)(threadIdx.x / kWave));
   const int lane = lane_id();
-  const int64_t item = (int64_t)blockIdx.x * kWavesPerBlock + wid;
+  const int64_t item = (int64_t)blockIdx.x * W + wid;
   if (item >= args.n * args.nchunks) return;
   const int64_t row = item / args.nchunks;
   const int chunk = (int)(item - row * args.nchunks);
@@ -506,6 +659,7 @@ __global__ __launch_bounds__(kBlock) void k_row_stats(StreamArgs args) {
   WaveState st;
   st.s = st.d = st.f = 0.0;
   st.r2h = -INFINITY;
+  st.nr2h = INFINITY;
   st.r2l = 0.0f;
   st.gate = -INFINITY;
   st.bmax = -INFINITY;
@@ -523,7 +677,55 @@ __global__ __launch_bounds__(kBlock) void k_row_stats(StreamArgs args) {
   st.nfa = st.nfb = 0;
 
   const int nfull = (hi - lo) / kSpan;
-  if (VEC) {
+  if constexpr (RING) {
+    // Full steps stream through a per-wave LDS ring: R - 1 steps are in
+    // flight (global -> LDS, no registers held) while one is processed.  A
+    // register-staged prefetch would have to be copied between register sets
+    // at every step, and that copy waits for the newest load.
+    constexpr int kStep = SH::kStep;
+    constexpr int D = kStep / 1024;  // DMA operations per step
+    char *ring = s_ring[wid];
+    const uint32_t ring_lds = (uint32_t)(uintptr_t)ring;
+    const char *pa = ra + (int64_t)lo * SA, *pb = rb + (int64_t)lo * SB;
+    const uint32_t voff = 16u * (uint32_t)lane;
+    const int npre = nfull < R - 1 ? nfull : R - 1;
+#pragma unroll 1
+    for (int q = 0; q < npre; ++q) {
+      const uint32_t l = ring_lds + (uint32_t)(q * kStep);
+      const char *ga = pa + (int64_t)q * kStepA, *gb = pb + (int64_t)q * kStepB;
+#pragma unroll
+      for (int c = 0; c < kStepA / 1024; ++c) dma_1k(ga + 1024 * c, voff, l + 1024u * c);
+#pragma unroll
+      for (int c = 0; c < kStepB / 1024; ++c) dma_1k(gb + 1024 * c, voff, l + kStepA + 1024u * c);
+    }
+    int rd = 0;      // slot of step sp
+    int wr = R - 1;  // slot of step sp + R - 1
+#pragma unroll 1
+    for (int sp = 0; sp < nfull; ++sp) {
+      const int q = sp + R - 1;
+      if (q < nfull) {
+        const uint32_t l = ring_lds + (uint32_t)(wr * kStep);
+        const char *ga = pa + (int64_t)q * kStepA, *gb = pb + (int64_t)q * kStepB;
+#pragma unroll
+        for (int c = 0; c < kStepA / 1024; ++c) dma_1k(ga + 1024 * c, voff, l + 1024u * c);
+#pragma unroll
+        for (int c = 0; c < kStepB / 1024; ++c) dma_1k(gb + 1024 * c, voff, l + kStepA + 1024u * c);
+      }
+      // steps issued after this one
+      const int ahead = nfull - 1 - sp < R - 1 ? nfull - 1 - sp : R - 1;
+      wait_step<D, R - 1>(ahead);
+      Raw<TA, TB> cur;
+      const char *slot = ring + rd * kStep;
+      cur.load_lds(slot, slot + kStepA, (uint32_t)lane);
+      uint32_t ua[8], ub[8];
+      cur.a.decode(ua);
+      cur.b.decode(ub);
+      process_step<CMP, BITS, W16, MAPB>(ua, ub, 0xffu, false, lo + sp * kSpan, lane, kint, st, ba,
+                                         bi);
+      rd = rd + 1 == R ? 0 : rd + 1;
+      wr = wr + 1 == R ? 0 : wr + 1;
+    }
+  } else if constexpr (VEC) {
     // Two register sets: while one step is processed the next one's loads are
     // in flight.  The prefetch is unconditional (the last step is fetched
     // twice): a load under a branch makes the wait before the current step's
@@ -613,14 +815,20 @@ __global__ __launch_bounds__(kBlock) void k_row_stats(StreamArgs args) {
 
 // ---------------------------------------------------------------- launcher
 
+template <int TA, int TB, bool CMP, bool BITS, bool VEC>
+static void launch_shape(const StreamArgs &a, hipStream_t stream) {
+  constexpr int W = Shape<TA, TB, CMP, VEC>::W;
+  const int64_t items = a.n * a.nchunks;
+  const dim3 grid((unsigned)((items + W - 1) / W));
+  hipLaunchKernelGGL((k_row_stats<TA, TB, CMP, BITS, VEC>), grid, dim3(W * kWave), 0, stream, a);
+}
+
 template <int TA, int TB, bool CMP, bool BITS>
 static hipError_t launch_typed(const StreamArgs &a, bool vec, hipStream_t stream) {
-  const int64_t items = a.n * a.nchunks;
-  const dim3 grid((unsigned)((items + kWavesPerBlock - 1) / kWavesPerBlock));
   if (vec)
-    hipLaunchKernelGGL((k_row_stats<TA, TB, CMP, BITS, true>), grid, dim3(kBlock), 0, stream, a);
+    launch_shape<TA, TB, CMP, BITS, true>(a, stream);
   else
-    hipLaunchKernelGGL((k_row_stats<TA, TB, CMP, BITS, false>), grid, dim3(kBlock), 0, stream, a);
+    launch_shape<TA, TB, CMP, BITS, false>(a, stream);
   return hipGetLastError();
 }
 
