@@ -423,30 +423,31 @@ __device__ __forceinline__ void process_step(const uint32_t (&ua)[8], const uint
   float sg = 0.0f, dg = 0.0f, fg = 0.0f;
   float sab = 0.0f, ssd = 0.0f, ssb = 0.0f;
   if (CMP) {
-    // e*phi(delta) = (e*delta) * R(delta), R(d) = d/2 - d^2/6 + d^3/24; the
-    // dropped d^4/120 term is below 3.3e-5 of R for |d| <= 1/8
+    // e*phi(delta) = (e*delta^2) * P(delta), P(d) = 1/2 - d/6 + d^2/24; the
+    // dropped d^3/120 term is below 3.3e-5 of P for |d| <= 1/8.  delta^2 is
+    // shared with the bitwise sum of squared differences.
     float s0, s1, d0, d1, f0, f1;
 #pragma unroll
     for (int j = 0; j < 8; j += 2) {
       const float e0 = __builtin_amdgcn_exp2f(fmaf(xa[j], kL2E, st.nr2h));
       const float e1 = __builtin_amdgcn_exp2f(fmaf(xa[j + 1], kL2E, st.nr2h));
-      const float ed0 = e0 * d[j], ed1 = e1 * d[j + 1];
-      const float r0 = d[j] * fmaf(d[j], fmaf(d[j], 1.0f / 24.0f, -1.0f / 6.0f), 0.5f);
-      const float r1 = d[j + 1] * fmaf(d[j + 1], fmaf(d[j + 1], 1.0f / 24.0f, -1.0f / 6.0f), 0.5f);
+      const float q0 = (d[j] * d[j]) * fmaf(d[j], fmaf(d[j], 1.0f / 24.0f, -1.0f / 6.0f), 0.5f);
+      const float q1 =
+          (d[j + 1] * d[j + 1]) * fmaf(d[j + 1], fmaf(d[j + 1], 1.0f / 24.0f, -1.0f / 6.0f), 0.5f);
       if (j == 0) {
         s0 = e0;
         s1 = e1;
-        d0 = ed0;
-        d1 = ed1;
-        f0 = ed0 * r0;
-        f1 = ed1 * r1;
+        d0 = e0 * d[j];
+        d1 = e1 * d[j + 1];
+        f0 = e0 * q0;
+        f1 = e1 * q1;
       } else {
         s0 += e0;
         s1 += e1;
-        d0 += ed0;
-        d1 += ed1;
-        f0 = fmaf(ed0, r0, f0);
-        f1 = fmaf(ed1, r1, f1);
+        d0 = fmaf(e0, d[j], d0);
+        d1 = fmaf(e1, d[j + 1], d1);
+        f0 = fmaf(e0, q0, f0);
+        f1 = fmaf(e1, q1, f1);
       }
     }
     sg = s0 + s1;
@@ -460,7 +461,7 @@ __device__ __forceinline__ void process_step(const uint32_t (&ua)[8], const uint
 #pragma unroll
     for (int j = 1; j < 8; ++j) {
       sab += fabsf(d[j]);
-      ssd = fmaf(d[j], d[j], ssd);
+      ssd += d[j] * d[j];
       ssb = fmaf(xa[j], xa[j], ssb);
     }
   }
@@ -627,7 +628,8 @@ __device__ __forceinline__ void process_step(const uint32_t (&ua)[8], const uint
 // ---------------------------------------------------------------- kernel
 
 template <int TA, int TB, bool CMP, bool BITS, bool VEC>
-__global__ __launch_bounds__((Shape<TA, TB, CMP, VEC>::W * kWave)) void k_row_stats(StreamArgs args) {
+__global__ __launch_bounds__((Shape<TA, TB, CMP, VEC>::W * kWave))
+__attribute__((amdgpu_waves_per_eu(4, 8))) void k_row_stats(StreamArgs args) {
   using SH = Shape<TA, TB, CMP, VEC>;
   constexpr bool MAPB = (TA == 1 && TB == 1);
   constexpr bool W16 = (TA == 1 && TB == 1);
