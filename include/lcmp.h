@@ -187,6 +187,10 @@ int lcmp_bitdiff(const void *a, int ta, int64_t lda, const void *b, int tb, int6
 
 /* ---------------------------------------------------------------- margin bins */
 
+#define LCMP_MAX_BIN_ROWS (1LL << 36) /* largest n of lcmp_bin_report */
+
+/* Workspace of lcmp_bin_report for n rows; 0 when n, n_groups or n_edges are
+ * out of range. */
 size_t lcmp_bin_workspace_bytes(int64_t n, int n_groups, int n_edges);
 
 /*
@@ -202,7 +206,8 @@ size_t lcmp_bin_workspace_bytes(int64_t n, int n_groups, int n_edges);
  *   big_margin   threshold of the stop rule (the page uses 1): a flip with
  *            margin > big_margin is counted in big_margin_flips.
  *   bins     device [n_groups * n_edges]; summary device [n_groups].
- * Sums are formed in a fixed order, so repeated calls are bit-identical.
+ * n above LCMP_MAX_BIN_ROWS returns LCMP_ESHAPE.  Sums are formed in a fixed
+ * order, so repeated calls are bit-identical.
  */
 int lcmp_bin_report(const double *margin, const uint8_t *flip, const double *kl_topk,
                     const double *kl_full, const uint8_t *status, const int32_t *group,

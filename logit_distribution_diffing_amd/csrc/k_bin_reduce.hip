@@ -3,10 +3,11 @@
 // flips are judged per margin bin, and a flip at a large margin is a stop).
 //
 // Two levels with a fixed order, so repeated calls are bit-identical:
-//   level 1: one wave per block of 256 rows; each 64-row batch is split by
-//            bin, every bin's values are summed with a fixed butterfly and
-//            added to the block's LDS accumulator in batch order; integer
-//            counts go through LDS atomics (exact, order-free).
+//   level 1: one wave per block of 64..2048 rows (more with more bins);
+//            each 64-row batch is split by bin, every bin's values are
+//            summed with a fixed butterfly and added to the block's LDS
+//            accumulator in batch order; integer counts go through LDS
+//            atomics (exact, order-free).
 //   level 2: one wave per bin (and per group) adds the block partials in a
 //            fixed lane-then-butterfly order.
 #include "common.hpp"
@@ -31,8 +32,8 @@ __global__ __launch_bounds__(kWave) void k_bin_partial(BinArgs a) {
   for (int g = lane; g < a.n_groups; g += kWave) grp[g][0] = grp[g][1] = grp[g][2] = 0ull;
   __syncthreads();
 
-  const int64_t r0 = (int64_t)blockIdx.x * kBinRowsPerBlock;
-  const int64_t r1 = min(a.n, r0 + kBinRowsPerBlock);
+  const int64_t r0 = (int64_t)blockIdx.x * a.rows;
+  const int64_t r1 = min(a.n, r0 + a.rows);
   for (int64_t base = r0; base < r1; base += kWave) {
     const int64_t r = base + lane;
     int bin = -1;  // flat bin id, or -1 when this lane adds to no bin

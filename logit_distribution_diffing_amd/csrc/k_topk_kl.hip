@@ -25,23 +25,87 @@ __device__ __forceinline__ void wave_fence2() {
 }
 
 __global__ __launch_bounds__(kWave) void k_topk_kl(FinalArgs a) {
-  extern __shared__ uint32_t smem[];
+  extern __shared__ __attribute__((aligned(16))) uint32_t smem[];
   const int lane = lane_id();
   const int64_t row = blockIdx.x;
   const int C = a.nchunks;
   const int kint = a.kint;
-  const int mcap = C * kint;
-  uint32_t *e_key = smem;                          // [mcap]
-  int32_t *e_idx = (int32_t *)(e_key + mcap);      // [mcap]
-  float *s_a = (float *)(e_idx + mcap);            // [kMaxK] sorted
-  int32_t *s_i = (int32_t *)(s_a + kMaxK);
+  const int mcap = C * kint;            // top-k slots of the row's chunks
+  const int mpad = (mcap + 3) & ~3;     // padded to whole 16-byte reads
+  uint32_t *e_key = smem;                          // [mpad]
+  int32_t *e_idx = (int32_t *)(e_key + mpad);      // [mpad]
+  float *s_a = (float *)(e_idx + mpad);            // [kMaxK] sorted
+  int32_t *s_i = (int32_t *)(s_a + kMaxK);         // [kMaxK]
+  int32_t *s_cnt = s_i + kMaxK;                    // [kMaxChunks]
 
-  if (a.bd) merge_bits(a.bits + row * C, C, a.v, a.bd + row);
-
-  // ---- chunk sums, rescaled to the largest reference
+  // ---- every load that does not depend on another goes out first: the chunk
+  // records, the bitwise chunk records and all top-k slots (the slots past a
+  // chunk's count are masked below)
   const bool has = lane < C;
   ChunkStats cs;
   if (has) cs = a.stats[row * C + lane];
+  ChunkBits cb;
+  cb.ndiff = 0;
+  cb.first = -1;
+  cb.nfa = cb.nfb = 0;
+  cb.max_ulp = 0;
+  cb.max_abs = 0.0;
+  cb.sum_abs = cb.ssd = cb.ssb = 0.0;
+  if (a.bd && has) cb = a.bits[row * C + lane];
+  const int64_t tb = row * (int64_t)mcap;
+  float v0 = 0.0f;
+  int x0 = 0;
+  if (lane < mcap) {
+    v0 = a.ta[tb + lane];
+    x0 = a.ti[tb + lane];
+  }
+  if (has) s_cnt[lane] = cs.cnt;
+  wave_fence2();
+  // slot e holds entry (e mod kint) of chunk e / kint; empty slots get key 0,
+  // below every stored key, and sort last
+  for (int e = lane; e < mpad; e += kWave) {
+    float v = v0;
+    int x = x0;
+    if (e >= kWave && e < mcap) {
+      v = a.ta[tb + e];
+      x = a.ti[tb + e];
+    }
+    const int c = e / kint;
+    const bool ok = e < mcap && e - c * kint < s_cnt[c];
+    e_key[e] = ok ? rank_key(v) : 0u;
+    e_idx[e] = ok ? x : 0x7fffffff;
+  }
+  for (int j = lane; j < kMaxK; j += kWave) {
+    s_a[j] = -INFINITY;
+    s_i[j] = -1;
+  }
+
+  if (a.bd) {
+    const int64_t ndiff = wave_sum(cb.ndiff);
+    const int64_t first = wave_min(cb.first >= 0 ? cb.first : INT64_MAX);
+    const int64_t nfa = wave_sum(cb.nfa), nfb = wave_sum(cb.nfb);
+    const uint32_t mu = wave_max(cb.max_ulp);
+    const double ma = wave_max(cb.max_abs);
+    const double sab = wave_sum(cb.sum_abs), ssd = wave_sum(cb.ssd), ssb = wave_sum(cb.ssb);
+    if (lane == 0) {
+      BitdiffRow r;
+      r.ndiff = ndiff;
+      r.first_diff = first == INT64_MAX ? -1 : first;
+      r.nonfinite_a = nfa;
+      r.nonfinite_b = nfb;
+      r.max_ulp = mu;
+      r.pad_ = 0;
+      r.max_abs = ma;
+      r.sum_abs = sab;
+      r.sum_sq_diff = ssd;
+      r.sum_sq_base = ssb;
+      r.mean_abs = sab / (double)a.v;
+      r.rel_l2 = ssb > 0.0 ? sqrt(ssd / ssb) : (ssd > 0.0 ? INFINITY : 0.0);
+      a.bd[row] = r;
+    }
+  }
+
+  // ---- chunk sums, rescaled to the largest reference
   const double r2 = has ? cs.r2 : -INFINITY;
   const double M2 = wave_max(r2);
   const int nb = wave_sum(has ? cs.n_bad : 0);
@@ -81,37 +145,23 @@ __global__ __launch_bounds__(kWave) void k_topk_kl(FinalArgs a) {
   const int bx = wave_min((has && cs.bidx >= 0 && bm == BM) ? cs.bidx : 0x7fffffff);
   const int top1_cand = bx == 0x7fffffff ? -1 : bx;
 
-  // ---- gather the chunk top-k sets
-  int off = 0, m = 0;
-  for (int c = 0; c < C; ++c) {
-    const int cc = __shfl(has ? cs.cnt : 0, c, kWave);
-    if (c < lane) off += cc;
-    m += cc;
-  }
-  for (int c = 0; c < C; ++c) {
-    const int cc = __shfl(has ? cs.cnt : 0, c, kWave);
-    const int oc = __shfl(off, c, kWave);
-    const int64_t src = (row * C + c) * kint;
-    for (int j = lane; j < cc; j += kWave) {
-      e_key[oc + j] = rank_key(a.ta[src + j]);
-      e_idx[oc + j] = a.ti[src + j];
-    }
-  }
-  for (int j = lane; j < kMaxK; j += kWave) {
-    s_a[j] = -INFINITY;
-    s_i[j] = -1;
-  }
+  // ---- rank of every slot among all slots (keys are distinct through the
+  // index; the valid slots number at least kint, so only they get ranks
+  // below kint), four slots per broadcast read
   wave_fence2();
-  // rank of each entry among all entries (keys are distinct through the index)
-  for (int e = lane; e < m; e += kWave) {
+  for (int e = lane; e < mpad; e += kWave) {
     const uint32_t ke = e_key[e];
     const int ie = e_idx[e];
     int rank = 0;
-    for (int f = 0; f < m; ++f) {
-      const uint32_t kf = e_key[f];
-      rank += (kf > ke || (kf == ke && e_idx[f] < ie)) ? 1 : 0;
+    for (int f = 0; f < mpad; f += 4) {
+      const uint4 k4 = *(const uint4 *)(e_key + f);
+      const int4 i4 = *(const int4 *)(e_idx + f);
+      rank += (k4.x > ke || (k4.x == ke && i4.x < ie)) ? 1 : 0;
+      rank += (k4.y > ke || (k4.y == ke && i4.y < ie)) ? 1 : 0;
+      rank += (k4.z > ke || (k4.z == ke && i4.z < ie)) ? 1 : 0;
+      rank += (k4.w > ke || (k4.w == ke && i4.w < ie)) ? 1 : 0;
     }
-    if (rank < kint) {
+    if (rank < kint && ke != 0u) {
       s_a[rank] = rank_key_inv(ke);
       s_i[rank] = ie;
     }
@@ -124,7 +174,9 @@ __global__ __launch_bounds__(kWave) void k_topk_kl(FinalArgs a) {
   const float ha = in_head ? s_a[lane] : -INFINITY;
   // gather the candidate logit at each head index
   float hb = -INFINITY;
-  if (in_head) {
+  // every chunk stores min(kint, its length) entries, so the merged head is
+  // full; the index test only keeps a damaged record from reading outside the row
+  if (in_head && s_i[lane] >= 0 && (int64_t)s_i[lane] < a.v) {
     const int64_t off = row * a.ldc + s_i[lane];
     hb = a.tc == 1 ? __uint_as_float((uint32_t)((const uint16_t *)a.cand)[off] << 16)
                    : ((const float *)a.cand)[off];
@@ -194,8 +246,8 @@ __global__ __launch_bounds__(kWave) void k_topk_kl(FinalArgs a) {
 
 hipError_t launch_topk_kl(const FinalArgs &a, hipStream_t stream) {
   if (a.n == 0) return hipSuccess;
-  const size_t mcap = (size_t)a.nchunks * a.kint;
-  const size_t shmem = mcap * 8 + (size_t)kMaxK * 8;
+  const size_t mpad = ((size_t)a.nchunks * a.kint + 3) & ~(size_t)3;
+  const size_t shmem = mpad * 8 + (size_t)kMaxK * 8 + (size_t)kMaxChunks * 4;
   hipLaunchKernelGGL(k_topk_kl, dim3((unsigned)a.n), dim3(kWave), shmem, stream, a);
   return hipGetLastError();
 }

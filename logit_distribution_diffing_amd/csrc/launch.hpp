@@ -58,7 +58,17 @@ struct GroupAcc {
   int64_t big_margin_flips, excluded, unbinned;
 };
 
-constexpr int kBinRowsPerBlock = 256;  // rows of one level-1 block (one wave)
+// Largest row count of a bin report (level-1 block count stays in 32 bits).
+constexpr int64_t kMaxBinRows = (int64_t)1 << 36;  // LCMP_MAX_BIN_ROWS
+
+// Rows of one level-1 block (one wave): small blocks spread short reports over
+// many CUs; with many bins the block grows so the partials it writes stay
+// smaller than the rows it reads.
+__host__ __device__ inline int bin_rows_per_block(int nbins) {
+  int r = 64;
+  while (r < 3 * nbins && r < 2048) r *= 2;
+  return r;
+}
 constexpr int kMaxBins = 256;           // n_groups * n_edges
 constexpr int kMaxGroups = 256;
 constexpr int kMaxEdges = 32;
@@ -74,6 +84,7 @@ struct BinArgs {
   BinAcc *part_bins;      // [nblk * n_groups * n_edges]
   GroupAcc *part_groups;  // [nblk * n_groups]
   int32_t nblk;
+  int32_t rows;           // rows per level-1 block
   BinAcc *bins;           // [n_groups * n_edges]
   GroupAcc *groups;       // [n_groups]
 };

@@ -14,7 +14,8 @@ static_assert(sizeof(lcmp_bitdiff_row) == sizeof(BitdiffRow), "bitdiff row layou
 static_assert(sizeof(lcmp_bin) == sizeof(BinAcc), "bin layout");
 static_assert(sizeof(lcmp_group_summary) == sizeof(GroupAcc), "group summary layout");
 static_assert(kMaxGroups == LCMP_MAX_GROUPS && kMaxBins == LCMP_MAX_BINS &&
-                  kMaxEdges == LCMP_MAX_EDGES && kMaxK == LCMP_MAX_K,
+                  kMaxEdges == LCMP_MAX_EDGES && kMaxK == LCMP_MAX_K &&
+                  kMaxBinRows == LCMP_MAX_BIN_ROWS,
               "limits of the header and of the kernels agree");
 
 namespace {
@@ -249,10 +250,11 @@ int lcmp_bitdiff(const void *a, int ta, int64_t lda, const void *b, int tb, int6
 }
 
 size_t lcmp_bin_workspace_bytes(int64_t n, int n_groups, int n_edges) {
-  if (n < 0 || n_groups < 1 || n_groups > kMaxGroups || n_edges < 1 || n_edges > kMaxEdges ||
+  if (n < 0 || n > kMaxBinRows || n_groups < 1 || n_groups > kMaxGroups || n_edges < 1 || n_edges > kMaxEdges ||
       n_groups * n_edges > kMaxBins)
     return 0;
-  const int64_t nblk = (n + kBinRowsPerBlock - 1) / kBinRowsPerBlock;
+  const int rows = bin_rows_per_block(n_groups * n_edges);
+  const int64_t nblk = (n + rows - 1) / rows;
   return align_up((size_t)nblk * (size_t)n_groups * n_edges * sizeof(BinAcc)) +
          align_up((size_t)nblk * (size_t)n_groups * sizeof(GroupAcc)) + kAlign;
 }
@@ -263,8 +265,8 @@ int lcmp_bin_report(const double *margin, const uint8_t *flip, const double *kl_
                     lcmp_bin *bins, lcmp_group_summary *summary, void *workspace,
                     size_t ws_bytes, void *stream) {
   if (n < 0 || !bins || !summary || !edges) return LCMP_EINVAL;
-  if (n_groups < 1 || n_groups > kMaxGroups || n_edges < 1 || n_edges > kMaxEdges ||
-      n_groups * n_edges > kMaxBins)
+  if (n > kMaxBinRows || n_groups < 1 || n_groups > kMaxGroups || n_edges < 1 ||
+      n_edges > kMaxEdges || n_groups * n_edges > kMaxBins)
     return LCMP_ESHAPE;
   for (int j = 0; j < n_edges; ++j) {
     if (isnan(edges[j]) || !(edges[j] > 0.0)) return LCMP_EEDGES;
@@ -275,7 +277,8 @@ int lcmp_bin_report(const double *margin, const uint8_t *flip, const double *kl_
   const size_t need = lcmp_bin_workspace_bytes(n, n_groups, n_edges);
   if (!workspace || ws_bytes < need) return LCMP_EWORKSPACE;
   if ((uintptr_t)workspace % 16 != 0) return LCMP_EINVAL;
-  const int64_t nblk = (n + kBinRowsPerBlock - 1) / kBinRowsPerBlock;
+  const int rows = bin_rows_per_block(n_groups * n_edges);
+  const int64_t nblk = (n + rows - 1) / rows;
   BinArgs ba;
   memset(&ba, 0, sizeof ba);
   ba.margin = margin;
@@ -294,6 +297,7 @@ int lcmp_bin_report(const double *margin, const uint8_t *flip, const double *kl_
   ba.part_groups =
       (GroupAcc *)(ws + align_up((size_t)nblk * (size_t)n_groups * n_edges * sizeof(BinAcc)));
   ba.nblk = (int32_t)nblk;
+  ba.rows = rows;
   ba.bins = (BinAcc *)bins;
   ba.groups = (GroupAcc *)summary;
   if (launch_bin_reduce(ba, (hipStream_t)stream) != hipSuccess) return LCMP_EHIP;

@@ -56,6 +56,7 @@ def test_workspace_queries(L):
     assert lib.lcmp_bin_workspace_bytes(65536, 1, 6) > 0
     assert lib.lcmp_bin_workspace_bytes(10, 0, 6) == 0
     assert lib.lcmp_bin_workspace_bytes(10, 16, 17) == 0            # more than 256 bins
+    assert lib.lcmp_bin_workspace_bytes((1 << 36) + 1, 1, 6) == 0   # more rows than the limit
 
 
 FAKE = 0x10000  # a non-null address that is never dereferenced: every call below fails validation
@@ -131,6 +132,7 @@ def test_bin_report_argument_errors(L):
     assert call(ng=300) == -3
     assert call(ng=100, edges=(0.1, 0.5, 1.0)) == -3       # 300 bins
     assert call(n=-1) == -1
+    assert call(n=(1 << 36) + 1) == -3                     # more rows than LCMP_MAX_BIN_ROWS
     assert call(bins=None) == -1
     assert call(margin=None) == -1
     assert call(ws=None) == -4
