@@ -395,6 +395,29 @@ __device__ __forceinline__ int lane_offset_dyn(int lane, int j) {
   return 4 * lane + j + (j >= 4 ? 252 : 0);
 }
 
+// ---------------------------------------------------------------- ULP distance
+
+// Distance of two patterns in the ordered integer image: |ua - ub| when the
+// signs agree, ma + mb + 1 (through zero) when they differ.  bf16 patterns sit
+// in the upper half, so the same formula yields the bf16 distance << 16.
+template <bool W16>
+__device__ __forceinline__ uint32_t ulp_exact(uint32_t ua, uint32_t ub) {
+  const uint32_t same = sad_u32(ua, ub);
+  const uint32_t cross = ua + ub + (W16 ? 0x80010000u : 0x80000001u);
+  return (int32_t)(ua ^ ub) < 0 ? cross : same;
+}
+
+// The same distance for a pair with |a - b| <= 1/8 (both finite): then a pair
+// of opposite signs has both magnitudes at most 1/8 (patterns <= 0x3e000000),
+// so |ua - ub| >= 0x42000000, while a pair of equal signs stays below
+// 0x3e000001; the size of |ua - ub| tells the two cases apart.
+template <bool W16>
+__device__ __forceinline__ uint32_t ulp_close(uint32_t ua, uint32_t ub) {
+  const uint32_t same = sad_u32(ua, ub);
+  const uint32_t cross = ua + ub + (W16 ? 0x80010000u : 0x80000001u);
+  return same >= 0x42000000u ? cross : same;
+}
+
 // ---------------------------------------------------------------- one wave step
 
 template <bool CMP, bool BITS, bool W16, bool MAPB>
@@ -489,7 +512,15 @@ __device__ __forceinline__ void process_step(const uint32_t (&ua)[8], const uint
       st.ssb += (double)ssb;
       st.max_abs = max3f(st.max_abs, dmax, dmax);
     }
+    if (CMP && BITS) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) st.max_ulp = max(st.max_ulp, ulp_close<W16>(ua[j], ub[j]));
+    }
   } else {
+    if (CMP && BITS) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) st.max_ulp = max(st.max_ulp, ulp_exact<W16>(ua[j], ub[j]));
+    }
     // exact element-by-element path: special values, large differences,
     // huge logits, ragged tails
     float s2 = 0.0f, d2 = 0.0f, f2 = 0.0f;
@@ -600,19 +631,14 @@ __device__ __forceinline__ void process_step(const uint32_t (&ua)[8], const uint
   }
 
   if (BITS) {
-    // distance in the ordered integer image: |ua - ub| when the signs agree,
-    // ma + mb + 1 (through zero) when they differ; bf16 patterns sit in the
-    // upper half, so the same formula yields the bf16 distance << 16
+    // differing patterns (and, without the comparison, the ULP distance)
     uint64_t any = 0;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      const uint32_t x = ua[j] ^ ub[j];
-      const uint64_t m = ballot(x != 0u);
+      const uint64_t m = ballot(ua[j] != ub[j]);
       st.ndiff += __popcll(m);
       any |= m;
-      const uint32_t same = sad_u32(ua[j], ub[j]);
-      const uint32_t cross = ua[j] + ub[j] + (W16 ? 0x80010000u : 0x80000001u);
-      st.max_ulp = max(st.max_ulp, (int32_t)x < 0 ? cross : same);
+      if (!CMP) st.max_ulp = max(st.max_ulp, ulp_exact<W16>(ua[j], ub[j]));
     }
     if (st.first < 0 && any) {
       int js = 8;  // first differing element of this lane
