@@ -37,14 +37,27 @@ struct Chunking {
 };
 
 Chunking choose_chunks(int64_t n, int64_t v) {
+  // Split rows into c chunks when there are too few rows to fill the chip.
+  // Cost model: waves run in rounds of kResidentWaves (256 CUs x 16 waves);
+  // a chunk of s steps costs s + kChunkOverheadSteps.  Among c in
+  // [1, min(16, steps / 16)] take the cheapest, the smallest c on ties.  The
+  // choice depends only on (n, v), so results are repeatable.
+  constexpr int64_t kResidentWaves = 256 * 16;
+  constexpr int64_t kChunkOverheadSteps = 2;
   const int64_t steps = (v + kSpan - 1) / kSpan;
-  const int64_t target_items = 4 * 256 * 16;
-  int64_t c = n > 0 ? (target_items + n - 1) / n : 1;
-  const int64_t cmax = steps / 16 > 1 ? steps / 16 : 1;
-  if (c > cmax) c = cmax;
-  if (c > 16) c = 16;
-  if (c < 1) c = 1;
-  const int64_t per = (steps + c - 1) / c;
+  int64_t cmax = steps / 16;
+  if (cmax > 16) cmax = 16;
+  if (cmax < 1) cmax = 1;
+  int64_t best_c = 1, best_cost = -1;
+  for (int64_t c = 1; c <= cmax; ++c) {
+    const int64_t rounds = n > 0 ? (n * c + kResidentWaves - 1) / kResidentWaves : 1;
+    const int64_t cost = rounds * ((steps + c - 1) / c + kChunkOverheadSteps);
+    if (best_cost < 0 || cost < best_cost) {
+      best_cost = cost;
+      best_c = c;
+    }
+  }
+  const int64_t per = (steps + best_c - 1) / best_c;
   Chunking ch;
   ch.chunk = per * kSpan;
   ch.nchunks = (int32_t)((v + ch.chunk - 1) / ch.chunk);
