@@ -165,8 +165,10 @@ def copy_probe(nbytes: int):
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    # the first ~15 launches run while the clocks settle under the load, so
+    # the default warm-up covers them
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=30)
     ap.add_argument("--workload", default="corpus", choices=["corpus", "segment", "stream", "tiny"])
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -228,8 +230,11 @@ def main():
     kern_ms = [hip.elapsed_ms(a, b) for a, b in evs]
     kern_avg_s = sum(kern_ms) / len(kern_ms) / 1e3
     ms_per_step = gpu_ms / args.steps
+    srt = sorted(kern_ms)
     log(f"[bench] {args.steps} steps: {gpu_ms:.3f} ms on the stream, {wall * 1e3:.3f} ms wall; "
-        f"streaming kernel avg {kern_avg_s * 1e6:.1f} us (min {min(kern_ms) * 1e3:.1f} us)")
+        f"streaming kernel avg {kern_avg_s * 1e6:.1f} us (min {srt[0] * 1e3:.1f}, median "
+        f"{srt[len(srt) // 2] * 1e3:.1f}, max {srt[-1] * 1e3:.1f} us; first five "
+        f"{[round(x * 1e3) for x in kern_ms[:5]]})")
 
     b_np, s_np = L.unpack_bins(bins, summ)
     log(f"[bench] bins count {list(b_np[0]['count'])} flips {list(b_np[0]['flips'])} "
