@@ -44,7 +44,7 @@
 extern "C" {
 #endif
 
-#define LCMP_ABI_VERSION 1
+#define LCMP_ABI_VERSION 2
 #define LCMP_MAX_K 64       /* largest top-k */
 #define LCMP_MAX_EDGES 32   /* largest number of margin-bin edges */
 #define LCMP_MAX_GROUPS 256 /* largest number of row groups in lcmp_bin_report */
@@ -90,12 +90,20 @@ typedef enum {
  *             entries past min(k, v) are -1.
  *   status    0 or a mask of LCMP_ROW_* bits.  A flagged row reports NaN in the
  *             double fields, -1 in the index fields and 0 in flip.
+ *   target    optional INPUT, device [n]: the teacher-forced next token of each
+ *             position (the token the fixed text continues with).
+ *   logp_base, logp_cand   ln p(target) = a[target] - lse_base and
+ *             ln q(target) = b[target] - lse_cand, the only numbers perplexity
+ *             looks at ([logits] perplexity（困惑度）看不出这一级的差别).  Require
+ *             target; a target outside [0, v) or a flagged row gives NaN.
  */
 typedef struct {
   double *kl_topk, *kl_full, *margin, *lse_base, *lse_cand;
   int32_t *top1_base, *top2_base, *top1_cand;
   uint8_t *flip, *status;
   int32_t *topk_idx;
+  const int32_t *target;
+  double *logp_base, *logp_cand;
 } lcmp_row_out;
 
 /*

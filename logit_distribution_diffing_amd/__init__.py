@@ -40,10 +40,14 @@ class LcmpError(RuntimeError):
         super().__init__(f"{where}: {STATUS_NAMES.get(status, status)} ({msg})")
 
 
+ROW_OUT_FIELDS = ("kl_topk", "kl_full", "margin", "lse_base", "lse_cand", "top1_base",
+                  "top2_base", "top1_cand", "flip", "status", "topk_idx", "target", "logp_base",
+                  "logp_cand")
+
+
 class RowOut(ctypes.Structure):
-    _fields_ = [(n, ctypes.c_void_p) for n in (
-        "kl_topk", "kl_full", "margin", "lse_base", "lse_cand", "top1_base", "top2_base",
-        "top1_cand", "flip", "status", "topk_idx")]
+    """lcmp_row_out: device pointers, NULL to skip (target is an input)."""
+    _fields_ = [(n, ctypes.c_void_p) for n in ROW_OUT_FIELDS]
 
 
 # record sizes of the C structs (int64 x4, uint32 x2, double x6) etc.
@@ -127,7 +131,8 @@ def compare_workspace_bytes(n: int, v: int, k: int = 20, with_bitdiff: bool = Fa
     return int(_lib.lcmp_compare_workspace_bytes(n, v, k, LCMP_WITH_BITDIFF if with_bitdiff else 0))
 
 
-def alloc_compare_outputs(n: int, k: int, device, with_bitdiff: bool = False) -> dict:
+def alloc_compare_outputs(n: int, k: int, device, with_bitdiff: bool = False,
+                          with_target: bool = False) -> dict:
     f64 = dict(dtype=torch.float64, device=device)
     i32 = dict(dtype=torch.int32, device=device)
     u8 = dict(dtype=torch.uint8, device=device)
@@ -139,34 +144,42 @@ def alloc_compare_outputs(n: int, k: int, device, with_bitdiff: bool = False) ->
                topk_idx=torch.empty((n, k), **i32))
     if with_bitdiff:
         out["bitdiff"] = torch.empty((n, BITDIFF_ROW_BYTES), **u8)
+    if with_target:
+        out["logp_base"] = torch.empty(n, **f64)
+        out["logp_cand"] = torch.empty(n, **f64)
     return out
 
 
 def lcmp_compare_logits(base: torch.Tensor, cand: torch.Tensor, k: int = 20,
                         with_bitdiff: bool = False, v: int | None = None, out: dict | None = None,
                         workspace: torch.Tensor | None = None, stream=None,
-                        events: tuple | None = None) -> dict:
+                        events: tuple | None = None,
+                        target: torch.Tensor | None = None) -> dict:
     """Compare baseline and candidate logits row by row (device tensors [n, >=v]).
 
     Returns a dict of device tensors (kl_topk, kl_full, margin, lse_base, lse_cand,
     top1_base, top2_base, top1_cand, flip, status, topk_idx and, with
     with_bitdiff, a raw [n, 88] uint8 `bitdiff` record tensor; see unpack_bitdiff).
-    `events`, a pair of raw hipEvent_t handles, selects lcmp_compare_logits_timed."""
+    `target` (int32 device [n], the teacher-forced next tokens) adds logp_base
+    and logp_cand.  `events`, a pair of raw hipEvent_t handles, selects
+    lcmp_compare_logits_timed."""
     n = base.size(0)
     if cand.size(0) != n:
         raise ValueError("baseline and candidate need the same number of rows")
     v = base.size(1) if v is None else v
     flags = LCMP_WITH_BITDIFF if with_bitdiff else 0
+    if target is not None and (target.dtype != torch.int32 or target.numel() != n
+                               or not target.is_contiguous()):
+        raise ValueError("target must be a contiguous int32 tensor of one id per row")
     if out is None:
-        out = alloc_compare_outputs(n, k, base.device, with_bitdiff)
+        out = alloc_compare_outputs(n, k, base.device, with_bitdiff, target is not None)
     ws_bytes = int(_lib.lcmp_compare_workspace_bytes(n, v, k, flags))
     if ws_bytes == 0:
         raise LcmpError(-3, "lcmp_compare_workspace_bytes")
     if workspace is None or workspace.numel() < ws_bytes:
         workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=base.device)
-    ro = RowOut(*[_ptr(out.get(f)) for f in (
-        "kl_topk", "kl_full", "margin", "lse_base", "lse_cand", "top1_base", "top2_base",
-        "top1_cand", "flip", "status", "topk_idx")])
+    ptrs = dict(out, target=target)
+    ro = RowOut(*[_ptr(ptrs.get(f)) for f in ROW_OUT_FIELDS])
     args = (base.data_ptr(), _dtype_code(base), _ld(base), cand.data_ptr(), _dtype_code(cand),
             _ld(cand), n, v, k, flags, ctypes.byref(ro), _ptr(out.get("bitdiff")),
             workspace.data_ptr(), workspace.numel(), _stream(stream))

@@ -129,6 +129,10 @@ __global__ __launch_bounds__(kWave) void k_topk_kl(FinalArgs a) {
       if (a.top1_cand) a.top1_cand[row] = -1;
       if (a.flip) a.flip[row] = 0;
       if (a.status) a.status[row] = status;
+      if (a.target) {
+        if (a.logp_base) a.logp_base[row] = NAN;
+        if (a.logp_cand) a.logp_cand[row] = NAN;
+      }
     }
     if (a.topk_idx)
       for (int j = lane; j < a.k; j += kWave) a.topk_idx[row * a.k + j] = -1;
@@ -241,6 +245,22 @@ __global__ __launch_bounds__(kWave) void k_topk_kl(FinalArgs a) {
     if (a.top1_cand) a.top1_cand[row] = top1_cand;
     if (a.flip) a.flip[row] = (uint8_t)(top1_cand != s_i[0]);
     if (a.status) a.status[row] = 0;
+    if (a.target) {
+      // log-probability of the teacher-forced next token on each side
+      const int t = a.target[row];
+      double lpb = NAN, lpc = NAN;
+      if (t >= 0 && (int64_t)t < a.v) {
+        const int64_t ob = row * a.ldb + t, oc = row * a.ldc + t;
+        const float xb = a.tb == 1 ? __uint_as_float((uint32_t)((const uint16_t *)a.base)[ob] << 16)
+                                   : ((const float *)a.base)[ob];
+        const float xc = a.tc == 1 ? __uint_as_float((uint32_t)((const uint16_t *)a.cand)[oc] << 16)
+                                   : ((const float *)a.cand)[oc];
+        lpb = (double)xb - lse_b;
+        lpc = (double)xc - (lse_b + log1p(u));
+      }
+      if (a.logp_base) a.logp_base[row] = lpb;
+      if (a.logp_cand) a.logp_cand[row] = lpc;
+    }
   }
 }
 

@@ -32,6 +32,11 @@ struct FinalArgs {
   const void *cand;  // candidate logits, read at the top-k indices
   int32_t tc;
   int64_t ldc;
+  const void *base;  // baseline logits, read at the target index
+  int32_t tb;
+  int64_t ldb;
+  const int32_t *target;  // NULL: no target log-probabilities
+  double *logp_base, *logp_cand;
   int64_t n, v;
   int32_t nchunks, kint, k;
   double *kl_topk, *kl_full, *margin, *lse_base, *lse_cand;

@@ -141,6 +141,7 @@ static int compare_impl(const void *base, int tb, int64_t ld_base, const void *c
     return LCMP_ESHAPE;
   const bool with_bits = (flags & LCMP_WITH_BITDIFF) != 0;
   if (with_bits && !bd) return LCMP_EINVAL;
+  if ((out->logp_base || out->logp_cand) && !out->target) return LCMP_EINVAL;
   if (n == 0) return LCMP_OK;
   if (!base || !cand) return LCMP_EINVAL;
   const CompareLayout L = compare_layout(n, v, k, flags);
@@ -177,6 +178,13 @@ static int compare_impl(const void *base, int tb, int64_t ld_base, const void *c
   fa.cand = cand;
   fa.tc = tc;
   fa.ldc = ld_cand;
+  fa.base = base;
+  fa.tb = tb;
+  fa.ldb = ld_base;
+  const bool with_target = out->target && (out->logp_base || out->logp_cand);
+  fa.target = with_target ? out->target : nullptr;
+  fa.logp_base = with_target ? out->logp_base : nullptr;
+  fa.logp_cand = with_target ? out->logp_cand : nullptr;
   fa.n = n;
   fa.v = v;
   fa.nchunks = L.ch.nchunks;

@@ -86,6 +86,8 @@ def _L():
         vp, i64, ci = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
         lib.orc_compare.restype = ci
         lib.orc_compare.argtypes = [vp, ci, i64, vp, ci, i64, i64, i64, ci] + [vp] * 11 + [ci]
+        lib.orc_target_logprob.restype = ci
+        lib.orc_target_logprob.argtypes = [vp, ci, i64, vp, ci, i64, i64, i64, vp, vp, vp, ci]
         lib.orc_bitdiff.restype = ci
         lib.orc_bitdiff.argtypes = [vp, ci, i64, vp, ci, i64, i64, i64, vp, ci]
         lib.orc_bin_report.restype = ci
@@ -129,6 +131,27 @@ def compare(base: np.ndarray, cand: np.ndarray, k: int = 20, v: int | None = Non
                           nthreads)
     if rc != 0:
         raise ValueError("orc_compare rejected its arguments")
+    return out
+
+
+def target_logprob(base: np.ndarray, cand: np.ndarray, target, v: int | None = None,
+                   nthreads: int = 0) -> dict:
+    """ln p(target) and ln q(target) per row (NaN for flagged rows and targets
+    outside [0, v)); `target` is one int32 id per row."""
+    assert base.ndim == 2 and cand.ndim == 2 and base.shape[0] == cand.shape[0]
+    base = np.ascontiguousarray(base)
+    cand = np.ascontiguousarray(cand)
+    n = base.shape[0]
+    v = base.shape[1] if v is None else v
+    target = np.ascontiguousarray(target, dtype=np.int32)
+    assert target.shape == (n,)
+    out = dict(logp_base=np.empty(n), logp_cand=np.empty(n))
+    rc = _L().orc_target_logprob(base.ctypes.data, dtype_code(base), base.shape[1],
+                                 cand.ctypes.data, dtype_code(cand), cand.shape[1], n, v,
+                                 target.ctypes.data, out["logp_base"].ctypes.data,
+                                 out["logp_cand"].ctypes.data, nthreads)
+    if rc != 0:
+        raise ValueError("orc_target_logprob rejected its arguments")
     return out
 
 

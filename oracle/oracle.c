@@ -33,6 +33,8 @@
  *     finite; non-finite elements are counted per side.
  *   - Margin bins are half-open [e_{j-1}, e_j) with e_{-1} = 0; a flip at
  *     margin strictly above the big-margin threshold is a big-margin flip.
+ *   - The target log-probability of a flagged row, or of a target outside
+ *     [0, v), is NaN.
  */
 #include <math.h>
 #include <stdint.h>
@@ -110,21 +112,25 @@ static void flag_row(orc_row *o, uint8_t status, int32_t *topk_idx, int k) {
   for (int j = 0; j < k; j++) topk_idx[j] = -1;
 }
 
-static void compare_row(const double *x, const double *y, int64_t v, int k, keyed *order,
-                        orc_row *o, int32_t *topk_idx) {
-  /* the finite check of the ladder in [dcu] §1 / §7 */
+/* the finite check of the ladder in [dcu] §1 / §7: a NaN or +inf on either
+ * side flags the row NONFINITE, a side that is entirely -inf flags it EMPTY */
+static uint8_t row_status(const double *x, const double *y, int64_t v) {
   int bad = 0, x_any = 0, y_any = 0;
   for (int64_t i = 0; i < v; i++) {
     if (isnan(x[i]) || isnan(y[i]) || x[i] == INFINITY || y[i] == INFINITY) bad = 1;
     if (x[i] > -INFINITY) x_any = 1;
     if (y[i] > -INFINITY) y_any = 1;
   }
-  if (bad) {
-    flag_row(o, ORC_ROW_NONFINITE, topk_idx, k);
-    return;
-  }
-  if (!x_any || !y_any) {
-    flag_row(o, ORC_ROW_EMPTY, topk_idx, k);
+  if (bad) return ORC_ROW_NONFINITE;
+  if (!x_any || !y_any) return ORC_ROW_EMPTY;
+  return 0;
+}
+
+static void compare_row(const double *x, const double *y, int64_t v, int k, keyed *order,
+                        orc_row *o, int32_t *topk_idx) {
+  const uint8_t st = row_status(x, y, v);
+  if (st) {
+    flag_row(o, st, topk_idx, k);
     return;
   }
   const int64_t keff = (int64_t)k < v ? (int64_t)k : v;
@@ -265,6 +271,60 @@ int orc_compare(const void *base, int tb, int64_t ld_base, const void *cand, int
     free(y);
     free(order);
     free(idx);
+  }
+  return failed ? -1 : 0;
+}
+
+/* ------------------------------------------------------ target log-probability */
+
+/*
+ * ln p(target) and ln q(target) of each row: the teacher-forced next token's
+ * log-probability under the baseline and the candidate softmax, the only
+ * number perplexity keeps of a distribution ([logits] perplexity（困惑度）看不出
+ * 这一级的差别).  NaN for a flagged row or a target outside [0, v).
+ */
+int orc_target_logprob(const void *base, int tb, int64_t ld_base, const void *cand, int tc,
+                       int64_t ld_cand, int64_t n, int64_t v, const int32_t *target,
+                       double *logp_base, double *logp_cand, int nthreads) {
+  if (!base || !cand || !target || !logp_base || !logp_cand || n < 0 || v < 2 ||
+      ld_base < v || ld_cand < v)
+    return -1;
+  if ((tb != ORC_F32 && tb != ORC_BF16) || (tc != ORC_F32 && tc != ORC_BF16)) return -1;
+  const size_t eb = tb == ORC_BF16 ? 2 : 4, ec = tc == ORC_BF16 ? 2 : 4;
+  int failed = 0;
+#ifdef _OPENMP
+  if (nthreads > 0) omp_set_num_threads(nthreads);
+#else
+  (void)nthreads;
+#endif
+#pragma omp parallel
+  {
+    double *x = (double *)malloc((size_t)v * sizeof(double));
+    double *y = (double *)malloc((size_t)v * sizeof(double));
+    if (!x || !y) {
+#pragma omp atomic write
+      failed = 1;
+    }
+#pragma omp for schedule(dynamic, 1)
+    for (int64_t r = 0; r < n; r++) {
+      if (!x || !y) continue;
+      const void *br = (const char *)base + (size_t)r * (size_t)ld_base * eb;
+      const void *cr = (const char *)cand + (size_t)r * (size_t)ld_cand * ec;
+      for (int64_t i = 0; i < v; i++) {
+        x[i] = value(br, tb, i);
+        y[i] = value(cr, tc, i);
+      }
+      const int32_t t = target[r];
+      if (row_status(x, y, v) != 0 || t < 0 || (int64_t)t >= v) {
+        logp_base[r] = NAN;
+        logp_cand[r] = NAN;
+        continue;
+      }
+      logp_base[r] = x[t] - log_normaliser(x, v);
+      logp_cand[r] = y[t] - log_normaliser(y, v);
+    }
+    free(x);
+    free(y);
   }
   return failed ? -1 : 0;
 }

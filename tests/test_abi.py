@@ -35,7 +35,7 @@ def test_every_declared_symbol_is_exported(L):
 
 def test_version_and_strerror(L):
     lib = L.lib()
-    assert lib.lcmp_abi_version() == 1
+    assert lib.lcmp_abi_version() == 2
     for st in (0, -1, -2, -3, -4, -5, -6):
         assert len(lib.lcmp_strerror(st)) > 0
     assert lib.lcmp_strerror(-99) == b"unknown status"
@@ -90,6 +90,9 @@ def test_compare_argument_errors(L):
     assert _compare(L, ws_bytes=16) == -4
     assert _compare(L, ws=FAKE + 4) == -1                # misaligned workspace
     assert _compare(L, n=0) == 0                         # empty batch: nothing to do
+    ro = L.RowOut()
+    ro.logp_cand = FAKE
+    assert _compare(L, out=ro) == -1                     # target log-probabilities need targets
 
 
 def test_bitdiff_argument_errors(L):

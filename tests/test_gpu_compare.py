@@ -169,3 +169,47 @@ def test_repeated_runs_bit_identical():
             assert g1[key].tobytes() == g2[key].tobytes()
         else:
             assert np.array_equal(g1[key].view(np.uint8), g2[key].view(np.uint8)), key
+
+
+def _logp_close(g, o, what):
+    g = np.asarray(g, np.float64)
+    o = np.asarray(o, np.float64)
+    assert np.array_equal(np.isnan(g), np.isnan(o)), f"{what}: NaN pattern"
+    assert np.array_equal(np.isinf(g), np.isinf(o)), f"{what}: infinities"
+    fin = np.isfinite(o)
+    tol = 2e-6 * np.maximum(1.0, np.abs(o[fin]))
+    assert np.all(np.abs(g[fin] - o[fin]) <= tol), f"{what}: worst {np.max(np.abs(g[fin] - o[fin]) / tol):.3g}"
+
+
+@pytest.mark.parametrize("tb,tc", [("f32", "f32"), ("f32", "bf16"), ("bf16", "bf16")])
+def test_target_logprob_parity(tb, tc):
+    import torch
+    import logit_distribution_diffing_amd as L
+    from helpers import to_device
+    _case(f"target log-probabilities {tb}/{tc}")
+    rng = np.random.default_rng(11)
+    n, v = 24, 151936
+    x = synth.segment(synth.SEED_BASE + 1, 0, n, v)[0]
+    y = (x + 0.02 * rng.standard_normal((n, v))).astype(np.float32)
+
+    def conv(t, arr):
+        if t == "f32":
+            return arr
+        return torch.from_numpy(arr).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+
+    a, b = conv(tb, x), conv(tc, y)
+    t = rng.integers(0, v, n).astype(np.int32)
+    t[:5] = [0, v - 1, -1, v, 7]
+    if tb == "f32":
+        a[4, 7] = -np.inf          # target with probability 0 on the baseline
+        a[5, 100] = np.nan         # flagged row
+    tt = torch.from_numpy(t).cuda()
+    out = L.lcmp_compare_logits(to_device(a), to_device(b), k=20, target=tt)
+    plain = L.lcmp_compare_logits(to_device(a), to_device(b), k=20)
+    torch.cuda.synchronize()
+    o = oracle.target_logprob(a, b, t)
+    _logp_close(out["logp_base"].cpu().numpy(), o["logp_base"], "logp_base")
+    _logp_close(out["logp_cand"].cpu().numpy(), o["logp_cand"], "logp_cand")
+    for key in plain:   # the targets change nothing else
+        assert np.array_equal(plain[key].cpu().numpy().view(np.uint8),
+                              out[key].cpu().numpy().view(np.uint8)), key

@@ -64,6 +64,10 @@ MUTANTS = [
     ("big margin taken as >= 1",
      "    if (flip[r] && m > big_margin) summary[g].big_margin_flips++;",
      "    if (flip[r] && m >= big_margin) summary[g].big_margin_flips++;"),
+    ("candidate log-probability normalised by the baseline",
+     "      logp_cand[r] = y[t] - log_normaliser(y, v);", "      logp_cand[r] = y[t] - log_normaliser(x, v);"),
+    ("target log-probability without the normaliser",
+     "      logp_base[r] = x[t] - log_normaliser(x, v);", "      logp_base[r] = x[t];"),
     ("flagged rows binned instead of excluded",
      "    if (status && status[r] != 0) {\n      summary[g].excluded++;\n      continue;\n    }",
      "    if (status && status[r] != 0) {\n      summary[g].excluded++;\n    }"),

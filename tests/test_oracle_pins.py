@@ -387,3 +387,50 @@ def test_bin_report_groups_and_unbinned():
     assert summ[1]["unbinned"] == 1 and summ[1]["big_margin_flips"] == 1
     assert summ[0]["unbinned"] == 1 and summ[0]["big_margin_flips"] == 1
     assert np.isneginf(bins[0]["max_kl_topk"][1])
+
+
+# ------------------------------------------------------------------ target log-probability
+def test_target_logprob_cat_dog_is_log_of_page_probabilities():
+    """With logits ln p, the log-probability of each token is ln p_t (the page's
+    cat/dog numbers), on both sides."""
+    g = _kv("cat_dog.txt")
+    p = np.array(g["p"], float)
+    q = np.array(g["q"], float)
+    a, b = np.repeat(_logits(p), 4, 0), np.repeat(_logits(q), 4, 0)
+    r = oracle.target_logprob(a, b, np.arange(4, dtype=np.int32))
+    assert np.allclose(r["logp_base"], np.log(p), rtol=0, atol=1e-6)
+    assert np.allclose(r["logp_cand"], np.log(q), rtol=0, atol=1e-6)
+
+
+@pytest.mark.parametrize("seed", [0, 1])
+def test_target_logprob_against_torch_log_softmax(seed):
+    import torch
+    rng = np.random.default_rng(seed)
+    n, v = 6, 777
+    a = (2.0 * rng.standard_normal((n, v))).astype(np.float32)
+    b = (a + 0.05 * rng.standard_normal((n, v))).astype(np.float32)
+    t = rng.integers(0, v, n).astype(np.int32)
+    r = oracle.target_logprob(a, b, t)
+    la = torch.log_softmax(torch.from_numpy(a).double(), dim=1).numpy()
+    lb = torch.log_softmax(torch.from_numpy(b).double(), dim=1).numpy()
+    assert np.allclose(r["logp_base"], la[np.arange(n), t], rtol=0, atol=1e-12)
+    assert np.allclose(r["logp_cand"], lb[np.arange(n), t], rtol=0, atol=1e-12)
+
+
+def test_target_logprob_shift_invariant_and_edge_cases():
+    rng = np.random.default_rng(3)
+    n, v = 8, 64
+    a = rng.standard_normal((n, v)).astype(np.float32)
+    b = a.copy()
+    t = np.array([0, 63, 5, -1, 64, 7, 9, 11], np.int32)
+    a[5, 7] = -np.inf      # the target itself has probability 0
+    b[6, 3] = np.nan       # flagged row
+    r = oracle.target_logprob(a, b, t)
+    shifted = oracle.target_logprob(a + 4.0, b - 2.0, t)
+    ok = [0, 1, 2, 7]
+    assert np.allclose(r["logp_base"][ok], shifted["logp_base"][ok], rtol=0, atol=1e-6)
+    assert np.array_equal(r["logp_base"][ok], r["logp_cand"][ok])  # identical rows
+    assert np.all(np.isnan(r["logp_base"][[3, 4, 6]]))             # out of range, flagged
+    assert r["logp_base"][5] == -np.inf
+    # perplexity of a row set is exp(-mean ln q(target)); identical sides agree
+    assert np.exp(-r["logp_base"][ok].mean()) == np.exp(-r["logp_cand"][ok].mean())
