@@ -88,6 +88,8 @@ def _L():
         lib.orc_compare.argtypes = [vp, ci, i64, vp, ci, i64, i64, i64, ci] + [vp] * 11 + [ci]
         lib.orc_target_logprob.restype = ci
         lib.orc_target_logprob.argtypes = [vp, ci, i64, vp, ci, i64, i64, i64, vp, vp, vp, ci]
+        lib.orc_perturb.restype = ci
+        lib.orc_perturb.argtypes = [vp, ci, i64, vp, ci, i64, i64, i64, ci, ci]
         lib.orc_bitdiff.restype = ci
         lib.orc_bitdiff.argtypes = [vp, ci, i64, vp, ci, i64, i64, i64, vp, ci]
         lib.orc_bin_report.restype = ci
@@ -153,6 +155,25 @@ def target_logprob(base: np.ndarray, cand: np.ndarray, target, v: int | None = N
     if rc != 0:
         raise ValueError("orc_target_logprob rejected its arguments")
     return out
+
+
+PERTURB_MANTISSA, PERTURB_E4M3, PERTURB_E4M3_SCALED = 0, 1, 2
+
+
+def perturb(src: np.ndarray, mode: int, param: int = 0, out_bf16: bool = False) -> np.ndarray:
+    """Precision perturbation of a [rows, cols] array (float32 or uint16 bf16
+    patterns): keep `param` fraction bits, or round to e4m3 (optionally after
+    scaling by 448).  Returns float32, or uint16 bf16 patterns with out_bf16."""
+    src = np.ascontiguousarray(src)
+    if src.ndim == 1:
+        src = src[None, :]
+    rows, cols = src.shape
+    dst = np.empty((rows, cols), np.uint16 if out_bf16 else np.float32)
+    rc = _L().orc_perturb(src.ctypes.data, dtype_code(src), cols, dst.ctypes.data,
+                          BF16 if out_bf16 else F32, cols, rows, cols, mode, param)
+    if rc != 0:
+        raise ValueError("orc_perturb rejected its arguments")
+    return dst
 
 
 def bitdiff(a: np.ndarray, b: np.ndarray, cols: int | None = None, nthreads: int = 0) -> np.ndarray:

@@ -329,6 +329,88 @@ int orc_target_logprob(const void *base, int tb, int64_t ld_base, const void *ca
   return failed ? -1 : 0;
 }
 
+/* ------------------------------------------------------ precision perturbations */
+
+/*
+ * The precision-knee experiments of [logits] (实验 section): keep only m
+ * fraction bits of an fp32 value with the exponent range unchanged, or round
+ * to fp8 e4m3 directly or after scaling by 448 (注意力权重 paragraph; the
+ * round_p variants).  Round to nearest, ties to even, written from the value:
+ * the quantum is 2^(E - m) with E = max(floor(log2 |x|), emin), the multiple
+ * of the quantum nearest to x is taken in double (exact: the quantum is a
+ * power of two), and the result converted back.  NaN stays NaN.
+ */
+#define ORC_PERTURB_MANTISSA 0
+#define ORC_PERTURB_E4M3 1
+#define ORC_PERTURB_E4M3_SCALED 2
+
+static double round_to_quantum(double x, int m, int emin) {
+  if (x == 0.0 || !isfinite(x)) return x;
+  int e;
+  frexp(x, &e); /* x = f * 2^e, 0.5 <= |f| < 1, so floor(log2 |x|) = e - 1 */
+  int E = e - 1;
+  if (E < emin) E = emin;
+  const double q = ldexp(1.0, E - m);
+  return rint(x / q) * q; /* rint: ties to even in the default rounding mode */
+}
+
+/* fp32 with m fraction bits: emin -126 (subnormals keep the fp32 quantum grid) */
+static float keep_mantissa(float x, int m) {
+  if (isnan(x)) return x;
+  return (float)round_to_quantum((double)x, m, -126); /* beyond FLT_MAX: inf */
+}
+
+/* OCP e4m3 (fn): 3 fraction bits, emin -6 (smallest subnormal 2^-9), largest
+ * finite 448, no infinity; out-of-range values saturate to +-448 */
+static float to_e4m3(float x) {
+  if (isnan(x)) return x;
+  double r = round_to_quantum((double)x, 3, -6);
+  if (r > 448.0) r = 448.0;
+  if (r < -448.0) r = -448.0;
+  return (float)r;
+}
+
+static float perturb_value(float x, int mode, int param) {
+  if (mode == ORC_PERTURB_MANTISSA) return keep_mantissa(x, param);
+  if (mode == ORC_PERTURB_E4M3) return to_e4m3(x);
+  /* scaled: the product and the quotient are fp32 operations, as in the listing
+   * of the page's round_p ("fp8, scaled by 448") */
+  const float t = x * 448.0f;
+  return to_e4m3(t) / 448.0f;
+}
+
+/*
+ * dst[r, c] = perturb(src[r, c]) for r < rows, c < cols.  src is fp32 or bf16
+ * (widened exactly); dst is fp32, or bf16 when every result is representable
+ * there (mantissa modes with m <= 7, and plain e4m3).  Returns 0 or -1.
+ */
+int orc_perturb(const void *src, int ts, int64_t ld_src, void *dst, int td, int64_t ld_dst,
+                int64_t rows, int64_t cols, int mode, int param) {
+  if (!src || !dst || rows < 0 || cols < 0 || ld_src < cols || ld_dst < cols) return -1;
+  if ((ts != ORC_F32 && ts != ORC_BF16) || (td != ORC_F32 && td != ORC_BF16)) return -1;
+  if (mode < ORC_PERTURB_MANTISSA || mode > ORC_PERTURB_E4M3_SCALED) return -1;
+  if (mode == ORC_PERTURB_MANTISSA && (param < 0 || param > 23)) return -1;
+  if (td == ORC_BF16 && !((mode == ORC_PERTURB_MANTISSA && param <= 7) || mode == ORC_PERTURB_E4M3))
+    return -1;
+  const size_t es = ts == ORC_BF16 ? 2 : 4, ed = td == ORC_BF16 ? 2 : 4;
+  for (int64_t r = 0; r < rows; r++) {
+    const void *sr = (const char *)src + (size_t)r * (size_t)ld_src * es;
+    char *dr = (char *)dst + (size_t)r * (size_t)ld_dst * ed;
+    for (int64_t c = 0; c < cols; c++) {
+      const float y = perturb_value((float)value(sr, ts, c), mode, param);
+      if (td == ORC_F32) {
+        memcpy(dr + 4 * c, &y, 4);
+      } else {
+        uint32_t u;
+        memcpy(&u, &y, 4);
+        const uint16_t h = (uint16_t)(u >> 16); /* exact: y has at most 7 fraction bits */
+        memcpy(dr + 2 * c, &h, 2);
+      }
+    }
+  }
+  return 0;
+}
+
 /* ------------------------------------------------------------ bitwise / ULP */
 
 typedef struct {

@@ -68,6 +68,12 @@ MUTANTS = [
      "      logp_cand[r] = y[t] - log_normaliser(y, v);", "      logp_cand[r] = y[t] - log_normaliser(x, v);"),
     ("target log-probability without the normaliser",
      "      logp_base[r] = x[t] - log_normaliser(x, v);", "      logp_base[r] = x[t];"),
+    ("perturbation ties rounded away from zero",
+     "  return rint(x / q) * q;", "  return round(x / q) * q;"),
+    ("perturbation without the subnormal floor of the exponent",
+     "  if (E < emin) E = emin;", "  (void)emin;"),
+    ("e4m3 without saturation",
+     "  if (r > 448.0) r = 448.0;", "  if (r > 480.0) r = 480.0;"),
     ("flagged rows binned instead of excluded",
      "    if (status && status[r] != 0) {\n      summary[g].excluded++;\n      continue;\n    }",
      "    if (status && status[r] != 0) {\n      summary[g].excluded++;\n    }"),

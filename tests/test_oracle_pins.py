@@ -434,3 +434,77 @@ def test_target_logprob_shift_invariant_and_edge_cases():
     assert r["logp_base"][5] == -np.inf
     # perplexity of a row set is exp(-mean ln q(target)); identical sides agree
     assert np.exp(-r["logp_base"][ok].mean()) == np.exp(-r["logp_cand"][ok].mean())
+
+
+# ------------------------------------------------------------------ precision perturbations
+def _bf16_patterns_sample():
+    hi = np.arange(0, 1 << 16, 7, dtype=np.uint32)
+    lows = np.array([0, 1, 0x7FFF, 0x8000, 0x8001, 0xFFFF], np.uint32)
+    u = ((hi[:, None] << 16) | lows[None, :]).ravel()
+    f = u.view(np.float32)
+    return f[np.isfinite(f)]
+
+
+def test_keep_7_mantissa_bits_is_bf16_rounding():
+    """fp32 and bf16 share the exponent range, so keeping 7 fraction bits is the
+    bf16 cast (torch, round to nearest even)."""
+    import torch
+    x = _bf16_patterns_sample()
+    ours = oracle.perturb(x, oracle.PERTURB_MANTISSA, 7)[0]
+    ref = torch.from_numpy(x).to(torch.bfloat16).float().numpy()
+    assert np.array_equal(ours.view(np.uint32), ref.view(np.uint32))
+    as_bf16 = oracle.perturb(x, oracle.PERTURB_MANTISSA, 7, out_bf16=True)[0]
+    assert np.array_equal(synth.bf16_to_f32(as_bf16).view(np.uint32), ref.view(np.uint32))
+
+
+def test_e4m3_against_torch_float8_in_range():
+    import torch
+    rng = np.random.default_rng(5)
+    x = np.concatenate([_bf16_patterns_sample(),
+                        (rng.standard_normal(200000) * 10 ** rng.uniform(-5, 2.6, 200000))])
+    x = x.astype(np.float32)
+    x = x[np.abs(x) <= 448.0]
+    ours = oracle.perturb(x, oracle.PERTURB_E4M3)[0]
+    ref = torch.from_numpy(x).to(torch.float8_e4m3fn).float().numpy()
+    assert np.array_equal(ours, ref)
+
+
+def test_e4m3_constants_match_page():
+    g = _kv("e4m3.txt")
+    tiny = np.float32(2.0 ** -9)
+    x = np.array([tiny, 2.0 ** -10, np.nextafter(np.float32(2.0 ** -10), np.float32(1)),
+                  np.float32(2.0 ** -11), 448.0, 460.0, 470.0, 1e6, -1e6], np.float32)
+    r = oracle.perturb(x, oracle.PERTURB_E4M3)[0]
+    assert r[0] == tiny and abs(float(tiny) - float(g["min_subnormal_approx"][0])) \
+        <= float(g["min_subnormal_tol"][0])
+    assert r[1] == 0.0 and r[3] == 0.0          # half of the smallest and below: 0
+    assert r[2] == tiny                         # just above half: the smallest value
+    assert r[4] == 448.0 and r[5] == 448.0      # 460 < 464: rounds to 448
+    assert r[6] == 448.0 and r[7] == 448.0 and r[8] == -448.0   # saturate
+    assert float(g["max_finite"][0]) == 448.0
+    # scaling by 448 first: the smallest weight that survives is near 2^-10 / 448
+    s = oracle.perturb(np.array([2.3e-6, 2.1e-6], np.float32), oracle.PERTURB_E4M3_SCALED)[0]
+    assert s[0] > 0.0 and s[1] == 0.0
+    assert 2.0 ** -10 / 448 < float(g["scaled_threshold_max"][0])
+
+
+@pytest.mark.parametrize("m", [0, 4, 7, 10, 13, 16, 22, 23])
+def test_keep_mantissa_closed_forms(m):
+    rng = np.random.default_rng(m)
+    x = (rng.standard_normal(100000) * 10 ** rng.uniform(-44, 38, 100000)).astype(np.float32)
+    x = np.concatenate([x, np.array([0.0, -0.0, np.inf, -np.inf, 1e-45, 3.4e38], np.float32)])
+    x = x[np.isfinite(x) | np.isinf(x)]
+    r = oracle.perturb(x, oracle.PERTURB_MANTISSA, m)[0]
+    fin = np.isfinite(x) & np.isfinite(r)
+    if m == 23:
+        assert np.array_equal(r.view(np.uint32), x.view(np.uint32))
+    # error at most half a quantum 2^(E - m), E = max(floor(log2 |x|), -126)
+    xd = x[fin].astype(np.float64)
+    E = np.maximum(np.floor(np.log2(np.abs(np.where(xd == 0, 1.0, xd)))), -126)
+    assert np.all(np.abs(r[fin] - xd) <= np.ldexp(0.5, (E - m).astype(int)) * (1 + 1e-12))
+    # idempotent, odd, monotone
+    assert np.array_equal(oracle.perturb(r, oracle.PERTURB_MANTISSA, m)[0].view(np.uint32),
+                          r.view(np.uint32))
+    assert np.array_equal(oracle.perturb(-x, oracle.PERTURB_MANTISSA, m)[0], -r)
+    order = np.argsort(x, kind="stable")
+    assert np.all(np.diff(r[order][np.isfinite(r[order])]) >= 0)
