@@ -193,6 +193,32 @@ int lcmp_bitdiff(const void *a, int ta, int64_t lda, const void *b, int tb, int6
                  int64_t rows, int64_t cols, lcmp_bitdiff_row *out, void *workspace,
                  size_t ws_bytes, void *stream);
 
+/* ---------------------------------------------------------------- perturbations */
+
+/* modes of lcmp_perturb */
+#define LCMP_PERTURB_MANTISSA 0   /* keep `param` (0..23) fraction bits, fp32 exponent range */
+#define LCMP_PERTURB_E4M3 1       /* fp8 e4m3 (fn): 3 fraction bits, largest 448, saturating */
+#define LCMP_PERTURB_E4M3_SCALED 2 /* e4m3(x * 448) / 448, product and quotient in fp32 */
+
+/*
+ * Precision perturbations for precision-knee experiments ([logits] 实验 section:
+ * cut a tensor's precision a step at a time -- keep only m fraction bits with
+ * the exponent range unchanged, or round to fp8 e4m3 directly or after scaling
+ * by 448 -- and watch where the KL starts to rise).  Elementwise:
+ *   dst[r, c] = perturb(src[r, c]),  r < rows, c < cols.
+ * Rounding is to nearest, ties to even; NaN stays NaN; a value rounded past
+ * the largest fp32 becomes inf (mantissa mode) or 448 (e4m3 modes).  bf16
+ * rounding is LCMP_PERTURB_MANTISSA with param 7.
+ *   src    device [rows, ld_src] of type ts (fp32 or bf16, widened exactly).
+ *   dst    device [rows, ld_dst] of type td; bf16 only when every result is a
+ *          bf16 value (mantissa mode with param <= 7, or LCMP_PERTURB_E4M3),
+ *          else LCMP_EDTYPE.  dst may be src when ts == td and ld_src == ld_dst.
+ * Errors: LCMP_EINVAL for an unknown mode, a param outside 0..23 or a NULL
+ * buffer; LCMP_ESHAPE for ld < cols or sizes too large.
+ */
+int lcmp_perturb(const void *src, int ts, int64_t ld_src, void *dst, int td, int64_t ld_dst,
+                 int64_t rows, int64_t cols, int mode, int param, void *stream);
+
 /* ---------------------------------------------------------------- margin bins */
 
 #define LCMP_MAX_BIN_ROWS (1LL << 36) /* largest n of lcmp_bin_report */

@@ -10,6 +10,7 @@ Entry points (same names as the C ABI):
   lcmp_compare_logits(base, cand, k=20, with_bitdiff=False)  -> dict of tensors
   lcmp_bitdiff(a, b)                                         -> structured tensor
   lcmp_bin_report(margin, flip, kl_topk, kl_full, edges, ...) -> (bins, summary)
+  lcmp_perturb(src, mode, param)                             -> perturbed tensor
 """
 from __future__ import annotations
 
@@ -25,12 +26,14 @@ LCMP_F32, LCMP_BF16 = 0, 1
 LCMP_WITH_BITDIFF = 1
 LCMP_ROW_NONFINITE, LCMP_ROW_EMPTY = 1, 2
 LCMP_MAX_K = 64
+ABI_VERSION = 2
+LCMP_PERTURB_MANTISSA, LCMP_PERTURB_E4M3, LCMP_PERTURB_E4M3_SCALED = 0, 1, 2
 STATUS_NAMES = {0: "LCMP_OK", -1: "LCMP_EINVAL", -2: "LCMP_EDTYPE", -3: "LCMP_ESHAPE",
                 -4: "LCMP_EWORKSPACE", -5: "LCMP_EHIP", -6: "LCMP_EEDGES"}
 
 EXPORTED = ("lcmp_abi_version", "lcmp_strerror", "lcmp_compare_workspace_bytes",
             "lcmp_compare_logits", "lcmp_compare_logits_timed", "lcmp_bitdiff_workspace_bytes",
-            "lcmp_bitdiff", "lcmp_bin_workspace_bytes", "lcmp_bin_report")
+            "lcmp_bitdiff", "lcmp_bin_workspace_bytes", "lcmp_bin_report", "lcmp_perturb")
 
 
 class LcmpError(RuntimeError):
@@ -83,10 +86,15 @@ def _load():
     lib.lcmp_bitdiff.argtypes = [vp, ci, i64, vp, ci, i64, i64, i64, vp, vp, sz, vp]
     lib.lcmp_bin_workspace_bytes.restype = sz
     lib.lcmp_bin_workspace_bytes.argtypes = [i64, ci, ci]
+    lib.lcmp_perturb.restype = ci
+    lib.lcmp_perturb.argtypes = [vp, ci, i64, vp, ci, i64, i64, i64, ci, ci, vp]
     lib.lcmp_bin_report.restype = ci
     lib.lcmp_bin_report.argtypes = [vp, vp, vp, vp, vp, vp, ci, i64,
                                     ctypes.POINTER(ctypes.c_double), ci, ctypes.c_double,
                                     vp, vp, vp, sz, vp]
+    if lib.lcmp_abi_version() != ABI_VERSION:
+        raise ImportError(f"{LIB_PATH} has ABI {lib.lcmp_abi_version()}, this binding expects "
+                          f"{ABI_VERSION}; rebuild it")
     _lib = lib
     return lib
 
@@ -237,6 +245,26 @@ def lcmp_bin_report(margin, flip, kl_topk, kl_full, edges, status=None, group=No
                               workspace.numel(), _stream(stream))
     _check(rc, "lcmp_bin_report")
     return bins, summ
+
+
+def lcmp_perturb(src: torch.Tensor, mode: int, param: int = 0, out: torch.Tensor | None = None,
+                 out_dtype: torch.dtype | None = None, stream=None) -> torch.Tensor:
+    """Precision perturbation of a [rows, cols] fp32 / bf16 device tensor (keep
+    `param` fraction bits, or e4m3, or e4m3 after x448); returns `out`, by
+    default a new fp32 tensor (bf16 with out_dtype=torch.bfloat16)."""
+    if src.dim() == 1:
+        src = src.view(1, -1)
+    rows, cols = src.shape
+    if out is None:
+        out = torch.empty((rows, cols), dtype=out_dtype or torch.float32, device=src.device)
+    elif out.dim() == 1:
+        out = out.view(1, -1)
+    if out.shape[0] != rows or out.shape[1] < cols:
+        raise ValueError("out must hold [rows, cols]")
+    rc = _lib.lcmp_perturb(src.data_ptr(), _dtype_code(src), _ld(src), out.data_ptr(),
+                           _dtype_code(out), _ld(out), rows, cols, mode, param, _stream(stream))
+    _check(rc, "lcmp_perturb")
+    return out
 
 
 # ----------------------------------------------------------------------------- unpacking

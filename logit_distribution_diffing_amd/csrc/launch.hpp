@@ -94,6 +94,17 @@ struct BinArgs {
   GroupAcc *groups;       // [n_groups]
 };
 
+// precision perturbation (k_perturb.hip)
+struct PerturbArgs {
+  const void *src;
+  void *dst;
+  int64_t ld_src, ld_dst, rows, cols, tiles;
+  int32_t ts, td, mode, param;
+  bool vec;  // rows of both sides aligned for 4-element vector accesses
+};
+int64_t perturb_tiles(int64_t cols);
+hipError_t launch_perturb(const PerturbArgs &a, hipStream_t stream);
+
 hipError_t launch_row_stats(const StreamArgs &a, int ta, int tb, bool cmp, bool bits, bool vec,
                             hipStream_t stream);
 hipError_t launch_topk_kl(const FinalArgs &a, hipStream_t stream);

@@ -280,6 +280,40 @@ size_t lcmp_bin_workspace_bytes(int64_t n, int n_groups, int n_edges) {
          align_up((size_t)nblk * (size_t)n_groups * sizeof(GroupAcc)) + kAlign;
 }
 
+int lcmp_perturb(const void *src, int ts, int64_t ld_src, void *dst, int td, int64_t ld_dst,
+                 int64_t rows, int64_t cols, int mode, int param, void *stream) {
+  if (!dtype_ok(ts) || !dtype_ok(td)) return LCMP_EDTYPE;
+  if (rows < 0 || cols < 0) return LCMP_EINVAL;
+  if (mode != LCMP_PERTURB_MANTISSA && mode != LCMP_PERTURB_E4M3 &&
+      mode != LCMP_PERTURB_E4M3_SCALED)
+    return LCMP_EINVAL;
+  if (mode == LCMP_PERTURB_MANTISSA && (param < 0 || param > 23)) return LCMP_EINVAL;
+  if (td == LCMP_BF16 &&
+      !((mode == LCMP_PERTURB_MANTISSA && param <= 7) || mode == LCMP_PERTURB_E4M3))
+    return LCMP_EDTYPE;  // the results would not all be bf16 values
+  if (ld_src < cols || ld_dst < cols || cols > kMaxCols) return LCMP_ESHAPE;
+  if (rows == 0 || cols == 0) return LCMP_OK;
+  if (!src || !dst) return LCMP_EINVAL;
+  PerturbArgs a;
+  a.src = src;
+  a.dst = dst;
+  a.ld_src = ld_src;
+  a.ld_dst = ld_dst;
+  a.rows = rows;
+  a.cols = cols;
+  a.tiles = perturb_tiles(cols);
+  if (rows > 0x7fffffffLL / a.tiles) return LCMP_ESHAPE;  // one block per tile
+  a.ts = ts;
+  a.td = td;
+  a.mode = mode;
+  a.param = mode == LCMP_PERTURB_MANTISSA ? param : 23;
+  const size_t as = ts == LCMP_BF16 ? 8 : 16, ad = td == LCMP_BF16 ? 8 : 16;
+  a.vec = (uintptr_t)src % as == 0 && ((size_t)ld_src * esize(ts)) % as == 0 &&
+          (uintptr_t)dst % ad == 0 && ((size_t)ld_dst * esize(td)) % ad == 0;
+  if (launch_perturb(a, (hipStream_t)stream) != hipSuccess) return LCMP_EHIP;
+  return LCMP_OK;
+}
+
 int lcmp_bin_report(const double *margin, const uint8_t *flip, const double *kl_topk,
                     const double *kl_full, const uint8_t *status, const int32_t *group,
                     int n_groups, int64_t n, const double *edges, int n_edges, double big_margin,

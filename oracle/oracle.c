@@ -403,7 +403,8 @@ int orc_perturb(const void *src, int ts, int64_t ld_src, void *dst, int td, int6
       } else {
         uint32_t u;
         memcpy(&u, &y, 4);
-        const uint16_t h = (uint16_t)(u >> 16); /* exact: y has at most 7 fraction bits */
+        /* exact: y has at most 7 fraction bits; a NaN keeps its quiet bit */
+        const uint16_t h = (uint16_t)((u >> 16) | (isnan(y) ? 0x0040u : 0u));
         memcpy(dr + 2 * c, &h, 2);
       }
     }

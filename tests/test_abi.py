@@ -148,3 +148,25 @@ def test_binding_rejects_unsupported_dtype(L):
     with pytest.raises(TypeError):
         L.lcmp_compare_logits(torch.zeros(2, 4, dtype=torch.float64),
                               torch.zeros(2, 4, dtype=torch.float64))
+
+
+def test_perturb_argument_errors(L):
+    lib = L.lib()
+
+    def call(**kw):
+        a = dict(src=FAKE, ts=0, lds=10, dst=FAKE, td=0, ldd=10, rows=2, cols=10, mode=0, param=7)
+        a.update(kw)
+        return lib.lcmp_perturb(a["src"], a["ts"], a["lds"], a["dst"], a["td"], a["ldd"],
+                                a["rows"], a["cols"], a["mode"], a["param"], None)
+
+    assert call(ts=2) == -2
+    assert call(mode=3) == -1
+    assert call(param=24) == -1
+    assert call(param=-1) == -1
+    assert call(td=1, param=8) == -2            # 8 fraction bits do not fit bf16
+    assert call(td=1, mode=2) == -2             # scaled e4m3 results are not bf16 values
+    assert call(lds=9) == -3
+    assert call(src=None) == -1
+    assert call(rows=-1) == -1
+    assert call(rows=0) == 0
+
