@@ -88,6 +88,11 @@ def _L():
         lib.orc_compare.argtypes = [vp, ci, i64, vp, ci, i64, i64, i64, ci] + [vp] * 11 + [ci]
         lib.orc_target_logprob.restype = ci
         lib.orc_target_logprob.argtypes = [vp, ci, i64, vp, ci, i64, i64, i64, vp, vp, vp, ci]
+        lib.orc_record.restype = ci
+        lib.orc_record.argtypes = [vp, ci, i64, i64, i64, ci, vp, vp, vp, vp, vp, vp, ci]
+        lib.orc_compare_record.restype = ci
+        lib.orc_compare_record.argtypes = [vp, vp, vp, vp, vp, ci, vp, ci, i64, i64, i64, ci,
+                                           vp] + [vp] * 12 + [ci]
         lib.orc_perturb.restype = ci
         lib.orc_perturb.argtypes = [vp, ci, i64, vp, ci, i64, i64, i64, ci, ci]
         lib.orc_bitdiff.restype = ci
@@ -154,6 +159,73 @@ def target_logprob(base: np.ndarray, cand: np.ndarray, target, v: int | None = N
                                  out["logp_cand"].ctypes.data, nthreads)
     if rc != 0:
         raise ValueError("orc_target_logprob rejected its arguments")
+    return out
+
+
+def record(base: np.ndarray, k: int = 20, target=None, v: int | None = None,
+           nthreads: int = 0) -> dict:
+    """Compact ground-truth record of baseline rows: the k largest logits
+    (idx [n, k] int32, val [n, k] float32), lse_rest [n] (ln of the mass outside
+    them), status [n], and logp_target [n] when `target` is given."""
+    assert base.ndim == 2
+    base = np.ascontiguousarray(base)
+    n = base.shape[0]
+    v = base.shape[1] if v is None else v
+    out = dict(idx=np.empty((n, k), np.int32), val=np.empty((n, k), np.float32),
+               lse_rest=np.empty(n), status=np.empty(n, np.uint8))
+    tg = None
+    if target is not None:
+        tg = np.ascontiguousarray(target, dtype=np.int32)
+        assert tg.shape == (n,)
+        out["logp_target"] = np.empty(n)
+    rc = _L().orc_record(base.ctypes.data, dtype_code(base), base.shape[1], n, v, k, _p(tg),
+                         out["idx"].ctypes.data, out["val"].ctypes.data,
+                         out["lse_rest"].ctypes.data, out["status"].ctypes.data,
+                         _p(out.get("logp_target")), nthreads)
+    if rc != 0:
+        raise ValueError("orc_record rejected its arguments")
+    return out
+
+
+def compare_record(rec: dict, cand: np.ndarray, k: int | None = None, target=None,
+                   v: int | None = None, nthreads: int = 0) -> dict:
+    """Compare candidate rows against a record (from record()) using its first
+    k entries; returns the outputs of compare() except kl_full, plus logp_base /
+    logp_cand when `target` is given (logp_base needs a record with targets)."""
+    assert cand.ndim == 2
+    cand = np.ascontiguousarray(cand)
+    n = cand.shape[0]
+    v = cand.shape[1] if v is None else v
+    k_rec = rec["idx"].shape[1]
+    k = k_rec if k is None else k
+    idx = np.ascontiguousarray(rec["idx"], np.int32)
+    val = np.ascontiguousarray(rec["val"], np.float32)
+    lse_rest = np.ascontiguousarray(rec["lse_rest"], np.float64)
+    st = np.ascontiguousarray(rec["status"], np.uint8)
+    assert idx.shape[0] == n
+    out = dict(kl_topk=np.empty(n), margin=np.empty(n), lse_base=np.empty(n),
+               lse_cand=np.empty(n), top1_base=np.empty(n, np.int32),
+               top2_base=np.empty(n, np.int32), top1_cand=np.empty(n, np.int32),
+               flip=np.empty(n, np.uint8), topk_idx=np.empty((n, k), np.int32),
+               status=np.empty(n, np.uint8))
+    tg = rl = None
+    if target is not None:
+        tg = np.ascontiguousarray(target, dtype=np.int32)
+        assert tg.shape == (n,)
+        out["logp_cand"] = np.empty(n)
+        if "logp_target" in rec:
+            rl = np.ascontiguousarray(rec["logp_target"], np.float64)
+            out["logp_base"] = np.empty(n)
+    rc = _L().orc_compare_record(idx.ctypes.data, val.ctypes.data, lse_rest.ctypes.data,
+                                 st.ctypes.data, _p(rl), k_rec, cand.ctypes.data,
+                                 dtype_code(cand), cand.shape[1], n, v, k, _p(tg),
+                                 *[_p(out.get(f)) for f in (
+                                     "kl_topk", "margin", "lse_base", "lse_cand", "top1_base",
+                                     "top2_base", "top1_cand", "flip", "topk_idx", "status",
+                                     "logp_base", "logp_cand")],
+                                 nthreads)
+    if rc != 0:
+        raise ValueError("orc_compare_record rejected its arguments")
     return out
 
 

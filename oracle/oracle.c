@@ -35,6 +35,10 @@
  *     margin strictly above the big-margin threshold is a big-margin flip.
  *   - The target log-probability of a flagged row, or of a target outside
  *     [0, v), is NaN.
+ *   - A stored baseline record keeps the k largest logits with their indices
+ *     and the log of the remaining mass; its status is the baseline's alone.
+ *     Comparing a candidate against it flags NONFINITE when either the record
+ *     or the candidate is NONFINITE, else EMPTY when either is EMPTY.
  */
 #include <math.h>
 #include <stdint.h>
@@ -325,6 +329,234 @@ int orc_target_logprob(const void *base, int tb, int64_t ld_base, const void *ca
     }
     free(x);
     free(y);
+  }
+  return failed ? -1 : 0;
+}
+
+/* ------------------------------------------------------ compact ground-truth record */
+
+/*
+ * The ground truth is run once and its distributions are stored; every later
+ * candidate is compared against that store, never against a previous candidate
+ * ([logits] 先要有一个 ground truth).  What the top-k comparison needs of a
+ * baseline row is its k largest logits with their indices and the mass of the
+ * rest, so that is what a record keeps:
+ *   idx[j], val[j]  the baseline's k largest logits (value descending, index
+ *                   ascending; -1 and -inf past min(k, v))
+ *   lse_rest        ln sum_{i not in the top k} exp(x_i); -inf when nothing is left
+ *   status          NONFINITE (a NaN or +inf) or EMPTY (all -inf) of the baseline
+ *                   alone; a flagged row holds -1 / NaN everywhere
+ *   logp_target     optional: ln p(target) = x[target] - ln sum_i exp(x_i)
+ */
+int orc_record(const void *base, int tb, int64_t ld_base, int64_t n, int64_t v, int k,
+               const int32_t *target, int32_t *idx, float *val, double *lse_rest,
+               uint8_t *status, double *logp_target, int nthreads) {
+  if (!base || !idx || !val || !lse_rest || !status || n < 0 || v < 2 || k < 2 || ld_base < v)
+    return -1;
+  if (tb != ORC_F32 && tb != ORC_BF16) return -1;
+  if (logp_target && !target) return -1;
+  const size_t eb = tb == ORC_BF16 ? 2 : 4;
+  int failed = 0;
+#ifdef _OPENMP
+  if (nthreads > 0) omp_set_num_threads(nthreads);
+#else
+  (void)nthreads;
+#endif
+#pragma omp parallel
+  {
+    double *x = (double *)malloc((size_t)v * sizeof(double));
+    keyed *order = (keyed *)malloc((size_t)v * sizeof(keyed));
+    if (!x || !order) {
+#pragma omp atomic write
+      failed = 1;
+    }
+#pragma omp for schedule(dynamic, 1)
+    for (int64_t r = 0; r < n; r++) {
+      if (!x || !order) continue;
+      const void *br = (const char *)base + (size_t)r * (size_t)ld_base * eb;
+      for (int64_t i = 0; i < v; i++) x[i] = value(br, tb, i);
+      int32_t *ri = idx + (size_t)r * (size_t)k;
+      float *rv = val + (size_t)r * (size_t)k;
+      const uint8_t st = row_status(x, x, v);
+      status[r] = st;
+      if (st) {
+        for (int j = 0; j < k; j++) {
+          ri[j] = -1;
+          rv[j] = NAN;
+        }
+        lse_rest[r] = NAN;
+        if (logp_target) logp_target[r] = NAN;
+        continue;
+      }
+      for (int64_t i = 0; i < v; i++) {
+        order[i].x = x[i];
+        order[i].i = i;
+      }
+      qsort(order, (size_t)v, sizeof(keyed), by_value_desc);
+      const int64_t keff = (int64_t)k < v ? (int64_t)k : v;
+      for (int j = 0; j < k; j++) {
+        ri[j] = j < keff ? (int32_t)order[j].i : -1;
+        rv[j] = j < keff ? (float)order[j].x : -INFINITY;
+      }
+      double m = -INFINITY;
+      for (int64_t j = keff; j < v; j++)
+        if (order[j].x > m) m = order[j].x;
+      if (m == -INFINITY) {
+        lse_rest[r] = -INFINITY;
+      } else {
+        double s = 0.0;
+        for (int64_t j = keff; j < v; j++) s += exp(order[j].x - m);
+        lse_rest[r] = m + log(s);
+      }
+      if (logp_target) {
+        const int32_t t = target[r];
+        logp_target[r] = (t < 0 || (int64_t)t >= v) ? NAN : x[t] - log_normaliser(x, v);
+      }
+    }
+    free(x);
+    free(order);
+  }
+  return failed ? -1 : 0;
+}
+
+/* ln(exp(a) + exp(b)) */
+static double log_add(double a, double b) {
+  if (a == -INFINITY) return b;
+  if (b == -INFINITY) return a;
+  const double m = a > b ? a : b;
+  return m + log(exp(a - m) + exp(b - m));
+}
+
+/*
+ * Compare candidate rows against a record of k_rec entries per row, using its
+ * first k (k <= k_rec): the same top-k + "other" KL, margin, flip, top-1 and
+ * normalisers as the full compare ([logits] 怎么比两个分布), from the record and
+ * the candidate row alone.  The baseline distribution over the head and the
+ * bucket is rebuilt from the record: ln p_j = val_j - L, ln p_o = R - L with
+ * R = ln(sum_{k <= j < k_rec} exp(val_j) + exp(lse_rest)) and L = ln(sum_{j<k}
+ * exp(val_j) + exp(R)).  The candidate's bucket is summed directly over the
+ * columns outside the head.  The full KL needs the whole baseline row and is
+ * not produced.  Status: NONFINITE if either the record or the candidate is
+ * NONFINITE, else EMPTY if either is EMPTY.
+ */
+int orc_compare_record(const int32_t *idx, const float *val, const double *lse_rest,
+                       const uint8_t *rec_status, const double *rec_logp, int k_rec,
+                       const void *cand, int tc, int64_t ld_cand, int64_t n, int64_t v, int k,
+                       const int32_t *target, double *kl_topk, double *margin, double *lse_base,
+                       double *lse_cand, int32_t *top1_base, int32_t *top2_base,
+                       int32_t *top1_cand, uint8_t *flip, int32_t *topk_idx, uint8_t *status,
+                       double *logp_base, double *logp_cand, int nthreads) {
+  if (!idx || !val || !lse_rest || !rec_status || !cand || n < 0 || v < 2 || k < 1 ||
+      k_rec < 2 || k > k_rec || ld_cand < v)
+    return -1;
+  if (tc != ORC_F32 && tc != ORC_BF16) return -1;
+  if ((logp_base && !rec_logp) || ((logp_base || logp_cand) && !target)) return -1;
+  const size_t ec = tc == ORC_BF16 ? 2 : 4;
+  int failed = 0;
+#ifdef _OPENMP
+  if (nthreads > 0) omp_set_num_threads(nthreads);
+#else
+  (void)nthreads;
+#endif
+#pragma omp parallel
+  {
+    double *y = (double *)malloc((size_t)v * sizeof(double));
+    unsigned char *in_head = (unsigned char *)malloc((size_t)v);
+    if (!y || !in_head) {
+#pragma omp atomic write
+      failed = 1;
+    }
+#pragma omp for schedule(dynamic, 1)
+    for (int64_t r = 0; r < n; r++) {
+      if (!y || !in_head) continue;
+      const void *cr = (const char *)cand + (size_t)r * (size_t)ld_cand * ec;
+      for (int64_t i = 0; i < v; i++) y[i] = value(cr, tc, i);
+      const int32_t *ri = idx + (size_t)r * (size_t)k_rec;
+      const float *rv = val + (size_t)r * (size_t)k_rec;
+      const uint8_t sc = row_status(y, y, v);
+      const uint8_t sr = rec_status[r];
+      const uint8_t st = (sr == ORC_ROW_NONFINITE || sc == ORC_ROW_NONFINITE) ? ORC_ROW_NONFINITE
+                         : (sr || sc)                                          ? ORC_ROW_EMPTY
+                                                                               : 0;
+      if (status) status[r] = st;
+      if (topk_idx)
+        for (int j = 0; j < k; j++) topk_idx[(size_t)r * k + j] = st ? -1 : ri[j];
+      if (st) {
+        if (kl_topk) kl_topk[r] = NAN;
+        if (margin) margin[r] = NAN;
+        if (lse_base) lse_base[r] = NAN;
+        if (lse_cand) lse_cand[r] = NAN;
+        if (top1_base) top1_base[r] = -1;
+        if (top2_base) top2_base[r] = -1;
+        if (top1_cand) top1_cand[r] = -1;
+        if (flip) flip[r] = 0;
+        if (logp_base) logp_base[r] = NAN;
+        if (logp_cand) logp_cand[r] = NAN;
+        continue;
+      }
+      /* baseline side from the record */
+      double R = lse_rest[r];
+      for (int j = k; j < k_rec; j++)
+        if (ri[j] >= 0) R = log_add(R, (double)rv[j]);
+      double L = R;
+      for (int j = 0; j < k; j++)
+        if (ri[j] >= 0) L = log_add(L, (double)rv[j]);
+      /* candidate side: full normaliser, and the bucket over columns outside the head */
+      const double lse_y = log_normaliser(y, v);
+      memset(in_head, 0, (size_t)v);
+      for (int j = 0; j < k; j++)
+        if (ri[j] >= 0) in_head[ri[j]] = 1;
+      double mo = -INFINITY;
+      for (int64_t i = 0; i < v; i++)
+        if (!in_head[i] && y[i] > mo) mo = y[i];
+      double Ry = -INFINITY;
+      if (mo > -INFINITY) {
+        double s = 0.0;
+        for (int64_t i = 0; i < v; i++)
+          if (!in_head[i]) s += exp(y[i] - mo);
+        Ry = mo + log(s);
+      }
+      /* top-k + other KL, with the infinite cases of the full compare */
+      double klk = 0.0;
+      int inf_k = 0;
+      for (int j = 0; j < k; j++) {
+        if (ri[j] < 0 || rv[j] == -INFINITY) continue;
+        const double yj = y[ri[j]];
+        if (yj == -INFINITY) {
+          inf_k = 1;
+          continue;
+        }
+        const double lp = (double)rv[j] - L, lq = yj - lse_y;
+        klk += exp(lp) * (lp - lq);
+      }
+      if (R > -INFINITY) {
+        if (Ry == -INFINITY) {
+          inf_k = 1;
+        } else {
+          const double lpo = R - L, lqo = Ry - lse_y;
+          klk += exp(lpo) * (lpo - lqo);
+        }
+      }
+      int64_t best = 0;
+      for (int64_t i = 1; i < v; i++)
+        if (y[i] > y[best]) best = i;
+      if (kl_topk) kl_topk[r] = inf_k ? INFINITY : klk;
+      if (margin) margin[r] = (double)rv[0] - (double)rv[1];
+      if (lse_base) lse_base[r] = L;
+      if (lse_cand) lse_cand[r] = lse_y;
+      if (top1_base) top1_base[r] = ri[0];
+      if (top2_base) top2_base[r] = ri[1];
+      if (top1_cand) top1_cand[r] = (int32_t)best;
+      if (flip) flip[r] = (uint8_t)(best != ri[0]);
+      if (logp_base || logp_cand) {
+        const int32_t t = target[r];
+        const int ok = t >= 0 && (int64_t)t < v;
+        if (logp_base) logp_base[r] = ok ? rec_logp[r] : NAN;
+        if (logp_cand) logp_cand[r] = ok ? y[t] - lse_y : NAN;
+      }
+    }
+    free(y);
+    free(in_head);
   }
   return failed ? -1 : 0;
 }

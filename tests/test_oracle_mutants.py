@@ -26,7 +26,7 @@ MUTANTS = [
     ("full KL log ratio sign",
      "    kl += exp(lp) * (lp - lq);", "    kl += exp(lp) * (lq - lp);"),
     ("other bucket dropped from top-k KL",
-     "      klk += exp(lpo) * (lpo - lqo);", "      klk += 0.0 * (lpo - lqo);"),
+     "\n      klk += exp(lpo) * (lpo - lqo);", "\n      klk += 0.0 * (lpo - lqo);"),
     ("other bucket on the candidate side uses baseline mass",
      "        sy += exp(y[i] - mo_y);", "        sy += exp(x[i] - mo_y);"),
     ("other bucket misses its first token",
@@ -37,9 +37,11 @@ MUTANTS = [
     ("top-k ties broken by the higher index",
      "  return (a->i < b->i) ? -1 : (a->i > b->i);", "  return (a->i > b->i) ? -1 : (a->i < b->i);"),
     ("top-k ranked by the candidate",
-     "    order[i].x = x[i];", "    order[i].x = y[i];"),
+     "\n    order[i].x = x[i];", "\n    order[i].x = y[i];"),
     ("candidate argmax ties broken by the higher index",
-     "    if (y[i] > y[best]) best = i;", "    if (y[i] >= y[best]) best = i;"),
+     "\n    if (y[i] > y[best]) best = i;", "\n    if (y[i] >= y[best]) best = i;"),
+    ("record compare argmax ties broken by the higher index",
+     "\n        if (y[i] > y[best]) best = i;", "\n        if (y[i] >= y[best]) best = i;"),
     ("margin sign",
      "  o->margin = order[0].x - order[1].x;", "  o->margin = order[1].x - order[0].x;"),
     ("+inf not flagged",
@@ -74,6 +76,17 @@ MUTANTS = [
      "  if (E < emin) E = emin;", "  (void)emin;"),
     ("e4m3 without saturation",
      "  if (r > 448.0) r = 448.0;", "  if (r > 480.0) r = 480.0;"),
+    ("record rest mass includes the head",
+     "        for (int64_t j = keff; j < v; j++) s += exp(order[j].x - m);",
+     "        for (int64_t j = 0; j < v; j++) s += exp(order[j].x - m);"),
+    ("record entries past k left out of the bucket",
+     "        if (ri[j] >= 0) R = log_add(R, (double)rv[j]);", "        (void)rv;"),
+    ("record baseline normalised without the bucket",
+     "      double L = R;", "      double L = -INFINITY;"),
+    ("candidate bucket includes the head",
+     "          if (!in_head[i]) s += exp(y[i] - mo);", "          s += exp(y[i] - mo);"),
+    ("record compare ignores a non-finite candidate",
+     "(sr == ORC_ROW_NONFINITE || sc == ORC_ROW_NONFINITE)", "(sr == ORC_ROW_NONFINITE)"),
     ("flagged rows binned instead of excluded",
      "    if (status && status[r] != 0) {\n      summary[g].excluded++;\n      continue;\n    }",
      "    if (status && status[r] != 0) {\n      summary[g].excluded++;\n    }"),

@@ -508,3 +508,105 @@ def test_keep_mantissa_closed_forms(m):
     assert np.array_equal(oracle.perturb(-x, oracle.PERTURB_MANTISSA, m)[0], -r)
     order = np.argsort(x, kind="stable")
     assert np.all(np.diff(r[order][np.isfinite(r[order])]) >= 0)
+
+
+# ------------------------------------------------------------------ compact record pins
+_REC_INT = ("top1_base", "top2_base", "top1_cand", "flip", "topk_idx", "status")
+
+
+def _assert_record_matches_full(base, cand, k, k_rec, target=None):
+    """The record path must give what the full compare (pinned above) gives:
+    the record is a sufficient statistic of the top-k + other comparison."""
+    full = oracle.compare(base, cand, k=k)
+    rec = oracle.record(base, k=k_rec, target=target)
+    r = oracle.compare_record(rec, cand, k=k, target=target)
+    for f in _REC_INT:
+        assert np.array_equal(full[f], r[f]), f
+    ok = full["status"] == 0
+    for f in ("kl_topk", "margin", "lse_base", "lse_cand"):
+        a, b = full[f][ok], r[f][ok]
+        fin = np.isfinite(a)
+        assert np.array_equal(fin, np.isfinite(b)) and np.array_equal(a[~fin], b[~fin]), f
+        assert np.all(np.abs(a[fin] - b[fin]) <= 1e-12 + 1e-8 * np.abs(a[fin])), f
+        assert np.all(np.isnan(r[f][~ok])), f
+    if target is not None:
+        lp = oracle.target_logprob(base, cand, target)
+        for f in ("logp_base", "logp_cand"):
+            a, b = lp[f], r[f]
+            assert np.array_equal(np.isnan(a), np.isnan(b)), f
+            m = ~np.isnan(a)
+            assert np.all(np.abs(a[m] - b[m]) <= 1e-12 * (1 + np.abs(a[m]))), f
+    return rec, r
+
+
+@pytest.mark.parametrize("k,k_rec", [(1, 2), (2, 2), (5, 20), (20, 20), (20, 64), (64, 64)])
+def test_record_path_equals_full_compare(k, k_rec):
+    a, b = synth.tiny(11, 0, 48, 700)
+    target = (np.arange(48, dtype=np.int32) * 37) % 700
+    target[3] = -1
+    target[4] = 700
+    _assert_record_matches_full(a, b, k, k_rec, target)
+
+
+def test_record_path_equals_full_compare_on_corpus_and_bf16_rows():
+    a, b = synth.corpus(5, 0, 24, 4099, 1000)          # fp32 baseline, bf16 candidate
+    _assert_record_matches_full(a, b, 20, 20)
+    sa, sb = synth.stream(6, 0, 24, 3001)              # both bf16
+    _assert_record_matches_full(sa, sb, 20, 32)
+
+
+def test_record_path_with_ties_and_small_vocabularies():
+    rng = np.random.default_rng(2)
+    a = rng.integers(-3, 3, (64, 40)).astype(np.float32)   # many equal logits
+    b = (a + rng.integers(-1, 2, a.shape)).astype(np.float32)
+    _assert_record_matches_full(a, b, 20, 20)
+    for v in (2, 3, 5):                                    # v <= k: nothing left over
+        rec, r = _assert_record_matches_full(a[:, :v].copy(), b[:, :v].copy(), 20, 20)
+        assert np.all(rec["lse_rest"] == -np.inf)
+        assert np.all(rec["idx"][:, v:] == -1) and np.all(rec["val"][:, v:] == -np.inf)
+
+
+def test_record_flagged_and_infinite_rows():
+    v = 16
+    a = np.zeros((7, v), np.float32)
+    b = np.zeros((7, v), np.float32)
+    a[0, 3] = np.nan                 # baseline NaN: the record itself is flagged
+    b[1, 4] = np.inf                 # candidate +inf outside the head
+    a[2, :] = -np.inf                # baseline empty
+    b[3, 5] = -np.inf                # candidate -inf in the bucket: finite top-k KL
+    b[4, :] = -np.inf                # candidate empty
+    b[5, 0] = np.nan                 # candidate NaN on a head token
+    a[6, 7:] = -np.inf               # baseline -inf tokens add nothing
+    b[6, 7:] = 1.0
+    rec, r = _assert_record_matches_full(a, b, 4, 8)
+    assert list(rec["status"]) == [1, 0, 2, 0, 0, 0, 0]
+    assert np.isnan(rec["lse_rest"][0]) and np.all(rec["idx"][0] == -1)
+    assert list(r["status"]) == [1, 1, 2, 0, 2, 1, 0]
+    r6 = oracle.compare_record(oracle.record(a[3:4], k=6), b[3:4], k=6)
+    assert r6["kl_topk"][0] == np.inf    # token 5 now in the head, candidate -inf
+
+
+def test_record_long_tail_example_and_merged_buckets():
+    """The page's long-tail example seen through a record: head unchanged and
+    tail total unchanged, so top-20 + other is zero; and with k = 2 of a record
+    of 4, top-2 + other is the KL of the merged 3-bucket distributions."""
+    g, p, q = _long_tail_rows()
+    r = oracle.compare_record(oracle.record(_logits(p), k=20), _logits(q), k=20)
+    assert abs(r["kl_topk"][0]) < 1e-9
+    g = _kv("cat_dog.txt")
+    p = np.array(g["p"], float)
+    q = np.array(g["q"], float)
+    r = oracle.compare_record(oracle.record(_logits(p), k=4), _logits(q), k=2)
+    pf = scipy.special.softmax(_logits(p).astype(np.float64)[0])
+    qf = scipy.special.softmax(_logits(q).astype(np.float64)[0])
+    pm = np.array([pf[0], pf[1], pf[2] + pf[3]])
+    qm = np.array([qf[0], qf[1], qf[2] + qf[3]])
+    assert r["kl_topk"][0] == pytest.approx(scipy.special.rel_entr(pm, qm).sum(), rel=1e-12)
+
+
+def test_record_rest_mass_closed_form():
+    """lse_rest of a uniform row of v equal logits with k taken is ln(v - k)."""
+    v, k = 1000, 20
+    rec = oracle.record(np.zeros((2, v), np.float32), k=k)
+    assert np.allclose(rec["lse_rest"], math.log(v - k), rtol=0, atol=1e-12)
+    assert np.array_equal(rec["idx"][0], np.arange(k))   # ties: lowest indices
