@@ -270,7 +270,7 @@ def bin_report(margin, flip, kl_topk, kl_full, edges, status=None, group=None, n
     margin = np.ascontiguousarray(margin, np.float64)
     flip = np.ascontiguousarray(flip, np.uint8)
     kl_topk = np.ascontiguousarray(kl_topk, np.float64)
-    kl_full = np.ascontiguousarray(kl_full, np.float64)
+    kl_full = None if kl_full is None else np.ascontiguousarray(kl_full, np.float64)
     edges = np.ascontiguousarray(edges, np.float64)
     st = None if status is None else np.ascontiguousarray(status, np.uint8)
     gr = None if group is None else np.ascontiguousarray(group, np.int32)
@@ -278,7 +278,7 @@ def bin_report(margin, flip, kl_topk, kl_full, edges, status=None, group=None, n
     bins = np.zeros((n_groups, edges.size), dtype=BIN_DTYPE)
     summ = np.zeros(n_groups, dtype=SUMMARY_DTYPE)
     rc = _L().orc_bin_report(margin.ctypes.data, flip.ctypes.data, kl_topk.ctypes.data,
-                             kl_full.ctypes.data, _p(st), _p(gr), n_groups, n, edges.ctypes.data,
+                             _p(kl_full), _p(st), _p(gr), n_groups, n, edges.ctypes.data,
                              edges.size, big_margin, bins.ctypes.data, summ.ctypes.data)
     if rc != 0:
         raise ValueError("orc_bin_report rejected its arguments")

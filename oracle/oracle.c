@@ -742,7 +742,7 @@ int orc_bin_report(const double *margin, const uint8_t *flip, const double *kl_t
                    const double *kl_full, const uint8_t *status, const int32_t *group,
                    int n_groups, int64_t n, const double *edges, int n_edges, double big_margin,
                    orc_bin *bins, orc_group_summary *summary) {
-  if (!margin || !flip || !kl_topk || !kl_full || !edges || !bins || !summary) return -1;
+  if (!margin || !flip || !kl_topk || !edges || !bins || !summary) return -1;
   if (n_groups < 1 || n_edges < 1 || n < 0) return -1;
   for (int j = 0; j < n_edges; j++) {
     if (isnan(edges[j]) || edges[j] <= 0.0) return -1;
@@ -776,7 +776,7 @@ int orc_bin_report(const double *margin, const uint8_t *flip, const double *kl_t
       bn->tie_flips += flip[r] ? 1 : 0;
     }
     bn->sum_kl_topk += kl_topk[r];
-    bn->sum_kl_full += kl_full[r];
+    bn->sum_kl_full += kl_full ? kl_full[r] : NAN; /* no full KL: NaN */
     if (kl_topk[r] > bn->max_kl_topk) bn->max_kl_topk = kl_topk[r];
   }
   return 0;

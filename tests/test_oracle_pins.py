@@ -376,6 +376,24 @@ def test_bin_report_hand_counted():
     assert summ[0]["excluded"] == 1 and summ[0]["unbinned"] == 0
 
 
+def test_bin_report_without_full_kl():
+    """A comparison against a record has no full KL: the counts and top-k sums
+    are those of the report with it, and sum_kl_full is NaN exactly in the bins
+    that hold rows."""
+    edges = np.array(synth.DEFAULT_EDGES)
+    margin = np.array([0.0, 0.05, 0.3, 1.5, 3.0])
+    flip = np.array([1, 0, 1, 1, 0], np.uint8)
+    kl = np.arange(5, dtype=np.float64) * 0.01
+    b1, s1 = oracle.bin_report(margin, flip, kl, kl * 2, edges)
+    b0, s0 = oracle.bin_report(margin, flip, kl, None, edges)
+    for f in ("count", "flips", "ties", "tie_flips", "sum_kl_topk", "max_kl_topk"):
+        assert np.array_equal(b0[f], b1[f]), f
+    assert s0.tobytes() == s1.tobytes()
+    held = b0["count"][0] > 0
+    assert np.all(np.isnan(b0["sum_kl_full"][0][held]))
+    assert np.all(b0["sum_kl_full"][0][~held] == 0.0)
+
+
 def test_bin_report_groups_and_unbinned():
     edges = np.array([0.5, 1.0])
     margin = np.array([0.2, 0.7, 5.0, 0.2, np.inf])
