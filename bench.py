@@ -18,8 +18,14 @@ Prints ONE JSON line on stdout (everything else goes to stderr):
              they were taken on the current kernel source, else null
   cpu_baseline  the double-precision CPU oracle on a bounded row sample
 
+With --path record the step is instead the comparison against a compact
+record of the baseline (lcmp_compare_record + lcmp_bin_report): the record is
+made once before the timed region, and the streaming kernel reads only the
+candidate rows (N*V*(bytes per candidate element) per launch).
+
 Flags: --gpus N (only 1 is supported: this path runs on one GPU),
 --steps K, --warmup W, --workload {corpus,segment,stream,tiny},
+--path {compare,record},
 --cpu-seconds S (budget of the oracle leg), --no-cpu-baseline,
 --copy-probe BYTES (run only a plain device copy of that size, for counter
 calibration under rocprofv3).
@@ -40,33 +46,41 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
 METRIC = "logit positions/sec at V=151936 + achieved HBM GB/s vs MI355X peak"
-COUNTERS_FILE = os.path.join(ROOT, "profiles", "k_row_stats_corpus_counters.md")
-KERNEL_SOURCES = ("k_row_stats.hip", "common.hpp")
+# per path: the dominant kernel, its committed counter summary and its sources
+PATHS = {
+    "compare": dict(kernel="k_row_stats",
+                    counters=os.path.join(ROOT, "profiles", "k_row_stats_corpus_counters.md"),
+                    sources=("k_row_stats.hip", "common.hpp", "dma.hpp")),
+    "record": dict(kernel="k_rest_sum",
+                   counters=os.path.join(ROOT, "profiles", "k_rest_sum_corpus_counters.md"),
+                   sources=("k_rest_sum.hip", "common.hpp", "dma.hpp")),
+}
 
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def kernel_hash() -> str:
+def kernel_hash(path: str = "compare") -> str:
     h = hashlib.sha256()
-    for name in KERNEL_SOURCES:
+    for name in PATHS[path]["sources"]:
         with open(os.path.join(ROOT, "logit_distribution_diffing_amd", "csrc", name), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
 
 
-def stored_traffic(workload: str):
-    """HBM bytes per launch of the streaming kernel from the committed counter
-    summary, if it was taken on this kernel source and workload."""
-    if not os.path.exists(COUNTERS_FILE):
+def stored_traffic(workload: str, path: str = "compare"):
+    """HBM bytes per launch of the path's streaming kernel from the committed
+    counter summary, if it was taken on this kernel source and workload."""
+    counters = PATHS[path]["counters"]
+    if not os.path.exists(counters):
         return None
-    text = open(COUNTERS_FILE).read()
+    text = open(counters).read()
     m = re.search(r"```json\n(.*?)\n```", text, re.S)
     if not m:
         return None
     rec = json.loads(m.group(1))
-    if rec.get("kernel_hash") != kernel_hash() or rec.get("workload") != workload:
+    if rec.get("kernel_hash") != kernel_hash(path) or rec.get("workload") != workload:
         return None
     return rec.get("traffic_bytes_per_launch")
 
@@ -151,6 +165,29 @@ def cpu_leg(host_a, host_b, k, edges, seconds: float):
                        f"{dt:.1f} s")
 
 
+def cpu_leg_record(host_a, host_b, k, edges, seconds: float):
+    """Time the oracle's comparison against a record (+ bins) on a bounded sample
+    of rows; the sample's record is made first, outside the timing, as the
+    record of a baseline is made once."""
+    import oracle
+    threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    rows_avail = host_a.shape[0]
+    probe = min(rows_avail, max(threads, 16))
+    rec = oracle.record(host_a[:probe], k=k, nthreads=threads)
+    t0 = time.perf_counter()
+    oracle.compare_record(rec, host_b[:probe], k=k, nthreads=threads)
+    per_row = (time.perf_counter() - t0) / probe
+    rows = int(max(probe, min(rows_avail, seconds / max(per_row, 1e-9))))
+    rec = oracle.record(host_a[:rows], k=k, nthreads=threads)
+    t0 = time.perf_counter()
+    o = oracle.compare_record(rec, host_b[:rows], k=k, nthreads=threads)
+    oracle.bin_report(o["margin"], o["flip"], o["kl_topk"], None, edges, status=o["status"])
+    dt = time.perf_counter() - t0
+    return dict(value=rows / dt, unit="positions/s", cores=threads, kind="oracle",
+                sample=f"first {rows} positions of the workload (comparison against their "
+                       f"record + bins), {dt:.1f} s")
+
+
 def copy_probe(nbytes: int):
     import torch
     src = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda").fill_(1.0)
@@ -173,6 +210,10 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", type=int, default=0)
+    ap.add_argument("--path", default="compare", choices=["compare", "record"],
+                    help="compare: baseline and candidate rows, full comparison (default); "
+                         "record: the candidate against a compact record of the baseline, "
+                         "made once before the timed steps")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -195,24 +236,46 @@ def main():
     edges = list(synth.DEFAULT_EDGES)
     base, cand, host_a, host_b = make_inputs(args.workload, w, torch)
     esize = {"f32": 4, "bf16": 2}
-    bytes_per_launch = n * v * (esize[w["base"]] + esize[w["cand"]])
-
-    out = L.alloc_compare_outputs(n, k, base.device, with_bitdiff=True)
-    ws = torch.empty(L.compare_workspace_bytes(n, v, k, True), dtype=torch.uint8, device="cuda")
+    hip = Hip()
+    evs = [(hip.event(), hip.event()) for _ in range(args.steps)]
+    stream = torch.cuda.current_stream()
     bws = torch.empty(int(L.lib().lcmp_bin_workspace_bytes(n, 1, len(edges))), dtype=torch.uint8,
                       device="cuda")
     bins = torch.empty((len(edges), L.BIN_BYTES), dtype=torch.uint8, device="cuda")
     summ = torch.empty((1, L.GROUP_SUMMARY_BYTES), dtype=torch.uint8, device="cuda")
-    hip = Hip()
-    evs = [(hip.event(), hip.event()) for _ in range(args.steps)]
-    stream = torch.cuda.current_stream()
 
-    def step(ev=None):
-        L.lcmp_compare_logits(base, cand, k=k, with_bitdiff=True, out=out, workspace=ws,
-                              stream=stream, events=ev)
-        L.lcmp_bin_report(out["margin"], out["flip"], out["kl_topk"], out["kl_full"], edges,
-                          status=out["status"], workspace=bws, stream=stream, bins=bins,
-                          summary=summ)
+    if args.path == "compare":
+        # the streaming kernel reads both rows once
+        bytes_per_launch = n * v * (esize[w["base"]] + esize[w["cand"]])
+        out = L.alloc_compare_outputs(n, k, base.device, with_bitdiff=True)
+        ws = torch.empty(L.compare_workspace_bytes(n, v, k, True), dtype=torch.uint8,
+                         device="cuda")
+
+        def step(ev=None):
+            L.lcmp_compare_logits(base, cand, k=k, with_bitdiff=True, out=out, workspace=ws,
+                                  stream=stream, events=ev)
+            L.lcmp_bin_report(out["margin"], out["flip"], out["kl_topk"], out["kl_full"], edges,
+                              status=out["status"], workspace=bws, stream=stream, bins=bins,
+                              summary=summ)
+    else:
+        # the baseline is recorded once; the timed steps read the candidate rows
+        # and the record only
+        record = L.lcmp_record_baseline(base, k_rec=k)
+        torch.cuda.synchronize()
+        del base
+        torch.cuda.empty_cache()
+        bytes_per_launch = n * v * esize[w["cand"]]
+        out = L.alloc_compare_outputs(n, k, cand.device)
+        del out["kl_full"]
+        ws = torch.empty(int(L.lib().lcmp_compare_record_workspace_bytes(n, v)),
+                         dtype=torch.uint8, device="cuda")
+
+        def step(ev=None):
+            L.lcmp_compare_record(record, cand, k=k, out=out, workspace=ws, stream=stream,
+                                  events=ev)
+            L.lcmp_bin_report(out["margin"], out["flip"], out["kl_topk"], None, edges,
+                              status=out["status"], workspace=bws, stream=stream, bins=bins,
+                              summary=summ)
 
     for _ in range(args.warmup):
         step()
@@ -241,14 +304,15 @@ def main():
         f"big-margin flips {int(s_np[0]['big_margin_flips'])}")
 
     achieved = bytes_per_launch / kern_avg_s / 1e9
-    traffic = stored_traffic(args.workload)
+    traffic = stored_traffic(args.workload, args.path)
     roofline = dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBS, unit="GB/s",
                     frac=round(achieved / HBM_PEAK_GBS, 4), traffic=traffic,
-                    kernel="k_row_stats", bytes_per_launch=bytes_per_launch)
+                    kernel=PATHS[args.path]["kernel"], bytes_per_launch=bytes_per_launch)
 
     cpu = None
     if not args.no_cpu_baseline and host_a is not None:
-        cpu = cpu_leg(host_a, host_b, k, edges, args.cpu_seconds)
+        leg = cpu_leg if args.path == "compare" else cpu_leg_record
+        cpu = leg(host_a, host_b, k, edges, args.cpu_seconds)
         log(f"[bench] cpu oracle: {cpu['value']:.1f} positions/s on {cpu['cores']} threads")
 
     value = n * args.steps / (gpu_ms / 1e3)
@@ -264,8 +328,9 @@ def main():
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
         "data": "synthetic",
-        "config": {"workload": wdesc, "n": n, "v": v, "k": k, "base": w["base"],
-                   "cand": w["cand"], "bitwise_stats": True, "margin_edges": len(edges),
+        "config": {"workload": wdesc, "path": args.path, "n": n, "v": v, "k": k,
+                   "base": w["base"], "cand": w["cand"],
+                   "bitwise_stats": args.path == "compare", "margin_edges": len(edges),
                    "hbm_gbs_step": round(bytes_per_launch / (ms_per_step / 1e3) / 1e9, 1)},
         "roofline": roofline,
         "cpu_baseline": cpu,

@@ -44,7 +44,7 @@
 extern "C" {
 #endif
 
-#define LCMP_ABI_VERSION 2
+#define LCMP_ABI_VERSION 3
 #define LCMP_MAX_K 64       /* largest top-k */
 #define LCMP_MAX_EDGES 32   /* largest number of margin-bin edges */
 #define LCMP_MAX_GROUPS 256 /* largest number of row groups in lcmp_bin_report */
@@ -219,6 +219,77 @@ int lcmp_bitdiff(const void *a, int ta, int64_t lda, const void *b, int tb, int6
 int lcmp_perturb(const void *src, int ts, int64_t ld_src, void *dst, int td, int64_t ld_dst,
                  int64_t rows, int64_t cols, int mode, int param, void *stream);
 
+/* ---------------------------------------------------------------- compact record */
+
+/*
+ * A compact record of baseline rows ([logits] 先要有一个 ground truth: run the
+ * ground truth once over the fixed text, store its distributions, and compare
+ * every later change against that store rather than against the previous
+ * version).  Per row it keeps what the top-k + "other" comparison needs:
+ *   topk_idx     device [n, k_rec]: the k_rec largest logits' columns, value
+ *                descending, index ascending; -1 past min(k_rec, v)
+ *   topk_val     device [n, k_rec]: those logits (bf16 widened exactly); -inf
+ *                past min(k_rec, v)
+ *   lse_rest     device [n]: ln of the sum of exp(logit) over every other
+ *                column; -inf when nothing is left
+ *   status       device [n]: LCMP_ROW_NONFINITE / LCMP_ROW_EMPTY of the baseline
+ *                row alone; a flagged row holds -1 / NaN in the fields above
+ *   logp_target  device [n] or NULL: ln p(target) of the baseline, filled when
+ *                the record is made with targets
+ * At k_rec = 20 a row takes 169 bytes (177 with logp_target), against 4 v bytes
+ * of an fp32 row.  Records are plain arrays: the caller stores and reloads them.
+ */
+typedef struct {
+  int32_t *topk_idx;
+  float *topk_val;
+  double *lse_rest;
+  uint8_t *status;
+  double *logp_target;
+} lcmp_record;
+
+/* Workspace bytes of lcmp_record_baseline (0 on invalid sizes). */
+size_t lcmp_record_workspace_bytes(int64_t n, int64_t v, int k_rec);
+
+/*
+ * Make the record of n baseline rows (the first v columns of each).
+ *   base     device [n, ld_base] of type tb.
+ *   k_rec    entries per row, 2..LCMP_MAX_K (a comparison may use any k <= k_rec).
+ *   target   device [n] or NULL; required when rec->logp_target is set.  A target
+ *            outside [0, v) gives NaN.
+ *   rec      host struct of device arrays, filled by the call.
+ * Errors: LCMP_ESHAPE for k_rec outside [2, LCMP_MAX_K], v < 2 or ld_base < v;
+ * LCMP_EINVAL for a NULL array or logp_target without target.
+ */
+int lcmp_record_baseline(const void *base, int tb, int64_t ld_base, int64_t n, int64_t v,
+                         int k_rec, const int32_t *target, const lcmp_record *rec,
+                         void *workspace, size_t ws_bytes, void *stream);
+
+/* Workspace bytes of lcmp_compare_record (0 on invalid sizes). */
+size_t lcmp_compare_record_workspace_bytes(int64_t n, int64_t v);
+
+/*
+ * Compare n candidate rows against a record made with k_rec entries per row,
+ * using its first k (1 <= k <= k_rec): reads the record and the candidate only,
+ * so half the bytes of lcmp_compare_logits for equal element types.
+ *   out   as for lcmp_compare_logits, with the same definitions, except:
+ *         kl_full must be NULL (it needs the whole baseline row; LCMP_EINVAL
+ *         otherwise); logp_base is the record's logp_target (LCMP_EINVAL when the
+ *         record has none); lse_base is rebuilt from the record.
+ * The status is LCMP_ROW_NONFINITE when the record row or the candidate row is,
+ * else LCMP_ROW_EMPTY when either is.  The record must come from
+ * lcmp_record_baseline with the same v; its entries are only read.
+ */
+int lcmp_compare_record(const lcmp_record *rec, int k_rec, const void *cand, int tc,
+                        int64_t ld_cand, int64_t n, int64_t v, int k, const lcmp_row_out *out,
+                        void *workspace, size_t ws_bytes, void *stream);
+
+/* Instrumented form: ev_before / ev_after (hipEvent_t, may be NULL) are recorded
+ * on `stream` around the candidate's streaming kernel. */
+int lcmp_compare_record_timed(const lcmp_record *rec, int k_rec, const void *cand, int tc,
+                              int64_t ld_cand, int64_t n, int64_t v, int k,
+                              const lcmp_row_out *out, void *workspace, size_t ws_bytes,
+                              void *stream, void *ev_before, void *ev_after);
+
 /* ---------------------------------------------------------------- margin bins */
 
 #define LCMP_MAX_BIN_ROWS (1LL << 36) /* largest n of lcmp_bin_report */
@@ -231,7 +302,9 @@ size_t lcmp_bin_workspace_bytes(int64_t n, int n_groups, int n_edges);
  * Flip counts and KL sums per margin bin and group ([logits] 三者联合起来验证精度
  * 问题: bin flips by margin, compare each bin with the normal difference, and
  * treat a flip at a large margin as a stop).
- *   margin, flip, kl_topk, kl_full   device [n], typically lcmp_compare_logits output.
+ *   margin, flip, kl_topk, kl_full   device [n], typically lcmp_compare_logits output;
+ *            kl_full may be NULL (a comparison against a record has none), and
+ *            then sum_kl_full is NaN in every bin that holds a row.
  *   status   device [n] or NULL; rows with a nonzero status count as `excluded`.
  *   group    device [n] or NULL (all rows in group 0); ids outside [0, n_groups)
  *            are skipped.

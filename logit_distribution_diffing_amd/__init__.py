@@ -11,6 +11,8 @@ Entry points (same names as the C ABI):
   lcmp_bitdiff(a, b)                                         -> structured tensor
   lcmp_bin_report(margin, flip, kl_topk, kl_full, edges, ...) -> (bins, summary)
   lcmp_perturb(src, mode, param)                             -> perturbed tensor
+  lcmp_record_baseline(base, k_rec=20, target=None)          -> record (dict of tensors)
+  lcmp_compare_record(record, cand, k=None, target=None)     -> dict of tensors
 """
 from __future__ import annotations
 
@@ -26,14 +28,17 @@ LCMP_F32, LCMP_BF16 = 0, 1
 LCMP_WITH_BITDIFF = 1
 LCMP_ROW_NONFINITE, LCMP_ROW_EMPTY = 1, 2
 LCMP_MAX_K = 64
-ABI_VERSION = 2
+ABI_VERSION = 3
 LCMP_PERTURB_MANTISSA, LCMP_PERTURB_E4M3, LCMP_PERTURB_E4M3_SCALED = 0, 1, 2
 STATUS_NAMES = {0: "LCMP_OK", -1: "LCMP_EINVAL", -2: "LCMP_EDTYPE", -3: "LCMP_ESHAPE",
                 -4: "LCMP_EWORKSPACE", -5: "LCMP_EHIP", -6: "LCMP_EEDGES"}
 
 EXPORTED = ("lcmp_abi_version", "lcmp_strerror", "lcmp_compare_workspace_bytes",
             "lcmp_compare_logits", "lcmp_compare_logits_timed", "lcmp_bitdiff_workspace_bytes",
-            "lcmp_bitdiff", "lcmp_bin_workspace_bytes", "lcmp_bin_report", "lcmp_perturb")
+            "lcmp_bitdiff", "lcmp_bin_workspace_bytes", "lcmp_bin_report", "lcmp_perturb",
+            "lcmp_record_workspace_bytes", "lcmp_record_baseline",
+            "lcmp_compare_record_workspace_bytes", "lcmp_compare_record",
+            "lcmp_compare_record_timed")
 
 
 class LcmpError(RuntimeError):
@@ -51,6 +56,14 @@ ROW_OUT_FIELDS = ("kl_topk", "kl_full", "margin", "lse_base", "lse_cand", "top1_
 class RowOut(ctypes.Structure):
     """lcmp_row_out: device pointers, NULL to skip (target is an input)."""
     _fields_ = [(n, ctypes.c_void_p) for n in ROW_OUT_FIELDS]
+
+
+RECORD_FIELDS = ("topk_idx", "topk_val", "lse_rest", "status", "logp_target")
+
+
+class Record(ctypes.Structure):
+    """lcmp_record: device arrays of a compact baseline record (logp_target may be NULL)."""
+    _fields_ = [(n, ctypes.c_void_p) for n in RECORD_FIELDS]
 
 
 # record sizes of the C structs (int64 x4, uint32 x2, double x6) etc.
@@ -92,6 +105,18 @@ def _load():
     lib.lcmp_bin_report.argtypes = [vp, vp, vp, vp, vp, vp, ci, i64,
                                     ctypes.POINTER(ctypes.c_double), ci, ctypes.c_double,
                                     vp, vp, vp, sz, vp]
+    lib.lcmp_record_workspace_bytes.restype = sz
+    lib.lcmp_record_workspace_bytes.argtypes = [i64, i64, ci]
+    lib.lcmp_record_baseline.restype = ci
+    lib.lcmp_record_baseline.argtypes = [vp, ci, i64, i64, i64, ci, vp, ctypes.POINTER(Record),
+                                         vp, sz, vp]
+    lib.lcmp_compare_record_workspace_bytes.restype = sz
+    lib.lcmp_compare_record_workspace_bytes.argtypes = [i64, i64]
+    lib.lcmp_compare_record.restype = ci
+    lib.lcmp_compare_record.argtypes = [ctypes.POINTER(Record), ci, vp, ci, i64, i64, i64, ci,
+                                        ctypes.POINTER(RowOut), vp, sz, vp]
+    lib.lcmp_compare_record_timed.restype = ci
+    lib.lcmp_compare_record_timed.argtypes = lib.lcmp_compare_record.argtypes + [vp, vp]
     if lib.lcmp_abi_version() != ABI_VERSION:
         raise ImportError(f"{LIB_PATH} has ABI {lib.lcmp_abi_version()}, this binding expects "
                           f"{ABI_VERSION}; rebuild it")
@@ -176,9 +201,7 @@ def lcmp_compare_logits(base: torch.Tensor, cand: torch.Tensor, k: int = 20,
         raise ValueError("baseline and candidate need the same number of rows")
     v = base.size(1) if v is None else v
     flags = LCMP_WITH_BITDIFF if with_bitdiff else 0
-    if target is not None and (target.dtype != torch.int32 or target.numel() != n
-                               or not target.is_contiguous()):
-        raise ValueError("target must be a contiguous int32 tensor of one id per row")
+    _check_target(target, n)
     if out is None:
         out = alloc_compare_outputs(n, k, base.device, with_bitdiff, target is not None)
     ws_bytes = int(_lib.lcmp_compare_workspace_bytes(n, v, k, flags))
@@ -196,6 +219,81 @@ def lcmp_compare_logits(base: torch.Tensor, cand: torch.Tensor, k: int = 20,
     else:
         rc = _lib.lcmp_compare_logits_timed(*args, events[0], events[1])
     _check(rc, "lcmp_compare_logits")
+    return out
+
+
+def _check_target(target, n):
+    if target is not None and (target.dtype != torch.int32 or target.numel() != n
+                               or not target.is_contiguous()):
+        raise ValueError("target must be a contiguous int32 tensor of one id per row")
+
+
+def lcmp_record_baseline(base: torch.Tensor, k_rec: int = 20, target: torch.Tensor | None = None,
+                         v: int | None = None, workspace: torch.Tensor | None = None,
+                         stream=None) -> dict:
+    """Compact record of baseline rows (device [n, >=v]): a dict of device
+    tensors topk_idx [n, k_rec] int32, topk_val [n, k_rec] float32, lse_rest [n]
+    float64, status [n] uint8, and logp_target [n] float64 when `target` is given."""
+    n = base.size(0)
+    v = base.size(1) if v is None else v
+    _check_target(target, n)
+    dev = base.device
+    rec = dict(topk_idx=torch.empty((n, k_rec), dtype=torch.int32, device=dev),
+               topk_val=torch.empty((n, k_rec), dtype=torch.float32, device=dev),
+               lse_rest=torch.empty(n, dtype=torch.float64, device=dev),
+               status=torch.empty(n, dtype=torch.uint8, device=dev))
+    if target is not None:
+        rec["logp_target"] = torch.empty(n, dtype=torch.float64, device=dev)
+    ws_bytes = int(_lib.lcmp_record_workspace_bytes(n, v, k_rec))
+    if ws_bytes == 0:
+        raise LcmpError(-3, "lcmp_record_workspace_bytes")
+    if workspace is None or workspace.numel() < ws_bytes:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    r = Record(*[_ptr(rec.get(f)) for f in RECORD_FIELDS])
+    rc = _lib.lcmp_record_baseline(base.data_ptr(), _dtype_code(base), _ld(base), n, v, k_rec,
+                                   _ptr(target), ctypes.byref(r), workspace.data_ptr(),
+                                   workspace.numel(), _stream(stream))
+    _check(rc, "lcmp_record_baseline")
+    return rec
+
+
+def lcmp_compare_record(record: dict, cand: torch.Tensor, k: int | None = None,
+                        target: torch.Tensor | None = None, v: int | None = None,
+                        out: dict | None = None, workspace: torch.Tensor | None = None,
+                        stream=None, events: tuple | None = None) -> dict:
+    """Compare candidate rows (device [n, >=v]) against a record from
+    lcmp_record_baseline, using its first k entries (default all).  Returns the
+    outputs of lcmp_compare_logits except kl_full (and bitdiff); with `target`,
+    logp_cand, plus logp_base when the record holds logp_target."""
+    n = cand.size(0)
+    v = cand.size(1) if v is None else v
+    k_rec = record["topk_idx"].size(1)
+    k = k_rec if k is None else k
+    if record["topk_idx"].size(0) != n:
+        raise ValueError("the record and the candidate need the same number of rows")
+    _check_target(target, n)
+    if out is None:
+        out = alloc_compare_outputs(n, k, cand.device)
+        del out["kl_full"]
+        if target is not None:
+            out["logp_cand"] = torch.empty(n, dtype=torch.float64, device=cand.device)
+            if record.get("logp_target") is not None:
+                out["logp_base"] = torch.empty(n, dtype=torch.float64, device=cand.device)
+    ws_bytes = int(_lib.lcmp_compare_record_workspace_bytes(n, v))
+    if ws_bytes == 0:
+        raise LcmpError(-3, "lcmp_compare_record_workspace_bytes")
+    if workspace is None or workspace.numel() < ws_bytes:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=cand.device)
+    r = Record(*[_ptr(record.get(f)) for f in RECORD_FIELDS])
+    ptrs = dict(out, target=target)
+    ro = RowOut(*[_ptr(ptrs.get(f)) for f in ROW_OUT_FIELDS])
+    args = (ctypes.byref(r), k_rec, cand.data_ptr(), _dtype_code(cand), _ld(cand), n, v, k,
+            ctypes.byref(ro), workspace.data_ptr(), workspace.numel(), _stream(stream))
+    if events is None:
+        rc = _lib.lcmp_compare_record(*args)
+    else:
+        rc = _lib.lcmp_compare_record_timed(*args, events[0], events[1])
+    _check(rc, "lcmp_compare_record")
     return out
 
 

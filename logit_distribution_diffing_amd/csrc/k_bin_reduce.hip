@@ -55,7 +55,7 @@ __global__ __launch_bounds__(kWave) void k_bin_partial(BinArgs a) {
           } else {
             bin = g * a.n_edges + j;
             kt = a.kl_topk[r];
-            kf = a.kl_full[r];
+            kf = a.kl_full ? a.kl_full[r] : NAN;
             tie = (m == 0.0);
             atomicAdd(&cnt[bin][0], 1ull);
             if (fl) atomicAdd(&cnt[bin][1], 1ull);

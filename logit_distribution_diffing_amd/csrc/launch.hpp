@@ -103,6 +103,66 @@ struct PerturbArgs {
   bool vec;  // rows of both sides aligned for 4-element vector accesses
 };
 int64_t perturb_tiles(int64_t cols);
+
+// ---- compact baseline record
+// One per (row, chunk) of the one-side pass: s = sum of 2^((y - r) * log2e)
+// over the chunk's columns outside the head set, r the reference (-FLT_MAX
+// before any finite value), and the chunk's largest value over all columns
+// with its lowest column (-1 if none).
+struct RestChunk {
+  double s;
+  float r, bmax;
+  int32_t bidx, pad_;
+};
+struct RestArgs {
+  const void *x;
+  int64_t ldx;
+  int64_t n, v, chunk;  // chunk: a multiple of kRestChunkQuantum columns
+  int32_t nchunks;
+  const int32_t *head;  // [n, ldh]: the first kh entries are excluded (-1 = none)
+  int64_t ldh;
+  int32_t kh;
+  RestChunk *out;  // [n * nchunks]
+};
+constexpr int kRestChunkQuantum = 1024;
+
+// Build the record from the full-compare outputs of the baseline against itself
+// (head indices and status already in place) and the rest sums.
+struct RecordArgs {
+  const void *base;
+  int32_t tb;
+  int64_t ldb, n, v;
+  int32_t krec, nchunks;
+  const RestChunk *rest;
+  const int32_t *idx;    // [n, krec]
+  const uint8_t *status;
+  float *val;            // [n, krec]
+  double *lse_rest;
+  const int32_t *target;  // NULL: no target log-probability
+  double *logp;
+};
+
+// Compare a candidate against a record.
+struct RecordCmpArgs {
+  const int32_t *idx;
+  const float *val;
+  const double *lse_rest;
+  const uint8_t *rec_status;
+  const double *rec_logp;
+  int32_t krec, k, nchunks, tc;
+  const void *cand;
+  int64_t ldc, n, v;
+  const RestChunk *rest;
+  const int32_t *target;
+  double *kl_topk, *margin, *lse_base, *lse_cand;
+  int32_t *top1_base, *top2_base, *top1_cand;
+  uint8_t *flip, *status;
+  int32_t *topk_idx;
+  double *logp_base, *logp_cand;
+};
+hipError_t launch_rest_sum(const RestArgs &a, int tx, bool vec, hipStream_t stream);
+hipError_t launch_record_final(const RecordArgs &a, hipStream_t stream);
+hipError_t launch_record_cmp(const RecordCmpArgs &a, hipStream_t stream);
 hipError_t launch_perturb(const PerturbArgs &a, hipStream_t stream);
 
 hipError_t launch_row_stats(const StreamArgs &a, int ta, int tb, bool cmp, bool bits, bool vec,

@@ -100,6 +100,45 @@ bool vector_ok(const void *a, int ta, int64_t lda, const void *b, int tb, int64_
          ((size_t)ldb * esize(tb)) % 16 == 0;
 }
 
+// Chunks of the one-side pass of the record comparison: the same cost model
+// as choose_chunks, in units of kRestChunkQuantum columns (two fp32 steps or
+// one bf16 step of a wave), with at least four units per chunk.
+struct RestLayout {
+  Chunking ch;
+  size_t bytes;
+};
+
+RestLayout rest_layout(int64_t n, int64_t v) {
+  constexpr int64_t kResidentWaves = 256 * 16;
+  constexpr int64_t kChunkOverhead = 1;
+  const int64_t units = (v + kRestChunkQuantum - 1) / kRestChunkQuantum;
+  int64_t cmax = units / 4;
+  if (cmax > 16) cmax = 16;
+  if (cmax < 1) cmax = 1;
+  int64_t best_c = 1, best_cost = -1;
+  for (int64_t c = 1; c <= cmax; ++c) {
+    const int64_t rounds = n > 0 ? (n * c + kResidentWaves - 1) / kResidentWaves : 1;
+    const int64_t cost = rounds * ((units + c - 1) / c + kChunkOverhead);
+    if (best_cost < 0 || cost < best_cost) {
+      best_cost = cost;
+      best_c = c;
+    }
+  }
+  RestLayout L;
+  L.ch.chunk = (units + best_c - 1) / best_c * kRestChunkQuantum;
+  L.ch.nchunks = (int32_t)((v + L.ch.chunk - 1) / L.ch.chunk);
+  L.bytes = align_up((size_t)n * (size_t)L.ch.nchunks * sizeof(RestChunk));
+  return L;
+}
+
+bool rows_aligned(const void *p, int t, int64_t ld) {
+  return (uintptr_t)p % 16 == 0 && ((size_t)ld * esize(t)) % 16 == 0;
+}
+
+bool record_ok(const lcmp_record *rec) {
+  return rec->topk_idx && rec->topk_val && rec->lse_rest && rec->status;
+}
+
 constexpr int64_t kMaxCols = 0x7fffffffLL - 4096;  // indices are 32-bit in the kernels
 constexpr int64_t kMaxRows = (int64_t)1 << 40;
 
@@ -328,7 +367,7 @@ int lcmp_bin_report(const double *margin, const uint8_t *flip, const double *kl_
     if (j > 0 && !(edges[j] > edges[j - 1])) return LCMP_EEDGES;
   }
   if (isnan(big_margin)) return LCMP_EINVAL;
-  if (n > 0 && (!margin || !flip || !kl_topk || !kl_full)) return LCMP_EINVAL;
+  if (n > 0 && (!margin || !flip || !kl_topk)) return LCMP_EINVAL;
   const size_t need = lcmp_bin_workspace_bytes(n, n_groups, n_edges);
   if (!workspace || ws_bytes < need) return LCMP_EWORKSPACE;
   if ((uintptr_t)workspace % 16 != 0) return LCMP_EINVAL;
@@ -357,6 +396,167 @@ int lcmp_bin_report(const double *margin, const uint8_t *flip, const double *kl_
   ba.groups = (GroupAcc *)summary;
   if (launch_bin_reduce(ba, (hipStream_t)stream) != hipSuccess) return LCMP_EHIP;
   return LCMP_OK;
+}
+
+// ---------------------------------------------------------------- compact record
+
+size_t lcmp_record_workspace_bytes(int64_t n, int64_t v, int k_rec) {
+  if (n < 0 || v < 2 || v > kMaxCols || n > kMaxRows || k_rec < 2 || k_rec > LCMP_MAX_K) return 0;
+  if (n == 0) return kAlign;
+  return compare_layout(n, v, k_rec, 0).total + rest_layout(n, v).bytes;
+}
+
+size_t lcmp_compare_record_workspace_bytes(int64_t n, int64_t v) {
+  if (n < 0 || v < 2 || v > kMaxCols || n > kMaxRows) return 0;
+  if (n == 0) return kAlign;
+  return rest_layout(n, v).bytes;
+}
+
+}  // extern "C"
+
+static int record_impl(const void *base, int tb, int64_t ld_base, int64_t n, int64_t v, int k_rec,
+                       const int32_t *target, const lcmp_record *rec, void *workspace,
+                       size_t ws_bytes, void *stream) {
+  if (!dtype_ok(tb)) return LCMP_EDTYPE;
+  if (n < 0 || !rec) return LCMP_EINVAL;
+  if (v < 2 || v > kMaxCols || n > kMaxRows || k_rec < 2 || k_rec > LCMP_MAX_K || ld_base < v)
+    return LCMP_ESHAPE;
+  if (rec->logp_target && !target) return LCMP_EINVAL;
+  if (n == 0) return LCMP_OK;
+  if (!base || !record_ok(rec)) return LCMP_EINVAL;
+  const CompareLayout CL = compare_layout(n, v, k_rec, 0);
+  const RestLayout RL = rest_layout(n, v);
+  if (!workspace || ws_bytes < CL.total + RL.bytes) return LCMP_EWORKSPACE;
+  if ((uintptr_t)workspace % 16 != 0) return LCMP_EINVAL;
+  hipStream_t s = (hipStream_t)stream;
+  // 1. the baseline's top-k_rec and status: the full compare of the baseline
+  //    with itself, writing only those two outputs
+  lcmp_row_out ro;
+  memset(&ro, 0, sizeof ro);
+  ro.topk_idx = rec->topk_idx;
+  ro.status = rec->status;
+  const int rc = compare_impl(base, tb, ld_base, base, tb, ld_base, n, v, k_rec, 0, &ro, nullptr,
+                              workspace, CL.total, stream, nullptr, nullptr);
+  if (rc != LCMP_OK) return rc;
+  // 2. the mass outside the top-k_rec
+  RestArgs ra;
+  ra.x = base;
+  ra.ldx = ld_base;
+  ra.n = n;
+  ra.v = v;
+  ra.chunk = RL.ch.chunk;
+  ra.nchunks = RL.ch.nchunks;
+  ra.head = rec->topk_idx;
+  ra.ldh = k_rec;
+  ra.kh = k_rec;
+  ra.out = (RestChunk *)((char *)workspace + CL.total);
+  if (launch_rest_sum(ra, tb, rows_aligned(base, tb, ld_base), s) != hipSuccess) return LCMP_EHIP;
+  // 3. values, rest mass and target log-probability
+  RecordArgs fa;
+  fa.base = base;
+  fa.tb = tb;
+  fa.ldb = ld_base;
+  fa.n = n;
+  fa.v = v;
+  fa.krec = k_rec;
+  fa.nchunks = RL.ch.nchunks;
+  fa.rest = ra.out;
+  fa.idx = rec->topk_idx;
+  fa.status = rec->status;
+  fa.val = rec->topk_val;
+  fa.lse_rest = rec->lse_rest;
+  fa.target = rec->logp_target ? target : nullptr;
+  fa.logp = rec->logp_target;
+  if (launch_record_final(fa, s) != hipSuccess) return LCMP_EHIP;
+  return LCMP_OK;
+}
+
+static int compare_record_impl(const lcmp_record *rec, int k_rec, const void *cand, int tc,
+                               int64_t ld_cand, int64_t n, int64_t v, int k,
+                               const lcmp_row_out *out, void *workspace, size_t ws_bytes,
+                               void *stream, void *ev_before, void *ev_after) {
+  if (!dtype_ok(tc)) return LCMP_EDTYPE;
+  if (n < 0 || !rec || !out) return LCMP_EINVAL;
+  if (v < 2 || v > kMaxCols || n > kMaxRows || k_rec < 2 || k_rec > LCMP_MAX_K || k < 1 ||
+      k > k_rec || ld_cand < v)
+    return LCMP_ESHAPE;
+  if (out->kl_full) return LCMP_EINVAL;  // needs the whole baseline row
+  if ((out->logp_base || out->logp_cand) && !out->target) return LCMP_EINVAL;
+  if (out->logp_base && !rec->logp_target) return LCMP_EINVAL;
+  if (n == 0) return LCMP_OK;
+  if (!cand || !record_ok(rec)) return LCMP_EINVAL;
+  const RestLayout RL = rest_layout(n, v);
+  if (!workspace || ws_bytes < RL.bytes) return LCMP_EWORKSPACE;
+  if ((uintptr_t)workspace % 16 != 0) return LCMP_EINVAL;
+  hipStream_t s = (hipStream_t)stream;
+  RestArgs ra;
+  ra.x = cand;
+  ra.ldx = ld_cand;
+  ra.n = n;
+  ra.v = v;
+  ra.chunk = RL.ch.chunk;
+  ra.nchunks = RL.ch.nchunks;
+  ra.head = rec->topk_idx;
+  ra.ldh = k_rec;
+  ra.kh = k;
+  ra.out = (RestChunk *)workspace;
+  if (ev_before && hipEventRecord((hipEvent_t)ev_before, s) != hipSuccess) return LCMP_EHIP;
+  if (launch_rest_sum(ra, tc, rows_aligned(cand, tc, ld_cand), s) != hipSuccess) return LCMP_EHIP;
+  if (ev_after && hipEventRecord((hipEvent_t)ev_after, s) != hipSuccess) return LCMP_EHIP;
+  RecordCmpArgs ca;
+  ca.idx = rec->topk_idx;
+  ca.val = rec->topk_val;
+  ca.lse_rest = rec->lse_rest;
+  ca.rec_status = rec->status;
+  ca.rec_logp = rec->logp_target;
+  ca.krec = k_rec;
+  ca.k = k;
+  ca.nchunks = RL.ch.nchunks;
+  ca.tc = tc;
+  ca.cand = cand;
+  ca.ldc = ld_cand;
+  ca.n = n;
+  ca.v = v;
+  ca.rest = ra.out;
+  const bool with_target = out->target && (out->logp_base || out->logp_cand);
+  ca.target = with_target ? out->target : nullptr;
+  ca.kl_topk = out->kl_topk;
+  ca.margin = out->margin;
+  ca.lse_base = out->lse_base;
+  ca.lse_cand = out->lse_cand;
+  ca.top1_base = out->top1_base;
+  ca.top2_base = out->top2_base;
+  ca.top1_cand = out->top1_cand;
+  ca.flip = out->flip;
+  ca.status = out->status;
+  ca.topk_idx = out->topk_idx;
+  ca.logp_base = with_target ? out->logp_base : nullptr;
+  ca.logp_cand = with_target ? out->logp_cand : nullptr;
+  if (launch_record_cmp(ca, s) != hipSuccess) return LCMP_EHIP;
+  return LCMP_OK;
+}
+
+extern "C" {
+
+int lcmp_record_baseline(const void *base, int tb, int64_t ld_base, int64_t n, int64_t v,
+                         int k_rec, const int32_t *target, const lcmp_record *rec,
+                         void *workspace, size_t ws_bytes, void *stream) {
+  return record_impl(base, tb, ld_base, n, v, k_rec, target, rec, workspace, ws_bytes, stream);
+}
+
+int lcmp_compare_record(const lcmp_record *rec, int k_rec, const void *cand, int tc,
+                        int64_t ld_cand, int64_t n, int64_t v, int k, const lcmp_row_out *out,
+                        void *workspace, size_t ws_bytes, void *stream) {
+  return compare_record_impl(rec, k_rec, cand, tc, ld_cand, n, v, k, out, workspace, ws_bytes,
+                             stream, nullptr, nullptr);
+}
+
+int lcmp_compare_record_timed(const lcmp_record *rec, int k_rec, const void *cand, int tc,
+                              int64_t ld_cand, int64_t n, int64_t v, int k,
+                              const lcmp_row_out *out, void *workspace, size_t ws_bytes,
+                              void *stream, void *ev_before, void *ev_after) {
+  return compare_record_impl(rec, k_rec, cand, tc, ld_cand, n, v, k, out, workspace, ws_bytes,
+                             stream, ev_before, ev_after);
 }
 
 }  // extern "C"

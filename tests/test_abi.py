@@ -35,7 +35,7 @@ def test_every_declared_symbol_is_exported(L):
 
 def test_version_and_strerror(L):
     lib = L.lib()
-    assert lib.lcmp_abi_version() == 2
+    assert lib.lcmp_abi_version() == 3
     for st in (0, -1, -2, -3, -4, -5, -6):
         assert len(lib.lcmp_strerror(st)) > 0
     assert lib.lcmp_strerror(-99) == b"unknown status"
@@ -170,3 +170,80 @@ def test_perturb_argument_errors(L):
     assert call(rows=-1) == -1
     assert call(rows=0) == 0
 
+
+
+def _record(L, **kw):
+    r = L.Record(topk_idx=FAKE, topk_val=FAKE, lse_rest=FAKE, status=FAKE, logp_target=None)
+    for key, val in kw.items():
+        setattr(r, key, val)
+    return r
+
+
+def test_record_workspace_queries(L):
+    lib = L.lib()
+    assert lib.lcmp_record_workspace_bytes(1000, 151936, 20) > lib.lcmp_compare_record_workspace_bytes(1000, 151936)
+    assert lib.lcmp_record_workspace_bytes(10, 100, 1) == 0       # k_rec < 2
+    assert lib.lcmp_record_workspace_bytes(10, 100, 65) == 0
+    assert lib.lcmp_record_workspace_bytes(10, 1, 20) == 0
+    assert lib.lcmp_compare_record_workspace_bytes(10, 1) == 0
+    assert lib.lcmp_compare_record_workspace_bytes(-1, 100) == 0
+    assert lib.lcmp_compare_record_workspace_bytes(0, 100) > 0
+
+
+def test_record_baseline_argument_errors(L):
+    lib = L.lib()
+
+    def call(rec=None, **kw):
+        a = dict(base=FAKE, tb=0, ld=100, n=4, v=100, k_rec=20, target=None, ws=FAKE,
+                 ws_bytes=1 << 30)
+        a.update(kw)
+        r = _record(L) if rec is None else rec
+        return lib.lcmp_record_baseline(a["base"], a["tb"], a["ld"], a["n"], a["v"], a["k_rec"],
+                                        a["target"], ctypes.byref(r), a["ws"], a["ws_bytes"], None)
+
+    assert call(tb=2) == -2
+    assert call(n=-1) == -1
+    assert call(k_rec=1) == -3
+    assert call(k_rec=65) == -3
+    assert call(ld=99) == -3
+    assert call(v=1) == -3
+    assert call(rec=_record(L, logp_target=FAKE)) == -1     # target log-probability needs targets
+    assert call(base=None) == -1
+    assert call(rec=_record(L, lse_rest=None)) == -1
+    assert call(ws=None) == -4
+    assert call(ws_bytes=8) == -4
+    assert call(n=0) == 0
+
+
+def test_compare_record_argument_errors(L):
+    lib = L.lib()
+
+    def call(rec=None, out=None, **kw):
+        a = dict(k_rec=20, cand=FAKE, tc=0, ld=100, n=4, v=100, k=20, ws=FAKE, ws_bytes=1 << 30)
+        a.update(kw)
+        r = _record(L) if rec is None else rec
+        o = L.RowOut() if out is None else out
+        return lib.lcmp_compare_record(ctypes.byref(r), a["k_rec"], a["cand"], a["tc"], a["ld"],
+                                       a["n"], a["v"], a["k"], ctypes.byref(o), a["ws"],
+                                       a["ws_bytes"], None)
+
+    assert call(tc=5) == -2
+    assert call(n=-1) == -1
+    assert call(k=21) == -3                       # more entries than the record holds
+    assert call(k=0) == -3
+    assert call(k_rec=1, k=1) == -3
+    assert call(ld=50) == -3
+    ro = L.RowOut()
+    ro.kl_full = FAKE
+    assert call(out=ro) == -1                     # the full KL needs the baseline rows
+    ro = L.RowOut()
+    ro.logp_cand = FAKE
+    assert call(out=ro) == -1                     # needs targets
+    ro.target = FAKE
+    ro.logp_base = FAKE
+    assert call(out=ro) == -1                     # the record holds no target log-probability
+    assert call(cand=None) == -1
+    assert call(ws=None) == -4
+    assert call(ws_bytes=8) == -4
+    assert call(ws=FAKE + 8) == -1
+    assert call(n=0) == 0

@@ -302,3 +302,29 @@ def test_bin_report_parity(n, n_groups, edges):
         assert np.all(np.abs(gb[f][~inf] - ob[f][~inf]) <= BIN_SUM_REL * ob[f][~inf]), f
     assert bins.cpu().numpy().tobytes() == bins2.cpu().numpy().tobytes()
     assert summ.cpu().numpy().tobytes() == summ2.cpu().numpy().tobytes()
+
+
+def test_bin_report_without_full_kl():
+    """kl_full = NULL (a comparison against a record): counts and top-k sums as
+    with it, sum_kl_full NaN exactly in the bins that hold rows."""
+    import torch
+    import logit_distribution_diffing_amd as L
+    n, n_groups, edges = 100000, 3, synth.DEFAULT_EDGES
+    _case(f"bins without full KL n={n}")
+    m, flip, kt, kf, status, group = _bin_inputs(n, n_groups, edges, seed=77)
+    dev = {name: torch.from_numpy(x).cuda() for name, x in
+           (("m", m), ("flip", flip), ("kt", kt), ("st", status), ("gr", group))}
+    bins, summ = L.lcmp_bin_report(dev["m"], dev["flip"], dev["kt"], None, edges,
+                                   status=dev["st"], group=dev["gr"], n_groups=n_groups)
+    torch.cuda.synchronize()
+    gb, gs = L.unpack_bins(bins, summ, n_groups)
+    ob, os_ = oracle.bin_report(m, flip, kt, None, edges, status=status, group=group,
+                                n_groups=n_groups)
+    for f in ("count", "flips", "ties", "tie_flips", "max_kl_topk"):
+        assert np.array_equal(gb[f], ob[f]), f
+    assert gs.tobytes() == os_.tobytes()
+    inf = np.isinf(ob["sum_kl_topk"])
+    assert np.all(np.abs(gb["sum_kl_topk"][~inf] - ob["sum_kl_topk"][~inf])
+                  <= BIN_SUM_REL * ob["sum_kl_topk"][~inf])
+    held = ob["count"] > 0
+    assert np.all(np.isnan(gb["sum_kl_full"][held])) and np.all(gb["sum_kl_full"][~held] == 0.0)
