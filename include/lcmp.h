@@ -49,6 +49,7 @@ extern "C" {
 #define LCMP_MAX_EDGES 32   /* largest number of margin-bin edges */
 #define LCMP_MAX_GROUPS 256 /* largest number of row groups in lcmp_bin_report */
 #define LCMP_MAX_BINS 256   /* largest n_groups * n_edges */
+#define LCMP_MAX_ROWS 2147483647LL /* largest n (rows) of the compare, bitwise and record calls */
 
 typedef enum { LCMP_F32 = 0, LCMP_BF16 = 1 } lcmp_dtype;
 
@@ -56,7 +57,7 @@ typedef enum {
   LCMP_OK = 0,
   LCMP_EINVAL = -1,     /* NULL required pointer, negative count, bad flag, misaligned workspace */
   LCMP_EDTYPE = -2,     /* unknown element type */
-  LCMP_ESHAPE = -3,     /* v < 2, k out of [1, LCMP_MAX_K], ld < columns, sizes or bin counts too large */
+  LCMP_ESHAPE = -3,     /* v < 2, k out of [1, LCMP_MAX_K], ld < columns, n > LCMP_MAX_ROWS, bin counts too large */
   LCMP_EWORKSPACE = -4, /* workspace NULL or smaller than the matching *_workspace_bytes() */
   LCMP_EHIP = -5,       /* a HIP launch or runtime call failed */
   LCMP_EEDGES = -6      /* edges not strictly ascending, not positive, NaN, or too many */

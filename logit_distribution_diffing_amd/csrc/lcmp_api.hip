@@ -140,7 +140,9 @@ bool record_ok(const lcmp_record *rec) {
 }
 
 constexpr int64_t kMaxCols = 0x7fffffffLL - 4096;  // indices are 32-bit in the kernels
-constexpr int64_t kMaxRows = (int64_t)1 << 40;
+// the per-row kernels launch one block per row, and a grid dimension holds
+// at most 2^31 - 1 blocks
+constexpr int64_t kMaxRows = LCMP_MAX_ROWS;
 
 }  // namespace
 

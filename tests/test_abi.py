@@ -51,6 +51,10 @@ def test_workspace_queries(L):
     assert lib.lcmp_compare_workspace_bytes(10, 100, 0, 0) == 0     # k < 1
     assert lib.lcmp_compare_workspace_bytes(10, 100, 65, 0) == 0    # k > 64
     assert lib.lcmp_compare_workspace_bytes(-1, 100, 20, 0) == 0
+    assert lib.lcmp_compare_workspace_bytes(1 << 31, 100, 20, 0) == 0   # one block per row
+    assert lib.lcmp_compare_workspace_bytes((1 << 31) - 1, 100, 20, 0) > 0
+    assert lib.lcmp_bitdiff_workspace_bytes(1 << 31, 10) == 0
+    assert lib.lcmp_compare_record_workspace_bytes(1 << 31, 100) == 0
     assert lib.lcmp_bitdiff_workspace_bytes(4096, 5120) > 0
     assert lib.lcmp_bitdiff_workspace_bytes(4, 0) == 0
     assert lib.lcmp_bin_workspace_bytes(65536, 1, 6) > 0
@@ -90,6 +94,7 @@ def test_compare_argument_errors(L):
     assert _compare(L, ws_bytes=16) == -4
     assert _compare(L, ws=FAKE + 4) == -1                # misaligned workspace
     assert _compare(L, n=0) == 0                         # empty batch: nothing to do
+    assert _compare(L, n=1 << 31) == -3                  # more rows than LCMP_MAX_ROWS
     ro = L.RowOut()
     ro.logp_cand = FAKE
     assert _compare(L, out=ro) == -1                     # target log-probabilities need targets
