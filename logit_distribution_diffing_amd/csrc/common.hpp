@@ -84,52 +84,82 @@ __device__ __forceinline__ float uniform(float x) {
   return __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(x)));
 }
 
-// Butterfly reductions: lane l combines with lane l^m, so every lane ends with
-// the same bit pattern (the combine is commutative) and the order is fixed.
+// Wave reductions without LDS traffic.  Inside each 16-lane row, four DPP
+// exchanges pair lane l with l^1, l^2, then the mirror lane in its 8-lane half
+// and in its row; every lane of a row then holds the row's total (the combine
+// is commutative, so partners compute the same bits).  The four row totals
+// are read out of lanes 0, 16, 32, 48 and combined in one fixed order, the same
+// on every lane.  All 64 lanes must be active.
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp32(uint32_t x) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, CTRL, 0xf, 0xf, false);
+}
+constexpr int kDppXor1 = 0xB1;        // quad_perm [1, 0, 3, 2]
+constexpr int kDppXor2 = 0x4E;        // quad_perm [2, 3, 0, 1]
+constexpr int kDppHalfMirror = 0x141; // lane i <-> 7 - i in each 8 lanes
+constexpr int kDppMirror = 0x140;     // lane i <-> 15 - i in each row
+
+template <typename T>
+struct Bits32 {
+  static_assert(sizeof(T) == 4 || sizeof(T) == 8, "32- or 64-bit values");
+  template <int CTRL>
+  static __device__ __forceinline__ T dpp(T x) {
+    if constexpr (sizeof(T) == 4) {
+      return __builtin_bit_cast(T, dpp32<CTRL>(__builtin_bit_cast(uint32_t, x)));
+    } else {
+      const uint64_t u = __builtin_bit_cast(uint64_t, x);
+      const uint64_t lo = dpp32<CTRL>((uint32_t)u), hi = dpp32<CTRL>((uint32_t)(u >> 32));
+      return __builtin_bit_cast(T, lo | (hi << 32));
+    }
+  }
+  static __device__ __forceinline__ T lane(T x, int l) {
+    if constexpr (sizeof(T) == 4) {
+      return __builtin_bit_cast(T, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), l));
+    } else {
+      const uint64_t u = __builtin_bit_cast(uint64_t, x);
+      const uint64_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)u, l);
+      const uint64_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(u >> 32), l);
+      return __builtin_bit_cast(T, lo | (hi << 32));
+    }
+  }
+};
+
+template <typename T, typename Op>
+__device__ __forceinline__ T wave_reduce(T x, Op op) {
+  using B = Bits32<T>;
+  x = op(x, B::template dpp<kDppXor1>(x));
+  x = op(x, B::template dpp<kDppXor2>(x));
+  x = op(x, B::template dpp<kDppHalfMirror>(x));
+  x = op(x, B::template dpp<kDppMirror>(x));
+  return op(op(B::lane(x, 0), B::lane(x, 16)), op(B::lane(x, 32), B::lane(x, 48)));
+}
+
 __device__ __forceinline__ double wave_sum(double x) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) x += __shfl_xor(x, m, kWave);
-  return x;
+  return wave_reduce(x, [](double a, double b) { return a + b; });
 }
 __device__ __forceinline__ int64_t wave_sum(int64_t x) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) x += __shfl_xor(x, m, kWave);
-  return x;
+  return wave_reduce(x, [](int64_t a, int64_t b) { return a + b; });
 }
 __device__ __forceinline__ int wave_sum(int x) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) x += __shfl_xor(x, m, kWave);
-  return x;
+  return wave_reduce(x, [](int a, int b) { return a + b; });
 }
 __device__ __forceinline__ double wave_max(double x) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) x = fmax(x, __shfl_xor(x, m, kWave));
-  return x;
+  return wave_reduce(x, [](double a, double b) { return fmax(a, b); });
 }
 __device__ __forceinline__ float wave_max(float x) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) x = fmaxf(x, __shfl_xor(x, m, kWave));
-  return x;
+  return wave_reduce(x, [](float a, float b) { return fmaxf(a, b); });
 }
 __device__ __forceinline__ uint32_t wave_max(uint32_t x) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) x = max(x, (uint32_t)__shfl_xor((int)x, m, kWave));
-  return x;
+  return wave_reduce(x, [](uint32_t a, uint32_t b) { return a > b ? a : b; });
 }
 __device__ __forceinline__ int wave_min(int x) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) x = min(x, __shfl_xor(x, m, kWave));
-  return x;
+  return wave_reduce(x, [](int a, int b) { return a < b ? a : b; });
 }
 __device__ __forceinline__ int64_t wave_min(int64_t x) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) x = min(x, (int64_t)__shfl_xor(x, m, kWave));
-  return x;
+  return wave_reduce(x, [](int64_t a, int64_t b) { return a < b ? a : b; });
 }
 __device__ __forceinline__ int wave_max(int x) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) x = max(x, __shfl_xor(x, m, kWave));
-  return x;
+  return wave_reduce(x, [](int a, int b) { return a > b ? a : b; });
 }
 
 // --------------------------------------------------------------------- values

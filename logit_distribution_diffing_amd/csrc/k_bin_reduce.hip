@@ -5,11 +5,11 @@
 // Two levels with a fixed order, so repeated calls are bit-identical:
 //   level 1: one wave per block of 64..2048 rows (more with more bins);
 //            each 64-row batch is split by bin, every bin's values are
-//            summed with a fixed butterfly and added to the block's LDS
+//            summed with a fixed-order wave reduction and added to the block's LDS
 //            accumulator in batch order; integer counts go through LDS
 //            atomics (exact, order-free).
 //   level 2: one wave per bin (and per group) adds the block partials in a
-//            fixed lane-then-butterfly order.
+//            fixed lane-then-wave-reduction order.
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -69,14 +69,12 @@ __global__ __launch_bounds__(kWave) void k_bin_partial(BinArgs a) {
     uint64_t pending = ballot(bin >= 0);
     while (pending) {
       const int leader = __builtin_ctzll(pending);
-      const int b = __shfl(bin, leader, kWave);
+      const int b = __builtin_amdgcn_readlane(bin, leader);
       const bool mine = (bin == b);
       pending &= ~ballot(mine);
       const double skt = wave_sum(mine ? kt : 0.0);
       const double skf = wave_sum(mine ? kf : 0.0);
-      double mx = mine ? kt : -INFINITY;
-#pragma unroll
-      for (int s = 32; s >= 1; s >>= 1) mx = fmax(mx, __shfl_xor(mx, s, kWave));
+      const double mx = wave_max(mine ? kt : -INFINITY);
       if (lane == 0) {
         acc_kt[b] += skt;
         acc_kf[b] += skf;
@@ -108,7 +106,7 @@ __global__ __launch_bounds__(kWave) void k_bin_partial(BinArgs a) {
 }
 
 // One wave per bin (then per group): lane l adds partials l, l+64, ... in order,
-// then the butterfly combines the lanes.
+// then the fixed-order wave reduction combines the lanes.
 __global__ __launch_bounds__(kWave) void k_bin_final(BinArgs a) {
   const int lane = lane_id();
   const int nbins = a.n_groups * a.n_edges;

@@ -6,8 +6,8 @@
 namespace lcmp {
 
 // Combine the chunk records of one row into the public record.  The whole wave
-// calls it; lane c reads chunk c (nchunks <= 64).  Sums use the fixed butterfly
-// order, so the result is the same on every run.
+// calls it; lane c reads chunk c (nchunks <= 64).  Sums use the fixed-order
+// wave reduction, so the result is the same on every run.
 __device__ __forceinline__ void merge_bits(const ChunkBits *cb, int nchunks, int64_t cols,
                                            BitdiffRow *out) {
   const int lane = lane_id();
