@@ -22,7 +22,9 @@
  *     which are host memory read during the call.
  *   - The caller owns every buffer.  The library allocates and frees nothing,
  *     keeps no mutable global state, is reentrant, and calls on different
- *     streams may run concurrently if their workspaces differ.
+ *     streams may run concurrently if their workspaces differ.  A call enqueues
+ *     kernels only (no memset, no copy), so it can be captured in a HIP graph
+ *     and replayed on new contents of the same buffers.
  *   - Work is enqueued on `stream` (a hipStream_t; NULL = the default
  *     stream) and is asynchronous: results are valid once the caller has
  *     synchronised with that stream.
