@@ -160,6 +160,55 @@ def _check(rc: int, where: str):
         raise LcmpError(rc, where)
 
 
+# ----------------------------------------------------------------------------- checks
+# The C side checks sizes and strides it is given; these checks make sure the
+# tensors behind the pointers are as large as those sizes say, of the right
+# element type and on the GPU, before any pointer reaches a kernel.
+
+# output field -> (dtype, elements per row; "k" = k per row)
+_OUT_SPEC = {
+    "kl_topk": (torch.float64, 1), "kl_full": (torch.float64, 1), "margin": (torch.float64, 1),
+    "lse_base": (torch.float64, 1), "lse_cand": (torch.float64, 1),
+    "logp_base": (torch.float64, 1), "logp_cand": (torch.float64, 1),
+    "top1_base": (torch.int32, 1), "top2_base": (torch.int32, 1), "top1_cand": (torch.int32, 1),
+    "flip": (torch.uint8, 1), "status": (torch.uint8, 1), "topk_idx": (torch.int32, "k"),
+    "bitdiff": (torch.uint8, BITDIFF_ROW_BYTES),
+}
+
+
+def _on_gpu(*named):
+    """(name, tensor) pairs; None tensors are skipped.  Run after the shape and
+    type checks, so those are reported first."""
+    for what, t in named:
+        if t is not None and t.device.type != "cuda":
+            raise ValueError(f"{what} must be a GPU tensor")
+
+
+def _check_buffer(t, dtype, numel: int, what: str):
+    if t.dtype != dtype or not t.is_contiguous() or t.numel() < numel:
+        raise ValueError(f"{what} must be a contiguous {dtype} tensor of at least {numel} "
+                         f"elements (got {t.dtype}, {t.numel()}, contiguous={t.is_contiguous()})")
+
+
+def _check_rows(t, n: int, v: int, what: str):
+    if t.dim() != 2 or t.size(0) != n or t.size(1) < v:
+        raise ValueError(f"{what} must be [n={n}, >= v={v}] (got {tuple(t.shape)})")
+    _dtype_code(t)
+
+
+def _check_out(out: dict, n: int, k: int, allowed=None):
+    for key, t in out.items():
+        if key not in _OUT_SPEC or (allowed is not None and key not in allowed):
+            raise ValueError(f"unexpected output field {key!r}")
+        dtype, per = _OUT_SPEC[key]
+        _check_buffer(t, dtype, n * (k if per == "k" else per), f"out[{key!r}]")
+
+
+def _check_workspace(ws):
+    if ws is not None:
+        _check_buffer(ws, torch.uint8, 0, "workspace")
+
+
 def compare_workspace_bytes(n: int, v: int, k: int = 20, with_bitdiff: bool = False) -> int:
     return int(_lib.lcmp_compare_workspace_bytes(n, v, k, LCMP_WITH_BITDIFF if with_bitdiff else 0))
 
@@ -197,13 +246,19 @@ def lcmp_compare_logits(base: torch.Tensor, cand: torch.Tensor, k: int = 20,
     and logp_cand.  `events`, a pair of raw hipEvent_t handles, selects
     lcmp_compare_logits_timed."""
     n = base.size(0)
-    if cand.size(0) != n:
-        raise ValueError("baseline and candidate need the same number of rows")
     v = base.size(1) if v is None else v
+    _check_rows(base, n, v, "base")
+    _check_rows(cand, n, v, "cand")
     flags = LCMP_WITH_BITDIFF if with_bitdiff else 0
     _check_target(target, n)
+    _check_workspace(workspace)
     if out is None:
         out = alloc_compare_outputs(n, k, base.device, with_bitdiff, target is not None)
+    _check_out(out, n, k)
+    if with_bitdiff and "bitdiff" not in out:
+        raise ValueError("with_bitdiff needs out['bitdiff']")
+    _on_gpu(("base", base), ("cand", cand), ("target", target), ("workspace", workspace),
+            *[(f"out[{key!r}]", t) for key, t in out.items()])
     ws_bytes = int(_lib.lcmp_compare_workspace_bytes(n, v, k, flags))
     if ws_bytes == 0:
         raise LcmpError(-3, "lcmp_compare_workspace_bytes")
@@ -223,9 +278,26 @@ def lcmp_compare_logits(base: torch.Tensor, cand: torch.Tensor, k: int = 20,
 
 
 def _check_target(target, n):
-    if target is not None and (target.dtype != torch.int32 or target.numel() != n
-                               or not target.is_contiguous()):
-        raise ValueError("target must be a contiguous int32 tensor of one id per row")
+    if target is not None:
+        if target.dtype != torch.int32 or target.numel() != n or not target.is_contiguous():
+            raise ValueError("target must be a contiguous int32 tensor of one id per row")
+
+
+_RECORD_SPEC = {"topk_idx": torch.int32, "topk_val": torch.float32, "lse_rest": torch.float64,
+                "status": torch.uint8, "logp_target": torch.float64}
+
+
+def _check_record(record: dict, n: int, k_rec: int):
+    for key in ("topk_idx", "topk_val", "lse_rest", "status"):
+        if key not in record:
+            raise ValueError(f"record lacks {key!r}")
+    for key, t in record.items():
+        if key not in _RECORD_SPEC:
+            raise ValueError(f"unexpected record field {key!r}")
+        if t is None:
+            continue
+        per = k_rec if key in ("topk_idx", "topk_val") else 1
+        _check_buffer(t, _RECORD_SPEC[key], n * per, f"record[{key!r}]")
 
 
 def lcmp_record_baseline(base: torch.Tensor, k_rec: int = 20, target: torch.Tensor | None = None,
@@ -236,7 +308,10 @@ def lcmp_record_baseline(base: torch.Tensor, k_rec: int = 20, target: torch.Tens
     float64, status [n] uint8, and logp_target [n] float64 when `target` is given."""
     n = base.size(0)
     v = base.size(1) if v is None else v
+    _check_rows(base, n, v, "base")
     _check_target(target, n)
+    _check_workspace(workspace)
+    _on_gpu(("base", base), ("target", target), ("workspace", workspace))
     dev = base.device
     rec = dict(topk_idx=torch.empty((n, k_rec), dtype=torch.int32, device=dev),
                topk_val=torch.empty((n, k_rec), dtype=torch.float32, device=dev),
@@ -267,11 +342,14 @@ def lcmp_compare_record(record: dict, cand: torch.Tensor, k: int | None = None,
     logp_cand, plus logp_base when the record holds logp_target."""
     n = cand.size(0)
     v = cand.size(1) if v is None else v
+    _check_rows(cand, n, v, "cand")
+    if record["topk_idx"].dim() != 2 or record["topk_idx"].size(0) != n:
+        raise ValueError("the record and the candidate need the same number of rows")
     k_rec = record["topk_idx"].size(1)
     k = k_rec if k is None else k
-    if record["topk_idx"].size(0) != n:
-        raise ValueError("the record and the candidate need the same number of rows")
+    _check_record(record, n, k_rec)
     _check_target(target, n)
+    _check_workspace(workspace)
     if out is None:
         out = alloc_compare_outputs(n, k, cand.device)
         del out["kl_full"]
@@ -279,6 +357,10 @@ def lcmp_compare_record(record: dict, cand: torch.Tensor, k: int | None = None,
             out["logp_cand"] = torch.empty(n, dtype=torch.float64, device=cand.device)
             if record.get("logp_target") is not None:
                 out["logp_base"] = torch.empty(n, dtype=torch.float64, device=cand.device)
+    _check_out(out, n, k, allowed=set(_OUT_SPEC) - {"kl_full", "bitdiff"})
+    _on_gpu(("cand", cand), ("target", target), ("workspace", workspace),
+            *[(f"record[{key!r}]", t) for key, t in record.items()],
+            *[(f"out[{key!r}]", t) for key, t in out.items()])
     ws_bytes = int(_lib.lcmp_compare_record_workspace_bytes(n, v))
     if ws_bytes == 0:
         raise LcmpError(-3, "lcmp_compare_record_workspace_bytes")
@@ -303,8 +385,13 @@ def lcmp_bitdiff(a: torch.Tensor, b: torch.Tensor, cols: int | None = None,
     """Per-row bitwise / ULP statistics; returns a raw [rows, 88] uint8 record tensor."""
     rows = a.size(0)
     cols = a.size(1) if cols is None else cols
+    _check_rows(a, rows, cols, "a")
+    _check_rows(b, rows, cols, "b")
+    _check_workspace(workspace)
     if out is None:
         out = torch.empty((rows, BITDIFF_ROW_BYTES), dtype=torch.uint8, device=a.device)
+    _check_buffer(out, torch.uint8, rows * BITDIFF_ROW_BYTES, "out")
+    _on_gpu(("a", a), ("b", b), ("out", out), ("workspace", workspace))
     ws_bytes = int(_lib.lcmp_bitdiff_workspace_bytes(rows, cols))
     if ws_bytes == 0:
         raise LcmpError(-3, "lcmp_bitdiff_workspace_bytes")
@@ -326,10 +413,21 @@ def lcmp_bin_report(margin, flip, kl_topk, kl_full, edges, status=None, group=No
     edges = [float(e) for e in edges]
     ne = len(edges)
     dev = margin.device
+    for what, t, dtype in (("margin", margin, torch.float64), ("flip", flip, torch.uint8),
+                           ("kl_topk", kl_topk, torch.float64), ("kl_full", kl_full, torch.float64),
+                           ("status", status, torch.uint8), ("group", group, torch.int32)):
+        if t is not None:
+            _check_buffer(t, dtype, n, what)
+    _check_workspace(workspace)
     if bins is None:
         bins = torch.empty((n_groups * ne, BIN_BYTES), dtype=torch.uint8, device=dev)
     if summary is None:
         summary = torch.empty((n_groups, GROUP_SUMMARY_BYTES), dtype=torch.uint8, device=dev)
+    _check_buffer(bins, torch.uint8, n_groups * ne * BIN_BYTES, "bins")
+    _check_buffer(summary, torch.uint8, n_groups * GROUP_SUMMARY_BYTES, "summary")
+    _on_gpu(("margin", margin), ("flip", flip), ("kl_topk", kl_topk), ("kl_full", kl_full),
+            ("status", status), ("group", group), ("workspace", workspace), ("bins", bins),
+            ("summary", summary))
     summ = summary
     ws_bytes = int(_lib.lcmp_bin_workspace_bytes(n, n_groups, ne))
     if ws_bytes == 0:
@@ -359,6 +457,9 @@ def lcmp_perturb(src: torch.Tensor, mode: int, param: int = 0, out: torch.Tensor
         out = out.view(1, -1)
     if out.shape[0] != rows or out.shape[1] < cols:
         raise ValueError("out must hold [rows, cols]")
+    _dtype_code(src)
+    _dtype_code(out)
+    _on_gpu(("src", src), ("out", out))
     rc = _lib.lcmp_perturb(src.data_ptr(), _dtype_code(src), _ld(src), out.data_ptr(),
                            _dtype_code(out), _ld(out), rows, cols, mode, param, _stream(stream))
     _check(rc, "lcmp_perturb")

@@ -252,3 +252,29 @@ def test_compare_record_argument_errors(L):
     assert call(ws_bytes=8) == -4
     assert call(ws=FAKE + 8) == -1
     assert call(n=0) == 0
+
+
+def test_binding_checks_tensors_before_any_call(L):
+    """Tensors too small, of the wrong type, or not on the GPU are rejected in
+    the binding, before a pointer reaches the library (CPU tensors here)."""
+    import torch
+    base = torch.zeros(4, 100)
+    with pytest.raises(ValueError, match="cand"):
+        L.lcmp_compare_logits(base, torch.zeros(3, 100))          # row counts differ
+    with pytest.raises(ValueError, match="base"):
+        L.lcmp_compare_logits(base, base, v=101)                  # v beyond the columns
+    small = {"kl_topk": torch.zeros(3, dtype=torch.float64)}
+    with pytest.raises(ValueError, match="kl_topk"):
+        L.lcmp_compare_logits(base, base, out=small)
+    with pytest.raises(ValueError):
+        L.lcmp_compare_logits(base, base)                         # host memory
+    rec = {"topk_idx": torch.zeros(4, 20, dtype=torch.int32),
+           "topk_val": torch.zeros(4, 20, dtype=torch.float64),  # wrong element type
+           "lse_rest": torch.zeros(4, dtype=torch.float64), "status": torch.zeros(4, dtype=torch.uint8)}
+    with pytest.raises(ValueError):
+        L.lcmp_compare_record(rec, base)
+    with pytest.raises(ValueError, match="margin"):
+        L.lcmp_bin_report(torch.zeros(10), torch.zeros(10, dtype=torch.uint8),
+                          torch.zeros(10, dtype=torch.float64), None, (0.5, 1.0))
+    with pytest.raises(ValueError):
+        L.lcmp_perturb(base, 0, 7)
