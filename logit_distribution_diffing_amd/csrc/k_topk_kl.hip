@@ -24,19 +24,23 @@ __device__ __forceinline__ void wave_fence2() {
   __builtin_amdgcn_wave_barrier();
 }
 
+// The row's top-k slots (C * kint of them, C <= kMaxMergeChunks) are held in
+// registers, R per lane (R * 64 >= C * kint; instances for R = 1, 2, 4, 16).
+constexpr int kMaxMergeChunks = 16;
+
+template <int R>
 __global__ __launch_bounds__(kWave) void k_topk_kl(FinalArgs a) {
-  extern __shared__ __attribute__((aligned(16))) uint32_t smem[];
+  constexpr int kSlotRounds = R;
+  __shared__ uint32_t sel_key[kMaxK];  // the kint selected slots, in slot order
+  __shared__ int32_t sel_idx[kMaxK];
+  __shared__ float s_a[kMaxK];         // the same, value descending, index ascending
+  __shared__ int32_t s_i[kMaxK];
   const int lane = lane_id();
   const int64_t row = blockIdx.x;
   const int C = a.nchunks;
   const int kint = a.kint;
   const int mcap = C * kint;            // top-k slots of the row's chunks
-  const int mpad = (mcap + 3) & ~3;     // padded to whole 16-byte reads
-  uint32_t *e_key = smem;                          // [mpad]
-  int32_t *e_idx = (int32_t *)(e_key + mpad);      // [mpad]
-  float *s_a = (float *)(e_idx + mpad);            // [kMaxK] sorted
-  int32_t *s_i = (int32_t *)(s_a + kMaxK);         // [kMaxK]
-  int32_t *s_cnt = s_i + kMaxK;                    // [kMaxChunks]
+  const int rounds = (mcap + kWave - 1) / kWave;
 
   // ---- every load that does not depend on another goes out first: the chunk
   // records, the bitwise chunk records and all top-k slots (the slots past a
@@ -53,31 +57,23 @@ __global__ __launch_bounds__(kWave) void k_topk_kl(FinalArgs a) {
   cb.sum_abs = cb.ssd = cb.ssb = 0.0;
   if (a.bd && has) cb = a.bits[row * C + lane];
   const int64_t tb = row * (int64_t)mcap;
-  float v0 = 0.0f;
-  int x0 = 0;
-  if (lane < mcap) {
-    v0 = a.ta[tb + lane];
-    x0 = a.ti[tb + lane];
-  }
-  if (has) s_cnt[lane] = cs.cnt;
-  wave_fence2();
-  // slot e holds entry (e mod kint) of chunk e / kint; empty slots get key 0,
-  // below every stored key, and sort last
-  for (int e = lane; e < mpad; e += kWave) {
-    float v = v0;
-    int x = x0;
-    if (e >= kWave && e < mcap) {
-      v = a.ta[tb + e];
-      x = a.ti[tb + e];
+  float sv[kSlotRounds];
+  int sx[kSlotRounds];
+#pragma unroll
+  for (int q = 0; q < kSlotRounds; ++q) {
+    const int e = lane + kWave * q;
+    sv[q] = 0.0f;
+    sx[q] = 0;
+    if (q < rounds && e < mcap) {
+      sv[q] = a.ta[tb + e];
+      sx[q] = a.ti[tb + e];
     }
-    const int c = e / kint;
-    const bool ok = e < mcap && e - c * kint < s_cnt[c];
-    e_key[e] = ok ? rank_key(v) : 0u;
-    e_idx[e] = ok ? x : 0x7fffffff;
   }
-  for (int j = lane; j < kMaxK; j += kWave) {
-    s_a[j] = -INFINITY;
-    s_i[j] = -1;
+  if (lane < kMaxK) {
+    s_a[lane] = -INFINITY;
+    s_i[lane] = -1;
+    sel_key[lane] = 0u;
+    sel_idx[lane] = 0x7fffffff;
   }
 
   if (a.bd) {
@@ -149,26 +145,90 @@ __global__ __launch_bounds__(kWave) void k_topk_kl(FinalArgs a) {
   const int bx = wave_min((has && cs.bidx >= 0 && bm == BM) ? cs.bidx : 0x7fffffff);
   const int top1_cand = bx == 0x7fffffff ? -1 : bx;
 
-  // ---- rank of every slot among all slots (keys are distinct through the
-  // index; the valid slots number at least kint, so only they get ranks
-  // below kint), four slots per broadcast read
+  // ---- the row's top kint slots.  Slot e holds entry (e mod kint) of chunk
+  // e / kint; empty slots get key 0, below every stored key.  Keys are
+  // distinct through the index, and at least kint slots are filled (every
+  // chunk stores min(kint, its length) entries).
+  uint32_t key[kSlotRounds];
+  int idx[kSlotRounds];
+#pragma unroll
+  for (int q = 0; q < kSlotRounds; ++q) {
+    key[q] = 0u;
+    idx[q] = 0x7fffffff;
+    if (q < rounds) {
+      const int e = lane + kWave * q;
+      const int c = e / kint;
+      // chunk c's entry count, from lane c
+      const int cnt_c = __builtin_amdgcn_ds_bpermute(min(c, kWave - 1) << 2, has ? cs.cnt : 0);
+      if (e < mcap && e - c * kint < cnt_c) {
+        key[q] = rank_key(sv[q]);
+        idx[q] = sx[q];
+      }
+    }
+  }
+  // kint-th largest key T, one bit at a time from the top; then the ties at T
+  // that are kept, lowest indices first
+  uint32_t T = 0;
+#pragma unroll 1
+  for (int bit = 31; bit >= 0; --bit) {
+    const uint32_t c = T | (1u << bit);
+    int n = 0;
+#pragma unroll
+    for (int q = 0; q < kSlotRounds; ++q)
+      if (q < rounds) n += __popcll(ballot(key[q] >= c));
+    if (n >= kint) T = c;
+  }
+  int ngt = 0, neq = 0;
+#pragma unroll
+  for (int q = 0; q < kSlotRounds; ++q) {
+    if (q < rounds) {
+      ngt += __popcll(ballot(key[q] > T));
+      neq += __popcll(ballot(key[q] == T));
+    }
+  }
+  const int need = kint - ngt;
+  uint32_t isel = 0x7fffffffu;
+  if (neq > need) {
+    uint32_t I = 0;
+#pragma unroll 1
+    for (int bit = 30; bit >= 0; --bit) {
+      const uint32_t c = I | (1u << bit);
+      int n = 0;
+#pragma unroll
+      for (int q = 0; q < kSlotRounds; ++q)
+        if (q < rounds) n += __popcll(ballot(key[q] == T && (uint32_t)idx[q] < c));
+      if (n < need) I = c;
+    }
+    isel = I;
+  }
+  // compact the kint kept slots, then order them: lane j < kint holds kept
+  // entry j and counts the kept entries ahead of it
+  int fill = 0;
+#pragma unroll
+  for (int q = 0; q < kSlotRounds; ++q) {
+    if (q < rounds) {
+      const bool keep = key[q] > T || (key[q] == T && (uint32_t)idx[q] <= isel);
+      const uint64_t m = ballot(keep);
+      const int pos = fill + prefix_count(m);
+      if (keep && pos < kint) {  // exactly kint are kept when kint slots are filled
+        sel_key[pos] = key[q];
+        sel_idx[pos] = idx[q];
+      }
+      fill += __popcll(m);
+    }
+  }
   wave_fence2();
-  for (int e = lane; e < mpad; e += kWave) {
-    const uint32_t ke = e_key[e];
-    const int ie = e_idx[e];
-    int rank = 0;
-    for (int f = 0; f < mpad; f += 4) {
-      const uint4 k4 = *(const uint4 *)(e_key + f);
-      const int4 i4 = *(const int4 *)(e_idx + f);
-      rank += (k4.x > ke || (k4.x == ke && i4.x < ie)) ? 1 : 0;
-      rank += (k4.y > ke || (k4.y == ke && i4.y < ie)) ? 1 : 0;
-      rank += (k4.z > ke || (k4.z == ke && i4.z < ie)) ? 1 : 0;
-      rank += (k4.w > ke || (k4.w == ke && i4.w < ie)) ? 1 : 0;
-    }
-    if (rank < kint && ke != 0u) {
-      s_a[rank] = rank_key_inv(ke);
-      s_i[rank] = ie;
-    }
+  const uint32_t kj = lane < kint ? sel_key[lane] : 0u;
+  const int ij = lane < kint ? sel_idx[lane] : 0x7fffffff;
+  int rank = 0;
+  for (int i = 0; i < kint; ++i) {
+    const uint32_t ki = (uint32_t)__builtin_amdgcn_readlane((int)kj, i);
+    const int ii = __builtin_amdgcn_readlane(ij, i);
+    rank += (ki > kj || (ki == kj && ii < ij)) ? 1 : 0;
+  }
+  if (lane < kint && kj != 0u) {
+    s_a[rank] = rank_key_inv(kj);
+    s_i[rank] = ij;
   }
   wave_fence2();
 
@@ -266,9 +326,17 @@ __global__ __launch_bounds__(kWave) void k_topk_kl(FinalArgs a) {
 
 hipError_t launch_topk_kl(const FinalArgs &a, hipStream_t stream) {
   if (a.n == 0) return hipSuccess;
-  const size_t mpad = ((size_t)a.nchunks * a.kint + 3) & ~(size_t)3;
-  const size_t shmem = mpad * 8 + (size_t)kMaxK * 8 + (size_t)kMaxChunks * 4;
-  hipLaunchKernelGGL(k_topk_kl, dim3((unsigned)a.n), dim3(kWave), shmem, stream, a);
+  if (a.nchunks > kMaxMergeChunks) return hipErrorInvalidValue;
+  const int rounds = (a.nchunks * a.kint + kWave - 1) / kWave;
+  const dim3 grid((unsigned)a.n);
+  if (rounds <= 1)
+    hipLaunchKernelGGL((k_topk_kl<1>), grid, dim3(kWave), 0, stream, a);
+  else if (rounds <= 2)
+    hipLaunchKernelGGL((k_topk_kl<2>), grid, dim3(kWave), 0, stream, a);
+  else if (rounds <= 4)
+    hipLaunchKernelGGL((k_topk_kl<4>), grid, dim3(kWave), 0, stream, a);
+  else
+    hipLaunchKernelGGL((k_topk_kl<16>), grid, dim3(kWave), 0, stream, a);
   return hipGetLastError();
 }
 
