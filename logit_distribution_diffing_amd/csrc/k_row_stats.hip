@@ -53,6 +53,7 @@ struct WaveState {
   // such chunks take the exact path throughout
   float r2h, r2l, gate;
   float nr2h;  // -r2h, kept where the per-element multiply-add reads it
+  int huge;    // r2l != 0 (uniform)
   // candidate argmax (uniform)
   float bmax;
   int bidx;
@@ -333,21 +334,33 @@ __device__ __forceinline__ uint32_t load_checked(uint32_t (&ua)[8], uint32_t (&u
 // ---------------------------------------------------------------- rare work
 
 // Move the exp2 reference when a logit outgrows it (rare after the first step).
-// The reference and the gate stay wave-uniform, in scalar registers.
+// The reference and the gate stay wave-uniform, in scalar registers.  Below
+// 2^28 (log2 units) the reference is an integer, so moving it scales the sums
+// by an exact power of two; above, it is the float product plus its rounding
+// residual, and the fractional part of the shift goes through exp2 in float
+// (relative error near 1e-7, common to the three sums).
 __device__ __forceinline__ void rescale(WaveState &st, float gm) {
   const float wm = uniform(wave_max(gm));
-  const float nh = uniform(wm * kL2E);
-  const bool huge = fabsf(nh) >= 268435456.0f && isfinite(nh);
-  const float nl = uniform(huge ? fmaf(wm, kL2E, -nh) : 0.0f);
-  // before the first reference the sums are still 0
-  const double sc =
-      st.r2h > -INFINITY ? exp2(((double)st.r2h + (double)st.r2l) - ((double)nh + (double)nl)) : 0.0;
+  const float xh = wm * kL2E;
+  const bool huge = fabsf(xh) >= 268435456.0f && isfinite(xh);
+  const float nh = uniform(huge ? xh : ceilf(xh));
+  const float nl = uniform(huge ? fmaf(wm, kL2E, -xh) : 0.0f);
+  // before the first reference the sums are still 0; a shift below 2^-2048
+  // (or undefined, with infinite references) clears them
+  double sc = 0.0;
+  const double dd = ((double)st.r2h - (double)nh) + ((double)st.r2l - (double)nl);
+  if (st.r2h > -INFINITY && dd > -2048.0) {
+    const double k = floor(dd);
+    const float fr = (float)(dd - k);
+    sc = ldexp(fr == 0.0f ? 1.0 : (double)__builtin_amdgcn_exp2f(fr), (int)k);
+  }
   st.s *= sc;
   st.d *= sc;
   st.f *= sc;
   st.r2h = nh;
   st.nr2h = -nh;
   st.r2l = nl;
+  st.huge = huge ? 1 : 0;
   st.gate = uniform((nh + kRescaleLog2) * (1.0f / kL2E));
 }
 
@@ -442,18 +455,13 @@ __device__ __forceinline__ void process_step(const uint32_t (&ua)[8], const uint
   // |delta| <= 1/8 bounds sum delta^2.
   bool ok = !tail;
   if (CMP && BITS)
-    ok = ok && st.r2l == 0.0f && (dmax <= kPolyMax) && isfinite(sab + ssb);
+    ok = ok && !st.huge && (dmax <= kPolyMax) && isfinite(sab + ssb);
   else if (CMP)
-    ok = ok && st.r2l == 0.0f && (dmax <= kPolyMax) && (dg == dg);
+    ok = ok && !st.huge && (dmax <= kPolyMax) && (dg == dg);
   else if (BITS)
     ok = ok && isfinite(sab + ssd + ssb);
 
   if (ok) {
-    if (CMP) {
-      st.s += (double)sg;
-      st.d += (double)dg;
-      st.f += (double)fg;
-    }
     if (BITS) {
       st.sab += (double)sab;
       st.ssd += (double)ssd;
@@ -470,8 +478,8 @@ __device__ __forceinline__ void process_step(const uint32_t (&ua)[8], const uint
       for (int j = 0; j < 8; ++j) st.max_ulp = max(st.max_ulp, ulp_exact<W16>(ua[j], ub[j]));
     }
     // exact element-by-element path: special values, large differences,
-    // huge logits, ragged tails
-    float s2 = 0.0f, d2 = 0.0f, f2 = 0.0f;
+    // huge logits, ragged tails.  The fast sums of this lane are replaced.
+    sg = dg = fg = 0.0f;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       if (!((valid >> j) & 1u)) continue;
@@ -498,31 +506,31 @@ __device__ __forceinline__ void process_step(const uint32_t (&ua)[8], const uint
           if (b == -INFINITY)
             st.n_binf++;
           else
-            f2 += __builtin_amdgcn_exp2f(fmaf(b, kL2E, -st.r2h) - st.r2l);  // q mass where p = 0
+            fg += __builtin_amdgcn_exp2f(fmaf(b, kL2E, -st.r2h) - st.r2l);  // q mass where p = 0
           continue;
         }
         const float e = __builtin_amdgcn_exp2f(fmaf(a, kL2E, -st.r2h) - st.r2l);
-        s2 += e;
+        sg += e;
         if (b == -INFINITY) {  // p > 0, q = 0: the full KL is infinite
           st.n_binf++;
           st.n_qzero++;
-          f2 -= e;
+          fg -= e;
           continue;
         }
         const float dj = a - b;
         const float ed = e * dj;
-        d2 += ed;
+        dg += ed;
         if (fabsf(dj) <= kPolyMax)
-          f2 = fmaf(ed * dj, phi_over_d2(dj), f2);
+          fg = fmaf(ed * dj, phi_over_d2(dj), fg);
         else  // e*phi = e*(delta - 1) + 2^(b*log2e - r2)
-          f2 += fmaf(e, dj - 1.0f, __builtin_amdgcn_exp2f(fmaf(b, kL2E, -st.r2h) - st.r2l));
+          fg += fmaf(e, dj - 1.0f, __builtin_amdgcn_exp2f(fmaf(b, kL2E, -st.r2h) - st.r2l));
       }
     }
-    if (CMP) {
-      st.s += (double)s2;
-      st.d += (double)d2;
-      st.f += (double)f2;
-    }
+  }
+  if (CMP) {
+    st.s += (double)sg;
+    st.d += (double)dg;
+    st.f += (double)fg;
   }
 
   if (CMP) {
@@ -637,6 +645,7 @@ __attribute__((amdgpu_waves_per_eu(4, 8))) void k_row_stats(StreamArgs args) {
   st.r2h = -INFINITY;
   st.nr2h = INFINITY;
   st.r2l = 0.0f;
+  st.huge = 0;
   st.gate = -INFINITY;
   st.bmax = -INFINITY;
   st.bidx = -1;
@@ -696,30 +705,39 @@ __attribute__((amdgpu_waves_per_eu(4, 8))) void k_row_stats(StreamArgs args) {
       uint32_t ua[8], ub[8];
       cur.a.decode(ua);
       cur.b.decode(ub);
-      process_step<CMP, BITS, W16, MAPB>(ua, ub, 0xffu, false, lo + sp * kSpan, lane, kint, st, ba,
-                                         bi);
+      process_step<CMP, BITS, W16, MAPB>(ua, ub, 0xffu, false, lo + sp * kSpan, lane, kint, st,
+                                            ba, bi);
       rd = rd + 1 == R ? 0 : rd + 1;
       wr = wr + 1 == R ? 0 : wr + 1;
     }
   } else if constexpr (VEC) {
-    // Two register sets: while one step is processed the next one's loads are
-    // in flight.  The prefetch is unconditional (the last step is fetched
-    // twice): a load under a branch makes the wait before the current step's
-    // use a full drain of the memory counter.
+    // Two register sets used in turn: while one step is processed the other
+    // set's loads are in flight, and nothing is copied between the sets.  The
+    // prefetch is unconditional (past the end the last step is fetched again):
+    // a load under a branch makes the wait before a use a full drain of the
+    // memory counter.
     const char *pa = ra + (int64_t)lo * SA, *pb = rb + (int64_t)lo * SB;
-    Raw<TA, TB> cur, nxt;
-    if (nfull > 0) cur.load(pa, pb, (uint32_t)lane);
-#pragma unroll 1
-    for (int sp = 0; sp < nfull; ++sp) {
-      const int sn = sp + 1 < nfull ? sp + 1 : sp;
-      nxt.load(pa + (int64_t)sn * kSpan * SA, pb + (int64_t)sn * kSpan * SB, (uint32_t)lane);
+    Raw<TA, TB> r0, r1;
+    auto fetch = [&](Raw<TA, TB> &r, int s) {
+      r.load(pa + (int64_t)s * kStepA, pb + (int64_t)s * kStepB, (uint32_t)lane);
+    };
+    auto step = [&](const Raw<TA, TB> &r, int s) {
       uint32_t ua[8], ub[8];
-      cur.a.decode(ua);
-      cur.b.decode(ub);
-      process_step<CMP, BITS, W16, MAPB>(ua, ub, 0xffu, false, lo + sp * kSpan, lane, kint, st, ba,
+      r.a.decode(ua);
+      r.b.decode(ub);
+      process_step<CMP, BITS, W16, MAPB>(ua, ub, 0xffu, false, lo + s * kSpan, lane, kint, st, ba,
                                          bi);
-      cur = nxt;
+    };
+    if (nfull > 0) fetch(r0, 0);
+    int sp = 0;
+#pragma unroll 1
+    for (; sp + 1 < nfull; sp += 2) {
+      fetch(r1, sp + 1);
+      step(r0, sp);
+      fetch(r0, sp + 2 < nfull ? sp + 2 : sp + 1);
+      step(r1, sp + 1);
     }
+    if (sp < nfull) step(r0, sp);
   } else {
 #pragma unroll 1
     for (int sp = 0; sp < nfull; ++sp) {
