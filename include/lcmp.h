@@ -165,6 +165,11 @@ size_t lcmp_compare_workspace_bytes(int64_t n, int64_t v, int k, uint32_t flags)
  *   flags         0 or LCMP_WITH_BITDIFF; with it, bd (device [n]) receives the
  *                 bitwise statistics of each row pair (bd may be NULL otherwise).
  *   out           host struct of device output pointers (see lcmp_row_out).
+ * One pass reads each row pair once.  Rows whose "other"-bucket term is
+ * ill-conditioned in the one-pass sums (the candidate keeps nearly all of its
+ * mass inside the baseline's top-k) are listed on the device and their two
+ * buckets are summed again directly, so such rows read their pair once more;
+ * ordinary rows never are.
  * Returns LCMP_OK or a negative lcmp_status.
  */
 int lcmp_compare_logits(const void *base, int tb, int64_t ld_base, const void *cand, int tc,

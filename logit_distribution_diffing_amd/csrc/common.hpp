@@ -36,9 +36,10 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 // --------------------------------------------------------------------- records
 
 // One per (row, chunk): streamed softmax sums and counters.  s, d, f are
-// sum e_i, sum e_i*delta_i and sum e_i*phi(delta_i) with e_i = 2^(a_i*kL2E - r2).
+// sum e_i, sum e_i*delta_i and sum e_i*phi(delta_i) with e_i = 2^(a_i*kL2E - r2);
+// w is the candidate's mass sum 2^(b_i*kL2E - r2), formed without cancellation.
 struct ChunkStats {
-  double s, d, f;
+  double s, d, f, w;
   double r2;     // reference in log2 units; -inf when the chunk held no finite logit
   float bmax;    // candidate maximum (-inf if none)
   int32_t bidx;  // lowest index of bmax, -1 if none

@@ -46,14 +46,19 @@ constexpr int kTauOpen = 0x7fffffff;
 constexpr int kTauLaneMax = 0x7ffffffe;  // same, after the lane-maxima bound was taken
 
 struct WaveState {
-  // softmax sums (per lane, double across 8-element runs)
-  double s, d, f;
+  // softmax sums (per lane, double across 8-element runs) and the candidate's
+  // mass w = sum 2^(b*log2e - r2): on the fast path each run adds s - d + f
+  // (every term e * e^-delta with |delta| <= 1/8, no cancellation), on the
+  // exact path each candidate weight is formed in double
+  double s, d, f, w;
   // uniform exp2 reference r2h + r2l: r2l is 0 unless the logits are so large
   // (|r2h| >= 2^28) that one float cannot hold the reference within a unit;
   // such chunks take the exact path throughout
   float r2h, r2l, gate;
   float nr2h;  // -r2h, kept where the per-element multiply-add reads it
   int huge;    // r2l != 0 (uniform)
+  int seen;    // a finite baseline logit was seen; until then the reference
+               // follows the candidate (uniform)
   // candidate argmax (uniform)
   float bmax;
   int bidx;
@@ -333,6 +338,45 @@ __device__ __forceinline__ uint32_t load_checked(uint32_t (&ua)[8], uint32_t (&u
 
 // ---------------------------------------------------------------- rare work
 
+// 2^x in double for the exact path: x = k + f with k = rint(x), then
+// e^(f ln 2) by its Taylor series to the 12th power (|f ln 2| <= 0.35, so the
+// dropped terms are below 1e-14 relative).  0 below 2^-1075, +inf from 2^1024.
+__device__ __forceinline__ double exp2_d(double x) {
+  if (!(x > -1075.0)) return 0.0;
+  if (x >= 1024.0) return INFINITY;
+  const double k = rint(x);
+  const double t = (x - k) * kLn2;
+  double p = 1.0 / 479001600.0;  // 1/12!
+  p = fma(p, t, 1.0 / 39916800.0);
+  p = fma(p, t, 1.0 / 3628800.0);
+  p = fma(p, t, 1.0 / 362880.0);
+  p = fma(p, t, 1.0 / 40320.0);
+  p = fma(p, t, 1.0 / 5040.0);
+  p = fma(p, t, 1.0 / 720.0);
+  p = fma(p, t, 1.0 / 120.0);
+  p = fma(p, t, 1.0 / 24.0);
+  p = fma(p, t, 1.0 / 6.0);
+  p = fma(p, t, 0.5);
+  p = fma(p, t, 1.0);
+  p = fma(p, t, 1.0);
+  return ldexp(p, (int)k);
+}
+
+// phi(d) = d + expm1(-d) = d^2 (1/2 - d/3! + d^2/4! - ...) in double for
+// |d| <= 1/8, to the 10th power of d (dropped terms below 1e-15 relative).
+__device__ __forceinline__ double phi_d(double d) {
+  double p = 1.0 / 3628800.0;  // 1/10!
+  p = fma(p, -d, 1.0 / 362880.0);
+  p = fma(p, -d, 1.0 / 40320.0);
+  p = fma(p, -d, 1.0 / 5040.0);
+  p = fma(p, -d, 1.0 / 720.0);
+  p = fma(p, -d, 1.0 / 120.0);
+  p = fma(p, -d, 1.0 / 24.0);
+  p = fma(p, -d, 1.0 / 6.0);
+  p = fma(p, -d, 0.5);
+  return d * d * p;
+}
+
 // Move the exp2 reference when a logit outgrows it (rare after the first step).
 // The reference and the gate stay wave-uniform, in scalar registers.  Below
 // 2^28 (log2 units) the reference is an integer, so moving it scales the sums
@@ -346,17 +390,20 @@ __device__ __forceinline__ void rescale(WaveState &st, float gm) {
   const float nh = uniform(huge ? xh : ceilf(xh));
   const float nl = uniform(huge ? fmaf(wm, kL2E, -xh) : 0.0f);
   // before the first reference the sums are still 0; a shift below 2^-2048
-  // (or undefined, with infinite references) clears them
+  // (or undefined, with infinite references) clears them.  A move down only
+  // happens before any fast-path sum was formed.
   double sc = 0.0;
   const double dd = ((double)st.r2h - (double)nh) + ((double)st.r2l - (double)nl);
   if (st.r2h > -INFINITY && dd > -2048.0) {
     const double k = floor(dd);
     const float fr = (float)(dd - k);
-    sc = ldexp(fr == 0.0f ? 1.0 : (double)__builtin_amdgcn_exp2f(fr), (int)k);
+    // a move down (only onto the first baseline logits) is capped at 2^1000
+    sc = ldexp(fr == 0.0f ? 1.0 : (double)__builtin_amdgcn_exp2f(fr), (int)fmin(k, 1000.0));
   }
   st.s *= sc;
   st.d *= sc;
   st.f *= sc;
+  st.w *= sc;
   st.r2h = nh;
   st.nr2h = -nh;
   st.r2l = nl;
@@ -410,8 +457,19 @@ __device__ __forceinline__ void process_step(const uint32_t (&ua)[8], const uint
   if (CMP) {
     ga = max8(xa);
     gb = max8(xb);
-    const float gm = max3f(ga, gb, gb);
-    if (ballot(gm > st.gate)) rescale(st, gm);
+    // The reference follows the baseline, so its weights e never underflow
+    // because the candidate runs far above it; the candidate's weights, in
+    // the exact path only, are formed in double.  Before the chunk's first
+    // finite baseline logit the candidate sets the reference, which then
+    // moves to the baseline, down if need be.
+    if (st.seen) {
+      if (ballot(ga > st.gate)) rescale(st, ga);
+    } else if (ballot(ga > -INFINITY)) {
+      rescale(st, ga);
+      st.seen = 1;
+    } else if (ballot(gb > st.gate)) {
+      rescale(st, gb);
+    }
   }
 
   // fast path: every element finite, |delta| <= 1/8
@@ -478,12 +536,24 @@ __device__ __forceinline__ void process_step(const uint32_t (&ua)[8], const uint
       for (int j = 0; j < 8; ++j) st.max_ulp = max(st.max_ulp, ulp_exact<W16>(ua[j], ub[j]));
     }
     // exact element-by-element path: special values, large differences,
-    // huge logits, ragged tails.  The fast sums of this lane are replaced.
+    // huge logits, ragged tails.  The fast sums of this lane are dropped; the
+    // weights are formed in double, where neither side under- or overflows.
     sg = dg = fg = 0.0f;
-#pragma unroll
+    double s2 = 0.0, d2 = 0.0, f2 = 0.0, w2 = 0.0;
+    const double r2d = (double)st.r2h + (double)st.r2l;
+    // one element per trip (j is uniform): the double exponentials appear
+    // once in the code rather than once per element
+#pragma unroll 1
     for (int j = 0; j < 8; ++j) {
       if (!((valid >> j) & 1u)) continue;
-      const float a = xa[j], b = xb[j];
+      float a = xa[0], b = xb[0];
+#pragma unroll
+      for (int t = 1; t < 8; ++t) {
+        if (j == t) {
+          a = xa[t];
+          b = xb[t];
+        }
+      }
       const bool fa = isfinite(a), fb = isfinite(b);
       if (BITS) {
         st.nfa += fa ? 0 : 1;
@@ -503,34 +573,46 @@ __device__ __forceinline__ void process_step(const uint32_t (&ua)[8], const uint
         }
         if (a == -INFINITY) {
           st.n_ainf++;
-          if (b == -INFINITY)
+          if (b == -INFINITY) {
             st.n_binf++;
-          else
-            fg += __builtin_amdgcn_exp2f(fmaf(b, kL2E, -st.r2h) - st.r2l);  // q mass where p = 0
+          } else {  // q mass where p = 0
+            const double eb = exp2_d((double)b * (double)kL2E - r2d);
+            f2 += eb;
+            w2 += eb;
+          }
           continue;
         }
-        const float e = __builtin_amdgcn_exp2f(fmaf(a, kL2E, -st.r2h) - st.r2l);
-        sg += e;
+        const double e = exp2_d((double)a * (double)kL2E - r2d);
+        s2 += e;
         if (b == -INFINITY) {  // p > 0, q = 0: the full KL is infinite
           st.n_binf++;
           st.n_qzero++;
-          fg -= e;
+          f2 -= e;
           continue;
         }
-        const float dj = a - b;
-        const float ed = e * dj;
-        dg += ed;
-        if (fabsf(dj) <= kPolyMax)
-          fg = fmaf(ed * dj, phi_over_d2(dj), fg);
+        const double dj = (double)a - (double)b;  // exact
+        const double eb = exp2_d((double)b * (double)kL2E - r2d);
+        d2 += e * dj;
+        w2 += eb;
+        if (fabs(dj) <= (double)kPolyMax)
+          f2 += e * phi_d(dj);
         else  // e*phi = e*(delta - 1) + 2^(b*log2e - r2)
-          fg += fmaf(e, dj - 1.0f, __builtin_amdgcn_exp2f(fmaf(b, kL2E, -st.r2h) - st.r2l));
+          f2 += fma(e, dj - 1.0, eb);
       }
+    }
+    if (CMP) {
+      st.s += s2;
+      st.d += d2;
+      st.f += f2;
+      st.w += w2;
     }
   }
   if (CMP) {
-    st.s += (double)sg;
-    st.d += (double)dg;
-    st.f += (double)fg;
+    const double sd = sg, dd = dg, fd = fg;
+    st.s += sd;
+    st.d += dd;
+    st.f += fd;
+    st.w += (sd - dd) + fd;
   }
 
   if (CMP) {
@@ -629,6 +711,8 @@ __attribute__((amdgpu_waves_per_eu(4, 8))) void k_row_stats(StreamArgs args) {
   const int lane = lane_id();
   const int64_t item = (int64_t)blockIdx.x * W + wid;
   if (item >= args.n * args.nchunks) return;
+  // the finalize of the same call appends to this list after the pass
+  if (item == 0 && lane == 0 && args.fix_count) *args.fix_count = 0u;
   const int64_t row = item / args.nchunks;
   const int chunk = (int)(item - row * args.nchunks);
   // column indices fit in 32 bits (the vocabulary is below 2^31)
@@ -642,10 +726,12 @@ __attribute__((amdgpu_waves_per_eu(4, 8))) void k_row_stats(StreamArgs args) {
 
   WaveState st;
   st.s = st.d = st.f = 0.0;
+  st.w = 0.0;
   st.r2h = -INFINITY;
   st.nr2h = INFINITY;
   st.r2l = 0.0f;
   st.huge = 0;
+  st.seen = 0;
   st.gate = -INFINITY;
   st.bmax = -INFINITY;
   st.bidx = -1;
@@ -766,6 +852,7 @@ __attribute__((amdgpu_waves_per_eu(4, 8))) void k_row_stats(StreamArgs args) {
       late.ti[tk + lane] = bi[lane];
     }
     const double S = wave_sum(st.s), D = wave_sum(st.d), F = wave_sum(st.f);
+    const double Wc = wave_sum(st.w);
     const int nb = wave_sum(st.n_bad), na = wave_sum(st.n_ainf), nbi = wave_sum(st.n_binf),
               nq = wave_sum(st.n_qzero);
     if (lane == 0) {
@@ -773,6 +860,7 @@ __attribute__((amdgpu_waves_per_eu(4, 8))) void k_row_stats(StreamArgs args) {
       cs.s = S;
       cs.d = D;
       cs.f = F;
+      cs.w = Wc;
       cs.r2 = st.r2h > -INFINITY ? (double)st.r2h + (double)st.r2l : -INFINITY;
       cs.bmax = st.bmax;
       cs.bidx = st.bidx;

@@ -2,7 +2,7 @@
 // comparison quantities, in double precision (one wave per row).
 //
 // With u = E/s (E = f - d = sum e*expm1(-delta)), L = lse_cand - lse_base =
-// log1p(u), and p_i = e_i/s:
+// log1p(u) = ln(w/s) (w the candidate's mass), and p_i = e_i/s:
 //   full KL    = sum_i p_i (delta_i + L)                 = f/s - psi(u)
 //   top-k KL   = sum_S p_i phi_i + p_o psi(E_o/p_o) - psi(u)
 // where psi(x) = x - log1p(x), phi_i = delta_i + expm1(-delta_i), S the
@@ -10,7 +10,15 @@
 // (g_i = expm1(-delta_i)).  Both are the KL of the page "在 agent 时代如何快速验证
 // kernel 对精度的影响" (section 怎么比两个分布: the KL equation and the top-20 +
 // "other" bucket) rewritten so that only second-order quantities are summed:
-// no difference of two nearly equal log-normalisers is ever formed.
+// no difference of two nearly equal log-normalisers is ever formed.  That
+// form holds while the two normalisers are close (-1/2 < u < 1).  Beyond,
+// f/s and psi(u) grow with u (or E loses the candidate mass as u nears -1),
+// so the first-order form is used, with L = ln(w/s) from the candidate mass:
+//   full KL    = d/s + L
+//   top-k KL   = sum_S p_i (delta_i + L) + p_o (ln(s_o / w_o) + L)
+// with s_o and w_o the two masses outside S.  When w_o is itself a small
+// difference of large sums, the row is listed for k_bucket_fix, which forms
+// s_o and w_o by summing the two buckets directly.
 #include "common.hpp"
 #include "launch.hpp"
 #include "merge.hpp"
@@ -138,6 +146,7 @@ __global__ __launch_bounds__(kWave) void k_topk_kl(FinalArgs a) {
   const double S = wave_sum(has ? cs.s * sc : 0.0);
   const double D = wave_sum(has ? cs.d * sc : 0.0);
   const double F = wave_sum(has ? cs.f * sc : 0.0);
+  const double W = wave_sum(has ? cs.w * sc : 0.0);
 
   // ---- candidate argmax across chunks: value descending, index ascending
   const float bm = has ? cs.bmax : -INFINITY;
@@ -245,8 +254,18 @@ __global__ __launch_bounds__(kWave) void k_topk_kl(FinalArgs a) {
     hb = a.tc == 1 ? __uint_as_float((uint32_t)((const uint16_t *)a.cand)[off] << 16)
                    : ((const float *)a.cand)[off];
   }
+  // the normalisers' log-ratio L (uniform: every lane computes it)
+  const double u = (F - D) / S;
+  const bool near = u > -0.5 && u < 1.0;
+  // the weights are powers of two of x * kL2E (kL2E a float, 1.3e-8 from
+  // log2 e): the logarithm of a ratio of them returns to natural units
+  // through 1 / (kL2E ln 2), so that a pure shift of the candidate gives
+  // L = -shift exactly
+  const double units = 1.0 / ((double)kL2E * kLn2);
+  const double L = near ? log1p(u) : log(W / S) * units;
+
   const bool ainf = ha == -INFINITY, binf = hb == -INFINITY;
-  double e = 0.0, tphi = 0.0, tg = 0.0;
+  double e = 0.0, eb = 0.0, tphi = 0.0, tg = 0.0, tpl = 0.0;
   int head_inf = 0;
   if (in_head && !ainf) {
     e = exp2((double)ha * (double)kL2E - M2);
@@ -259,9 +278,12 @@ __global__ __launch_bounds__(kWave) void k_topk_kl(FinalArgs a) {
       const double g = expm1(-dl);
       tphi = p * (dl + g);
       tg = p * g;
+      tpl = p * (dl + L);  // p_i ln(p_i / q_i)
     }
   }
+  if (in_head && !binf) eb = exp2((double)hb * (double)kL2E - M2);
   const double sum_e = wave_sum(e), sum_pphi = wave_sum(tphi), sum_pg = wave_sum(tg);
+  const double sum_eb = wave_sum(eb), sum_pl = wave_sum(tpl);
   const int n_sa = wave_sum((in_head && ainf) ? 1 : 0);
   const int n_sb = wave_sum((in_head && binf) ? 1 : 0);
   const int any_head_inf = wave_max(head_inf);
@@ -269,16 +291,15 @@ __global__ __launch_bounds__(kWave) void k_topk_kl(FinalArgs a) {
   if (a.topk_idx)
     for (int j = lane; j < a.k; j += kWave) a.topk_idx[row * a.k + j] = j < keff ? s_i[j] : -1;
 
+  int fix_slot = -1;
   if (lane == 0) {
-    double u = (F - D) / S;
-    if (!(u > -1.0)) u = -1.0 + 0x1p-52;
     const double lse_b = M2 * kLn2 + log(S);
-    const double kl_full = nq > 0 ? INFINITY : F / S - psi(u);
+    const double kl_full = nq > 0 ? INFINITY : near ? F / S - psi(u) : D / S + L;
     double klk;
     if (any_head_inf) {
       klk = INFINITY;
     } else {
-      klk = sum_pphi - psi(u);
+      klk = near ? sum_pphi - psi(u) : sum_pl;
       const int64_t n_other = a.v - keff;
       const int64_t o_fin_a = n_other - ((int64_t)na - n_sa);
       const int64_t o_fin_b = n_other - ((int64_t)nbi - n_sb);
@@ -286,11 +307,42 @@ __global__ __launch_bounds__(kWave) void k_topk_kl(FinalArgs a) {
         if (o_fin_b == 0) {
           klk = INFINITY;
         } else {
-          const double p_o = fmax(0.0, (S - sum_e) / S);
+          const double s_o = S - sum_e;
+          const double p_o = fmax(0.0, s_o / S);
           if (p_o > 0.0) {
-            double x = (u - sum_pg) / p_o;
-            if (!(x > -1.0)) x = -1.0 + 0x1p-52;
-            klk += p_o * psi(x);
+            // The bucket term needs the candidate's mass outside S, here a
+            // difference of the one-pass sums.  When that difference is
+            // small against its terms it is ill-conditioned: with the
+            // normalisers close, when the candidate keeps all but 2^-10 of
+            // the baseline's bucket share inside S (its float-accumulated
+            // parts then dominate the error); with them far apart, when the
+            // candidate's mass outside S is below 2^-30 of its total (a
+            // large head weight swamps it in double).  Such rows go to
+            // k_bucket_fix, which sums both buckets directly; the value
+            // written here stands until then.
+            bool ill;
+            if (near) {
+              double x = (u - sum_pg) / p_o;
+              ill = !(x > -1.0 + 0x1p-10);
+              if (!(x > -1.0)) x = -1.0 + 0x1p-52;
+              klk += p_o * psi(x);
+            } else {
+              ill = !(W - sum_eb > W * 0x1p-30);
+              const double w_o = fmax(W - sum_eb, W * 0x1p-52);
+              klk += p_o * (log(s_o / w_o) * units + L);
+            }
+            if (ill && a.fix && a.kl_topk) {
+              fix_slot = (int)atomicAdd(a.fix_count, 1u);
+              FixEntry fe;
+              fe.row = row;
+              fe.m2 = M2;
+              fe.s = S;
+              fe.head = sum_pl;
+              fe.l = L;
+              fe.keff = keff;
+              fe.done = 0u;
+              a.fix[fix_slot] = fe;
+            }
           }
         }
       }
@@ -299,7 +351,7 @@ __global__ __launch_bounds__(kWave) void k_topk_kl(FinalArgs a) {
     if (a.kl_full) a.kl_full[row] = kl_full;
     if (a.margin) a.margin[row] = (double)s_a[0] - (double)s_a[1];
     if (a.lse_base) a.lse_base[row] = lse_b;
-    if (a.lse_cand) a.lse_cand[row] = lse_b + log1p(u);
+    if (a.lse_cand) a.lse_cand[row] = lse_b + L;
     if (a.top1_base) a.top1_base[row] = s_i[0];
     if (a.top2_base) a.top2_base[row] = s_i[1];
     if (a.top1_cand) a.top1_cand[row] = top1_cand;
@@ -316,12 +368,14 @@ __global__ __launch_bounds__(kWave) void k_topk_kl(FinalArgs a) {
         const float xc = a.tc == 1 ? __uint_as_float((uint32_t)((const uint16_t *)a.cand)[oc] << 16)
                                    : ((const float *)a.cand)[oc];
         lpb = (double)xb - lse_b;
-        lpc = (double)xc - (lse_b + log1p(u));
+        lpc = (double)xc - (lse_b + L);
       }
       if (a.logp_base) a.logp_base[row] = lpb;
       if (a.logp_cand) a.logp_cand[row] = lpc;
     }
   }
+  fix_slot = __shfl(fix_slot, 0, kWave);
+  if (fix_slot >= 0 && lane < keff) a.fix_head[(int64_t)fix_slot * a.k + lane] = s_i[lane];
 }
 
 hipError_t launch_topk_kl(const FinalArgs &a, hipStream_t stream) {
@@ -337,6 +391,142 @@ hipError_t launch_topk_kl(const FinalArgs &a, hipStream_t stream) {
     hipLaunchKernelGGL((k_topk_kl<4>), grid, dim3(kWave), 0, stream, a);
   else
     hipLaunchKernelGGL((k_topk_kl<16>), grid, dim3(kWave), 0, stream, a);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------- exact buckets
+
+// The rows listed by k_topk_kl are cut into blocks of kFixCols columns, one
+// 256-thread block each (a strided loop over the list, whose length every
+// block reads the same way).  A block loads its 16 columns per thread at
+// once, drops the head columns, and sums 2^(x*kL2E - max) on each side
+// against the block's maxima.  The block that finishes a row last (a counter
+// per row, after a fence) merges the row's blocks in column order and
+// completes the top-k KL: sum_S p_i (delta_i + L) + p_o (ln(s_o / w_o) + L),
+// the last logarithm brought to natural units.
+constexpr int kFixBlock = 256;
+constexpr int kFixPer = kFixCols / kFixBlock;
+
+__device__ __forceinline__ float fix_load(const void *p, int t, int64_t off) {
+  if (t == 1) return __uint_as_float((uint32_t)((const uint16_t *)p)[off] << 16);
+  return ((const float *)p)[off];
+}
+
+__global__ __launch_bounds__(kFixBlock) void k_bucket_fix(FixArgs f) {
+  constexpr int kW = kFixBlock / kWave;
+  __shared__ int32_t head[kMaxK];  // ascending
+  __shared__ float red_f[2][kW];
+  __shared__ double red_d[2][kW];
+  __shared__ int s_last;
+  const int tid = threadIdx.x, lane = lane_id(), wid = tid / kWave;
+  const int64_t items = (int64_t)(*f.fix_count) * f.ncb;
+  for (int64_t it = blockIdx.x; it < items; it += gridDim.x) {
+    const int64_t e = it / f.ncb;
+    const int cb = (int)(it - e * f.ncb);
+    const FixEntry fe = f.fix[e];
+    const int keff = fe.keff;
+    if (wid == 0) {  // order the head indices: lane j ranks its index
+      const int hj = lane < keff ? f.fix_head[e * f.k + lane] : 0x7fffffff;
+      int rank = 0;
+      for (int i = 0; i < keff; ++i) rank += __shfl(hj, i, kWave) < hj ? 1 : 0;
+      if (lane < keff) head[rank] = hj;
+    }
+    __syncthreads();
+    // this thread's columns c0 + tid + 256 j ascend with j, and so does its
+    // position in the sorted head
+    const int64_t c0 = (int64_t)cb * kFixCols + tid;
+    const int64_t ra = fe.row * f.ldb, rb = fe.row * f.ldc;
+    float xa[kFixPer], xb[kFixPer];
+#pragma unroll
+    for (int j = 0; j < kFixPer; ++j) {
+      const int64_t c = c0 + (int64_t)j * kFixBlock;
+      xa[j] = c < f.v ? fix_load(f.base, f.tb, ra + c) : -INFINITY;
+      xb[j] = c < f.v ? fix_load(f.cand, f.tc, rb + c) : -INFINITY;
+    }
+    float ma = -INFINITY, mb = -INFINITY;
+    int hp = 0;
+#pragma unroll
+    for (int j = 0; j < kFixPer; ++j) {
+      const int64_t c = c0 + (int64_t)j * kFixBlock;
+      while (hp < keff && head[hp] < c) ++hp;
+      if (hp < keff && head[hp] == c) xa[j] = xb[j] = -INFINITY;
+      ma = fmaxf(ma, xa[j]);
+      mb = fmaxf(mb, xb[j]);
+    }
+    ma = wave_max(ma);
+    mb = wave_max(mb);
+    if (lane == 0) {
+      red_f[0][wid] = ma;
+      red_f[1][wid] = mb;
+    }
+    __syncthreads();
+    ma = red_f[0][0];
+    mb = red_f[1][0];
+    for (int w = 1; w < kW; ++w) {
+      ma = fmaxf(ma, red_f[0][w]);
+      mb = fmaxf(mb, red_f[1][w]);
+    }
+    const float ra2 = ma * kL2E, rb2 = mb * kL2E;  // every term below is at most 1
+    double sa = 0.0, sb = 0.0;
+#pragma unroll
+    for (int j = 0; j < kFixPer; ++j) {
+      if (xa[j] > -INFINITY) sa += (double)__builtin_amdgcn_exp2f(fmaf(xa[j], kL2E, -ra2));
+      if (xb[j] > -INFINITY) sb += (double)__builtin_amdgcn_exp2f(fmaf(xb[j], kL2E, -rb2));
+    }
+    sa = wave_sum(sa);
+    sb = wave_sum(sb);
+    if (lane == 0) {
+      red_d[0][wid] = sa;
+      red_d[1][wid] = sb;
+    }
+    __syncthreads();
+    if (tid == 0) {
+      sa = red_d[0][0];
+      sb = red_d[1][0];
+      for (int w = 1; w < kW; ++w) {
+        sa += red_d[0][w];
+        sb += red_d[1][w];
+      }
+      FixPart pt;
+      pt.ra2 = ra2;
+      pt.rb2 = rb2;
+      pt.sa = sa;
+      pt.sb = sb;
+      f.part[e * f.ncb + cb] = pt;
+      __threadfence();
+      s_last = atomicAdd(&f.fix[e].done, 1u) == (uint32_t)(f.ncb - 1);
+    }
+    __syncthreads();
+    if (s_last && tid == 0) {
+      __threadfence();
+      // the row's blocks in column order, against the largest maxima
+      double Ma = -INFINITY, Mb = -INFINITY;
+      for (int q = 0; q < f.ncb; ++q) {
+        const FixPart pq = f.part[e * f.ncb + q];
+        if (pq.sa > 0.0) Ma = fmax(Ma, (double)pq.ra2);
+        if (pq.sb > 0.0) Mb = fmax(Mb, (double)pq.rb2);
+      }
+      double Sa = 0.0, Sb = 0.0;
+      for (int q = 0; q < f.ncb; ++q) {
+        const FixPart pq = f.part[e * f.ncb + q];
+        if (pq.sa > 0.0) Sa += pq.sa * exp2((double)pq.ra2 - Ma);
+        if (pq.sb > 0.0) Sb += pq.sb * exp2((double)pq.rb2 - Mb);
+      }
+      // s_o = Sa 2^(Ma - m2) and w_o = Sb 2^(Mb - m2) against the row reference
+      const double units = 1.0 / ((double)kL2E * kLn2);
+      const double p_o = Sa * exp2(Ma - fe.m2) / fe.s;
+      const double lr = log(Sa) - log(Sb) + (Ma - Mb) * kLn2;
+      if (f.kl_topk) f.kl_topk[fe.row] = fe.head + p_o * (lr * units + fe.l);
+    }
+    __syncthreads();  // head[], the partials and s_last are reused
+  }
+}
+
+hipError_t launch_bucket_fix(const FixArgs &a, int64_t max_rows, hipStream_t stream) {
+  if (max_rows == 0) return hipSuccess;
+  const int64_t most = max_rows * a.ncb;
+  const unsigned blocks = (unsigned)(most < 1024 ? most : 1024);
+  hipLaunchKernelGGL(k_bucket_fix, dim3(blocks), dim3(kFixBlock), 0, stream, a);
   return hipGetLastError();
 }
 

@@ -114,6 +114,105 @@ def test_special_values_and_flags():
     assert_bitdiff_equal(g["bitdiff"], oracle.bitdiff(a, b))
 
 
+def test_reference_moves_within_a_chunk():
+    """Rows whose maximum keeps growing move the exp2 reference again and again
+    inside one chunk (by exact powers of two below 2^28 in log2 units), cross
+    into the range where the reference needs a second float, or start far
+    below zero and then jump up; the sums must follow the oracle."""
+    _case("reference moves")
+    rng = np.random.default_rng(12)
+    v = 20000
+    j = np.arange(v)
+    a = np.zeros((7, v), np.float32)
+    a[0] = -1000.0 + 0.1 * j + 0.5 * rng.standard_normal(v)       # a move nearly every step
+    a[1] = 1e6 * 1000.0 ** (j / v)                                 # 1e6 .. 1e9, crosses 2^28 / log2e
+    a[2] = rng.standard_normal(v)
+    a[2, [1000, 5000, 9000, 15000, 19000]] = [50.0, 100.0, 200.0, 400.0, 380.0]
+    a[3] = -1e9 + 100.0 * rng.standard_normal(v)                   # far below zero, then a jump
+    a[3, 12345] = 5.0
+    a[4] = 1000.0 - 0.1 * j                                        # descending: one move only
+    a[5] = rng.uniform(-1e9, 1e9, v)
+    a[6] = -1000.0 + 0.1 * j + 0.5 * rng.standard_normal(v)
+    b = (a + 0.01 * rng.standard_normal(a.shape)).astype(np.float32)
+    b[1] = a[1]
+    flip = rng.random(v) < 0.01
+    b[1, flip] = np.nextafter(a[1, flip], np.float32(np.inf))
+    b[3, 12345] = 5.05
+    b[5] = a[5]
+    b[6, -1] = a[6, -1] + 40.0                                     # the candidate's max outgrows the baseline's
+    g = gpu_compare(a, b, k=20, with_bitdiff=True)
+    assert_compare_equal(g, oracle.compare(a, b, k=20))
+    assert_bitdiff_equal(g["bitdiff"], oracle.bitdiff(a, b))
+
+
+def test_far_apart_normalisers():
+    """Candidates whose normaliser is far from the baseline's: a uniform shift
+    (the same distribution, KL 0) up or down by 40, a spike far above the
+    baseline's maximum, and a candidate far below it except on a few tokens."""
+    _case("far-apart normalisers")
+    rng = np.random.default_rng(13)
+    v = 30011
+    a = (1.5 * rng.standard_normal((8, v))).astype(np.float32)
+    a[:, 7] += 9.0
+    b = (a + 0.01 * rng.standard_normal(a.shape)).astype(np.float32)
+    b[0] = a[0] + 40.0                       # shift up: same softmax up to rounding of b
+    b[1] = a[1] - 40.0                       # shift down
+    b[2] = a[2] + 0.5                        # moderate shift
+    b[3, 123] = a[3].max() + 40.0            # spike on a token outside the baseline's head
+    b[4, 7] = a[4, 7] + 40.0                 # spike on the baseline's top token
+    b[5] = a[5] - 60.0                       # far below, except on a few tokens
+    b[5, [3, 99, 2000]] = a[5, [3, 99, 2000]]
+    b[6] = a[6] + 25.0 * rng.standard_normal(v).astype(np.float32)   # unrelated candidate
+    b[7] = -a[7]                             # reversed
+    g = gpu_compare(a, b, k=20, with_bitdiff=True)
+    o = oracle.compare(a, b, k=20)
+    assert_compare_equal(g, o)
+
+
+@pytest.mark.parametrize("tb,tc", [("f32", "f32"), ("bf16", "bf16"), ("f32", "bf16")])
+def test_candidate_bucket_far_below(tb, tc):
+    """The candidate keeps the baseline's top-20 and pushes everything else far
+    down, so its "other" bucket is a tiny fraction of the baseline's, with the
+    normalisers close (rows 0, 1) or far apart (rows 2, 3); rows 4 and 5 put a
+    large spike inside the head.  The bucket masses are summed again exactly
+    for such rows; strided rows exercise that pass's addressing."""
+    import torch
+    import logit_distribution_diffing_amd as L
+    _case(f"bucket far below {tb}/{tc}")
+    rng = np.random.default_rng(14)
+    n, v, ld = 6, 20011, 20032
+    a = (1.5 * rng.standard_normal((n, ld))).astype(np.float32)
+    a[:, 100:120] += 6.0                      # a clear head
+    b = (a + 0.01 * rng.standard_normal(a.shape)).astype(np.float32)
+    rest = np.ones(ld, bool)
+    rest[100:120] = False
+    a[0:2, 100:120] += 2.0                    # baseline bucket share about 1/4
+    b[0:2, 100:120] += 2.0
+    b[0, rest] -= 20.0
+    b[1, rest] -= 60.0
+    a[2, 100:120] -= 6.0                      # baseline mass mostly outside the head
+    b[2, rest] = a[2, rest] - 30.0
+    b[3, rest] = a[3, rest] - 80.0
+    b[3, 100:120] += 10.0
+    b[4, 105] += 45.0
+    b[5, 100:120] += 35.0
+
+    def conv(t, arr):
+        if t == "f32":
+            return arr
+        return torch.from_numpy(arr).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+
+    def side(t, arr):
+        x = torch.from_numpy(arr)
+        return x.cuda() if t == "f32" else x.view(torch.int16).view(torch.bfloat16).cuda()
+
+    ca, cb = conv(tb, a), conv(tc, b)
+    o = oracle.compare(np.ascontiguousarray(ca[:, :v]), np.ascontiguousarray(cb[:, :v]), k=20)
+    out = L.lcmp_compare_logits(side(tb, ca), side(tc, cb), k=20, v=v)
+    g = {kk: vv.cpu().numpy() for kk, vv in out.items()}
+    assert_compare_equal(g, o)
+
+
 def test_identical_inputs_exact_zero():
     _case("identical")
     a, _ = synth.tiny(synth.SEED_BASE, 0, 16, 1024)

@@ -27,6 +27,9 @@ def _inputs(seed, n, v):
     b = (a + 0.03 * rng.standard_normal((n, v))).astype(np.float32)
     c = (int(np.argmax(a[3])) + 1) % v
     b[3, c] = a[3].max() + 1.0                       # one constructed flip
+    b[5] = a[5] - 30.0                               # far-apart normalisers: the
+    b[6, :] -= 40.0                                  # bucket pass has rows to redo
+    b[6, np.argsort(a[6])[-20:]] += 40.0
     return a, b
 
 
