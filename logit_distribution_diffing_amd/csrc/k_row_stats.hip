@@ -46,11 +46,13 @@ constexpr int kTauOpen = 0x7fffffff;
 constexpr int kTauLaneMax = 0x7ffffffe;  // same, after the lane-maxima bound was taken
 
 struct WaveState {
-  // softmax sums (per lane, double across 8-element runs) and the candidate's
-  // mass w = sum 2^(b*log2e - r2): on the fast path each run adds s - d + f
-  // (every term e * e^-delta with |delta| <= 1/8, no cancellation), on the
-  // exact path each candidate weight is formed in double
-  double s, d, f, w;
+  // softmax sums of the fast path (per lane, double across 8-element runs)
+  double s, d, f;
+  // the same sums of the exact path, and there also the candidate's mass
+  // wx = sum 2^(b*log2e - r2), each weight formed in double.  The candidate's
+  // mass of the fast path is s - d + f (every term e * e^-delta with
+  // |delta| <= 1/8, no cancellation), formed once per chunk.
+  double sx, dx, fx, wx;
   // uniform exp2 reference r2h + r2l: r2l is 0 unless the logits are so large
   // (|r2h| >= 2^28) that one float cannot hold the reference within a unit;
   // such chunks take the exact path throughout
@@ -65,14 +67,14 @@ struct WaveState {
   // top-k threshold key (uniform) and buffer fill
   float tau_a;
   int tau_i, cnt;
-  // counters (per lane)
+  // counters (uniform: ballot counts over the exact path)
   int n_bad, n_ainf, n_binf, n_qzero;
   // bitwise statistics
   int ndiff, first;  // uniform (a chunk holds fewer than 2^31 elements)
   uint32_t max_ulp;
   float max_abs;
   double max_abs_d, sab, ssd, ssb;
-  int nfa, nfb;
+  int nfa, nfb;  // uniform, as the counters above
 };
 
 __device__ __forceinline__ void wave_fence() {
@@ -403,7 +405,10 @@ __device__ __forceinline__ void rescale(WaveState &st, float gm) {
   st.s *= sc;
   st.d *= sc;
   st.f *= sc;
-  st.w *= sc;
+  st.sx *= sc;
+  st.dx *= sc;
+  st.fx *= sc;
+  st.wx *= sc;
   st.r2h = nh;
   st.nr2h = -nh;
   st.r2l = nl;
@@ -462,14 +467,19 @@ __device__ __forceinline__ void process_step(const uint32_t (&ua)[8], const uint
     // the exact path only, are formed in double.  Before the chunk's first
     // finite baseline logit the candidate sets the reference, which then
     // moves to the baseline, down if need be.
+    // (one call site: the sums stay in place on the common path)
+    bool need;
+    float gsel = ga;
     if (st.seen) {
-      if (ballot(ga > st.gate)) rescale(st, ga);
+      need = ballot(ga > st.gate) != 0;
     } else if (ballot(ga > -INFINITY)) {
-      rescale(st, ga);
+      need = true;
       st.seen = 1;
-    } else if (ballot(gb > st.gate)) {
-      rescale(st, gb);
+    } else {
+      need = ballot(gb > st.gate) != 0;
+      gsel = gb;
     }
+    if (need) rescale(st, gsel);
   }
 
   // fast path: every element finite, |delta| <= 1/8
@@ -520,6 +530,11 @@ __device__ __forceinline__ void process_step(const uint32_t (&ua)[8], const uint
     ok = ok && isfinite(sab + ssd + ssb);
 
   if (ok) {
+    if (CMP) {
+      st.s += (double)sg;
+      st.d += (double)dg;
+      st.f += (double)fg;
+    }
     if (BITS) {
       st.sab += (double)sab;
       st.ssd += (double)ssd;
@@ -530,22 +545,22 @@ __device__ __forceinline__ void process_step(const uint32_t (&ua)[8], const uint
 #pragma unroll
       for (int j = 0; j < 8; ++j) st.max_ulp = max(st.max_ulp, ulp_close<W16>(ua[j], ub[j]));
     }
-  } else {
-    if (CMP && BITS) {
+  }
+  // exact element-by-element path for the lanes that are not ok: special
+  // values, large differences, huge logits, ragged tails.  The branch is
+  // taken by the whole wave (the lanes that are ok do nothing), so the
+  // counters stay wave-uniform: ballots over the lanes at work.  The weights
+  // are formed in double, where neither side under- or overflows.
+  if (ballot(!ok)) {
+    if (CMP && BITS && !ok) {
 #pragma unroll
       for (int j = 0; j < 8; ++j) st.max_ulp = max(st.max_ulp, ulp_exact<W16>(ua[j], ub[j]));
     }
-    // exact element-by-element path: special values, large differences,
-    // huge logits, ragged tails.  The fast sums of this lane are dropped; the
-    // weights are formed in double, where neither side under- or overflows.
-    sg = dg = fg = 0.0f;
-    double s2 = 0.0, d2 = 0.0, f2 = 0.0, w2 = 0.0;
     const double r2d = (double)st.r2h + (double)st.r2l;
     // one element per trip (j is uniform): the double exponentials appear
     // once in the code rather than once per element
 #pragma unroll 1
     for (int j = 0; j < 8; ++j) {
-      if (!((valid >> j) & 1u)) continue;
       float a = xa[0], b = xb[0];
 #pragma unroll
       for (int t = 1; t < 8; ++t) {
@@ -554,11 +569,12 @@ __device__ __forceinline__ void process_step(const uint32_t (&ua)[8], const uint
           b = xb[t];
         }
       }
+      const bool act = !ok && ((valid >> j) & 1u);
       const bool fa = isfinite(a), fb = isfinite(b);
       if (BITS) {
-        st.nfa += fa ? 0 : 1;
-        st.nfb += fb ? 0 : 1;
-        if (fa && fb) {
+        st.nfa += __popcll(ballot(act && !fa));
+        st.nfb += __popcll(ballot(act && !fb));
+        if (act && fa && fb) {
           const double dd = (double)a - (double)b;
           st.sab += fabs(dd);
           st.ssd += dd * dd;
@@ -567,52 +583,39 @@ __device__ __forceinline__ void process_step(const uint32_t (&ua)[8], const uint
         }
       }
       if (CMP) {
-        if (isnan(a) || isnan(b) || a == INFINITY || b == INFINITY) {
-          st.n_bad++;
-          continue;
-        }
-        if (a == -INFINITY) {
-          st.n_ainf++;
-          if (b == -INFINITY) {
-            st.n_binf++;
-          } else {  // q mass where p = 0
-            const double eb = exp2_d((double)b * (double)kL2E - r2d);
-            f2 += eb;
-            w2 += eb;
+        const bool bad = act && (isnan(a) || isnan(b) || a == INFINITY || b == INFINITY);
+        const bool ainf = act && !bad && a == -INFINITY;
+        const bool binf = act && !bad && b == -INFINITY;
+        st.n_bad += __popcll(ballot(bad));
+        st.n_ainf += __popcll(ballot(ainf));
+        st.n_binf += __popcll(ballot(binf));
+        st.n_qzero += __popcll(ballot(binf && !ainf));  // p > 0, q = 0: the full KL is infinite
+        if (act && !bad) {
+          if (ainf) {
+            if (!binf) {  // q mass where p = 0
+              const double eb = exp2_d((double)b * (double)kL2E - r2d);
+              st.fx += eb;
+              st.wx += eb;
+            }
+          } else {
+            const double e = exp2_d((double)a * (double)kL2E - r2d);
+            st.sx += e;
+            if (binf) {
+              st.fx -= e;
+            } else {
+              const double dj = (double)a - (double)b;  // exact
+              const double eb = exp2_d((double)b * (double)kL2E - r2d);
+              st.dx += e * dj;
+              st.wx += eb;
+              if (fabs(dj) <= (double)kPolyMax)
+                st.fx += e * phi_d(dj);
+              else  // e*phi = e*(delta - 1) + 2^(b*log2e - r2)
+                st.fx += fma(e, dj - 1.0, eb);
+            }
           }
-          continue;
         }
-        const double e = exp2_d((double)a * (double)kL2E - r2d);
-        s2 += e;
-        if (b == -INFINITY) {  // p > 0, q = 0: the full KL is infinite
-          st.n_binf++;
-          st.n_qzero++;
-          f2 -= e;
-          continue;
-        }
-        const double dj = (double)a - (double)b;  // exact
-        const double eb = exp2_d((double)b * (double)kL2E - r2d);
-        d2 += e * dj;
-        w2 += eb;
-        if (fabs(dj) <= (double)kPolyMax)
-          f2 += e * phi_d(dj);
-        else  // e*phi = e*(delta - 1) + 2^(b*log2e - r2)
-          f2 += fma(e, dj - 1.0, eb);
       }
     }
-    if (CMP) {
-      st.s += s2;
-      st.d += d2;
-      st.f += f2;
-      st.w += w2;
-    }
-  }
-  if (CMP) {
-    const double sd = sg, dd = dg, fd = fg;
-    st.s += sd;
-    st.d += dd;
-    st.f += fd;
-    st.w += (sd - dd) + fd;
   }
 
   if (CMP) {
@@ -726,7 +729,7 @@ __attribute__((amdgpu_waves_per_eu(4, 8))) void k_row_stats(StreamArgs args) {
 
   WaveState st;
   st.s = st.d = st.f = 0.0;
-  st.w = 0.0;
+  st.sx = st.dx = st.fx = st.wx = 0.0;
   st.r2h = -INFINITY;
   st.nr2h = INFINITY;
   st.r2l = 0.0f;
@@ -851,10 +854,10 @@ __attribute__((amdgpu_waves_per_eu(4, 8))) void k_row_stats(StreamArgs args) {
       late.ta[tk + lane] = ba[lane];
       late.ti[tk + lane] = bi[lane];
     }
-    const double S = wave_sum(st.s), D = wave_sum(st.d), F = wave_sum(st.f);
-    const double Wc = wave_sum(st.w);
-    const int nb = wave_sum(st.n_bad), na = wave_sum(st.n_ainf), nbi = wave_sum(st.n_binf),
-              nq = wave_sum(st.n_qzero);
+    const double S = wave_sum(st.s + st.sx), D = wave_sum(st.d + st.dx),
+                 F = wave_sum(st.f + st.fx);
+    const double Wc = wave_sum(((st.s - st.d) + st.f) + st.wx);
+    const int nb = st.n_bad, na = st.n_ainf, nbi = st.n_binf, nq = st.n_qzero;
     if (lane == 0) {
       ChunkStats cs;
       cs.s = S;
@@ -875,7 +878,7 @@ __attribute__((amdgpu_waves_per_eu(4, 8))) void k_row_stats(StreamArgs args) {
   }
   if (BITS) {
     const double sab = wave_sum(st.sab), ssd = wave_sum(st.ssd), ssb = wave_sum(st.ssb);
-    const int nfa = wave_sum(st.nfa), nfb = wave_sum(st.nfb);
+    const int nfa = st.nfa, nfb = st.nfb;
     const uint32_t mu = wave_max(st.max_ulp) >> (W16 ? 16 : 0);
     const double ma = wave_max(fmax((double)st.max_abs, st.max_abs_d));
     if (lane == 0) {

@@ -332,7 +332,12 @@ __global__ __launch_bounds__(kWave) void k_topk_kl(FinalArgs a) {
               klk += p_o * (log(s_o / w_o) * units + L);
             }
             if (ill && a.fix && a.kl_topk) {
-              fix_slot = (int)atomicAdd(a.fix_count, 1u);
+              const uint32_t slot = atomicAdd(a.fix_count, 1u);
+              // the streaming pass cleared the count, so at most n rows
+              // arrive; a slot past n is dropped rather than written
+              fix_slot = (int64_t)slot < a.n ? (int)slot : -1;
+            }
+            if (fix_slot >= 0) {
               FixEntry fe;
               fe.row = row;
               fe.m2 = M2;
@@ -419,11 +424,16 @@ __global__ __launch_bounds__(kFixBlock) void k_bucket_fix(FixArgs f) {
   __shared__ double red_d[2][kW];
   __shared__ int s_last;
   const int tid = threadIdx.x, lane = lane_id(), wid = tid / kWave;
-  const int64_t items = (int64_t)(*f.fix_count) * f.ncb;
+  // the list never holds more than n rows; an entry that does not name a row
+  // of the call, or a head larger than k, is skipped (every block reads the
+  // same bounds, so the loop and its barriers stay uniform)
+  const int64_t count = min((int64_t)(*f.fix_count), f.n);
+  const int64_t items = count * f.ncb;
   for (int64_t it = blockIdx.x; it < items; it += gridDim.x) {
     const int64_t e = it / f.ncb;
     const int cb = (int)(it - e * f.ncb);
     const FixEntry fe = f.fix[e];
+    if (fe.row < 0 || fe.row >= f.n || fe.keff < 1 || fe.keff > f.k) continue;
     const int keff = fe.keff;
     if (wid == 0) {  // order the head indices: lane j ranks its index
       const int hj = lane < keff ? f.fix_head[e * f.k + lane] : 0x7fffffff;

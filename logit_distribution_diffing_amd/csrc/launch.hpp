@@ -78,6 +78,7 @@ struct FixArgs {
   const uint32_t *fix_count;
   FixPart *part;  // [n * ncb]
   int32_t ncb;    // column blocks per row
+  int64_t n;      // rows of the call: the list holds at most n entries
   const void *base, *cand;
   int32_t tb, tc;
   int64_t ldb, ldc;

@@ -267,6 +267,7 @@ static int compare_impl(const void *base, int tb, int64_t ld_base, const void *c
     xa.fix_count = fa.fix_count;
     xa.part = (FixPart *)(ws + L.off_fix_part);
     xa.ncb = L.fix_ncb;
+    xa.n = n;
     xa.base = base;
     xa.cand = cand;
     xa.tb = tb;
