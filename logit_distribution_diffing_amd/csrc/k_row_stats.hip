@@ -26,6 +26,7 @@
 #include "dma.hpp"
 #include "launch.hpp"
 
+#include <float.h>
 #include <math.h>
 
 namespace lcmp {
@@ -482,10 +483,20 @@ __device__ __forceinline__ void process_step(const uint32_t (&ua)[8], const uint
     if (need) rescale(st, gsel);
   }
 
-  // fast path: every element finite, |delta| <= 1/8
+  // fast path: every element finite, |delta| <= 1/8.  In the ragged last
+  // step the columns past the end enter it as a neutral pair: equal values
+  // of zero weight (-FLT_MAX, whose exp2 is 0) and no square.
+  float ya[8], yb[8], sq[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const bool vj = !tail || ((valid >> j) & 1u);
+    ya[j] = vj ? xa[j] : -FLT_MAX;
+    yb[j] = vj ? xb[j] : -FLT_MAX;
+    sq[j] = vj ? xa[j] : 0.0f;
+  }
   float d[8];
 #pragma unroll
-  for (int j = 0; j < 8; ++j) d[j] = xa[j] - xb[j];
+  for (int j = 0; j < 8; ++j) d[j] = ya[j] - yb[j];
   const float dmax = max8abs(d);
   float sg = 0.0f, dg = 0.0f, fg = 0.0f;
   float sab = 0.0f, ssd = 0.0f, ssb = 0.0f;
@@ -493,13 +504,13 @@ __device__ __forceinline__ void process_step(const uint32_t (&ua)[8], const uint
     // e*phi(delta) = (e*delta^2) * P(delta), P(d) = 1/2 - d/6 + d^2/24; the
     // dropped d^3/120 term is below 3.3e-5 of P for |d| <= 1/8.  One
     // accumulator per sum: four waves per SIMD hide the chain latency.
-    float e = __builtin_amdgcn_exp2f(fmaf(xa[0], kL2E, st.nr2h));
+    float e = __builtin_amdgcn_exp2f(fmaf(ya[0], kL2E, st.nr2h));
     sg = e;
     dg = e * d[0];
     fg = e * ((d[0] * d[0]) * fmaf(d[0], fmaf(d[0], 1.0f / 24.0f, -1.0f / 6.0f), 0.5f));
 #pragma unroll
     for (int j = 1; j < 8; ++j) {
-      e = __builtin_amdgcn_exp2f(fmaf(xa[j], kL2E, st.nr2h));
+      e = __builtin_amdgcn_exp2f(fmaf(ya[j], kL2E, st.nr2h));
       const float q = (d[j] * d[j]) * fmaf(d[j], fmaf(d[j], 1.0f / 24.0f, -1.0f / 6.0f), 0.5f);
       sg += e;
       dg = fmaf(e, d[j], dg);
@@ -509,19 +520,19 @@ __device__ __forceinline__ void process_step(const uint32_t (&ua)[8], const uint
   if (BITS) {
     sab = fabsf(d[0]);
     ssd = d[0] * d[0];
-    ssb = xa[0] * xa[0];
+    ssb = sq[0] * sq[0];
 #pragma unroll
     for (int j = 1; j < 8; ++j) {
       sab += fabsf(d[j]);
       ssd += d[j] * d[j];
-      ssb = fmaf(xa[j], xa[j], ssb);
+      ssb = fmaf(sq[j], sq[j], ssb);
     }
   }
   // Every special value reaches a NaN or an infinity in the checked sums:
   // with the comparison, a NaN or inf on either side makes delta NaN or
   // infinite (sab, or dg alone), a huge baseline makes sum a^2 infinite, and
   // |delta| <= 1/8 bounds sum delta^2.
-  bool ok = !tail;
+  bool ok = true;
   if (CMP && BITS)
     ok = ok && !st.huge && (dmax <= kPolyMax) && isfinite(sab + ssb);
   else if (CMP)
