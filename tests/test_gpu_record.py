@@ -216,6 +216,35 @@ def test_adversarial_rows():
     assert np.isfinite(grec["lse_rest"].cpu().numpy()[2])
 
 
+def test_far_apart_normalisers_against_a_record():
+    """The candidate rows of the full compare's far-apart test against a
+    stored baseline: shifts of +-40 (KL 0), spikes outside and on the head, a
+    candidate far below except on a few tokens, the head kept while the rest
+    drops by 20 or 60 nats, an unrelated and a reversed candidate."""
+    _case("record far-apart normalisers")
+    rng = np.random.default_rng(13)
+    v = 30011
+    a = (1.5 * rng.standard_normal((10, v))).astype(np.float32)
+    a[:, 7] += 9.0
+    a[8:10, 100:120] += 8.0
+    b = (a + 0.01 * rng.standard_normal(a.shape)).astype(np.float32)
+    b[0] = a[0] + 40.0
+    b[1] = a[1] - 40.0
+    b[2] = a[2] + 0.5
+    b[3, 123] = a[3].max() + 40.0
+    b[4, 7] = a[4, 7] + 40.0
+    b[5] = a[5] - 60.0
+    b[5, [3, 99, 2000]] = a[5, [3, 99, 2000]]
+    b[6] = a[6] + 25.0 * rng.standard_normal(v).astype(np.float32)
+    b[7] = -a[7]
+    rest = np.ones(v, bool)
+    rest[100:120] = False
+    b[8, rest] -= 20.0
+    b[9, rest] -= 60.0
+    check_both(a, b, 20, 20)
+    check_both(a, b, 5, 20)
+
+
 def test_record_compare_matches_full_compare_on_corpus_rows():
     """2048 corpus rows (fp32 baseline, bf16 candidate): the record path gives
     the full compare's indices, flips and margins bit for bit, and its top-k KL
