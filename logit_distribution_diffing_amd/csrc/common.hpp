@@ -135,6 +135,37 @@ __device__ __forceinline__ T wave_reduce(T x, Op op) {
   return op(op(B::lane(x, 0), B::lane(x, 16)), op(B::lane(x, 32), B::lane(x, 48)));
 }
 
+// The same combine over lanes 0 .. n-1 only (n uniform, 1 <= n <= 64): with
+// few lanes (the chunks of a row) a chain of lane reads in lane order is
+// cheaper than the full exchange; either way the order is fixed.
+template <typename T, typename Op>
+__device__ __forceinline__ T lanes_reduce(T x, int n, Op op) {
+  if (n > 8) return wave_reduce(x, op);
+  using B = Bits32<T>;
+  T r = B::lane(x, 0);
+  for (int l = 1; l < n; ++l) r = op(r, B::lane(x, l));
+  return r;
+}
+template <typename T>
+__device__ __forceinline__ T lanes_sum(T x, int n) {
+  return lanes_reduce(x, n, [](T a, T b) { return a + b; });
+}
+__device__ __forceinline__ double lanes_max(double x, int n) {
+  return lanes_reduce(x, n, [](double a, double b) { return fmax(a, b); });
+}
+__device__ __forceinline__ float lanes_max(float x, int n) {
+  return lanes_reduce(x, n, [](float a, float b) { return fmaxf(a, b); });
+}
+__device__ __forceinline__ uint32_t lanes_max(uint32_t x, int n) {
+  return lanes_reduce(x, n, [](uint32_t a, uint32_t b) { return a > b ? a : b; });
+}
+__device__ __forceinline__ int lanes_min(int x, int n) {
+  return lanes_reduce(x, n, [](int a, int b) { return a < b ? a : b; });
+}
+__device__ __forceinline__ int64_t lanes_min(int64_t x, int n) {
+  return lanes_reduce(x, n, [](int64_t a, int64_t b) { return a < b ? a : b; });
+}
+
 __device__ __forceinline__ double wave_sum(double x) {
   return wave_reduce(x, [](double a, double b) { return a + b; });
 }

@@ -85,12 +85,13 @@ __global__ __launch_bounds__(kWave) void k_topk_kl(FinalArgs a) {
   }
 
   if (a.bd) {
-    const int64_t ndiff = wave_sum(cb.ndiff);
-    const int64_t first = wave_min(cb.first >= 0 ? cb.first : INT64_MAX);
-    const int64_t nfa = wave_sum(cb.nfa), nfb = wave_sum(cb.nfb);
-    const uint32_t mu = wave_max(cb.max_ulp);
-    const double ma = wave_max(cb.max_abs);
-    const double sab = wave_sum(cb.sum_abs), ssd = wave_sum(cb.ssd), ssb = wave_sum(cb.ssb);
+    const int64_t ndiff = lanes_sum(cb.ndiff, C);
+    const int64_t first = lanes_min(cb.first >= 0 ? cb.first : INT64_MAX, C);
+    const int64_t nfa = lanes_sum(cb.nfa, C), nfb = lanes_sum(cb.nfb, C);
+    const uint32_t mu = lanes_max(cb.max_ulp, C);
+    const double ma = lanes_max(cb.max_abs, C);
+    const double sab = lanes_sum(cb.sum_abs, C), ssd = lanes_sum(cb.ssd, C),
+                 ssb = lanes_sum(cb.ssb, C);
     if (lane == 0) {
       BitdiffRow r;
       r.ndiff = ndiff;
@@ -111,11 +112,11 @@ __global__ __launch_bounds__(kWave) void k_topk_kl(FinalArgs a) {
 
   // ---- chunk sums, rescaled to the largest reference
   const double r2 = has ? cs.r2 : -INFINITY;
-  const double M2 = wave_max(r2);
-  const int nb = wave_sum(has ? cs.n_bad : 0);
-  const int na = wave_sum(has ? cs.n_ainf : 0);
-  const int nbi = wave_sum(has ? cs.n_binf : 0);
-  const int nq = wave_sum(has ? cs.n_qzero : 0);
+  const double M2 = lanes_max(r2, C);
+  const int nb = lanes_sum(has ? cs.n_bad : 0, C);
+  const int na = lanes_sum(has ? cs.n_ainf : 0, C);
+  const int nbi = lanes_sum(has ? cs.n_binf : 0, C);
+  const int nq = lanes_sum(has ? cs.n_qzero : 0, C);
   uint8_t status = 0;
   if (nb > 0)
     status = 1;  // LCMP_ROW_NONFINITE
@@ -143,15 +144,15 @@ __global__ __launch_bounds__(kWave) void k_topk_kl(FinalArgs a) {
     return;
   }
   const double sc = (has && r2 > -INFINITY) ? exp2(r2 - M2) : 0.0;
-  const double S = wave_sum(has ? cs.s * sc : 0.0);
-  const double D = wave_sum(has ? cs.d * sc : 0.0);
-  const double F = wave_sum(has ? cs.f * sc : 0.0);
-  const double W = wave_sum(has ? cs.w * sc : 0.0);
+  const double S = lanes_sum(has ? cs.s * sc : 0.0, C);
+  const double D = lanes_sum(has ? cs.d * sc : 0.0, C);
+  const double F = lanes_sum(has ? cs.f * sc : 0.0, C);
+  const double W = lanes_sum(has ? cs.w * sc : 0.0, C);
 
   // ---- candidate argmax across chunks: value descending, index ascending
   const float bm = has ? cs.bmax : -INFINITY;
-  const float BM = uniform(wave_max(bm));
-  const int bx = wave_min((has && cs.bidx >= 0 && bm == BM) ? cs.bidx : 0x7fffffff);
+  const float BM = uniform(lanes_max(bm, C));
+  const int bx = lanes_min((has && cs.bidx >= 0 && bm == BM) ? cs.bidx : 0x7fffffff, C);
   const int top1_cand = bx == 0x7fffffff ? -1 : bx;
 
   // ---- the row's top kint slots.  Slot e holds entry (e mod kint) of chunk
@@ -284,9 +285,9 @@ __global__ __launch_bounds__(kWave) void k_topk_kl(FinalArgs a) {
   if (in_head && !binf) eb = exp2((double)hb * (double)kL2E - M2);
   const double sum_e = wave_sum(e), sum_pphi = wave_sum(tphi), sum_pg = wave_sum(tg);
   const double sum_eb = wave_sum(eb), sum_pl = wave_sum(tpl);
-  const int n_sa = wave_sum((in_head && ainf) ? 1 : 0);
-  const int n_sb = wave_sum((in_head && binf) ? 1 : 0);
-  const int any_head_inf = wave_max(head_inf);
+  const int n_sa = __popcll(ballot(in_head && ainf));
+  const int n_sb = __popcll(ballot(in_head && binf));
+  const int any_head_inf = ballot(head_inf != 0) != 0;
 
   if (a.topk_idx)
     for (int j = lane; j < a.k; j += kWave) a.topk_idx[row * a.k + j] = j < keff ? s_i[j] : -1;
@@ -535,7 +536,8 @@ __global__ __launch_bounds__(kFixBlock) void k_bucket_fix(FixArgs f) {
 hipError_t launch_bucket_fix(const FixArgs &a, int64_t max_rows, hipStream_t stream) {
   if (max_rows == 0) return hipSuccess;
   const int64_t most = max_rows * a.ncb;
-  const unsigned blocks = (unsigned)(most < 1024 ? most : 1024);
+  // one block per CU loops over the list: an empty list costs one small launch
+  const unsigned blocks = (unsigned)(most < 256 ? most : 256);
   hipLaunchKernelGGL(k_bucket_fix, dim3(blocks), dim3(kFixBlock), 0, stream, a);
   return hipGetLastError();
 }

@@ -6,8 +6,8 @@
 namespace lcmp {
 
 // Combine the chunk records of one row into the public record.  The whole wave
-// calls it; lane c reads chunk c (nchunks <= 64).  Sums use the fixed-order
-// wave reduction, so the result is the same on every run.
+// calls it; lane c reads chunk c (1 <= nchunks <= 64).  Sums run over the
+// chunk lanes in a fixed order, so the result is the same on every run.
 __device__ __forceinline__ void merge_bits(const ChunkBits *cb, int nchunks, int64_t cols,
                                            BitdiffRow *out) {
   const int lane = lane_id();
@@ -23,12 +23,13 @@ __device__ __forceinline__ void merge_bits(const ChunkBits *cb, int nchunks, int
     c.max_abs = 0.0;
     c.sum_abs = c.ssd = c.ssb = 0.0;
   }
-  const int64_t ndiff = wave_sum(c.ndiff);
-  const int64_t first = wave_min(c.first >= 0 ? c.first : INT64_MAX);
-  const int64_t nfa = wave_sum(c.nfa), nfb = wave_sum(c.nfb);
-  const uint32_t mu = wave_max(c.max_ulp);
-  const double ma = wave_max(c.max_abs);
-  const double sab = wave_sum(c.sum_abs), ssd = wave_sum(c.ssd), ssb = wave_sum(c.ssb);
+  const int64_t ndiff = lanes_sum(c.ndiff, nchunks);
+  const int64_t first = lanes_min(c.first >= 0 ? c.first : INT64_MAX, nchunks);
+  const int64_t nfa = lanes_sum(c.nfa, nchunks), nfb = lanes_sum(c.nfb, nchunks);
+  const uint32_t mu = lanes_max(c.max_ulp, nchunks);
+  const double ma = lanes_max(c.max_abs, nchunks);
+  const double sab = lanes_sum(c.sum_abs, nchunks), ssd = lanes_sum(c.ssd, nchunks),
+               ssb = lanes_sum(c.ssb, nchunks);
   if (lane == 0) {
     BitdiffRow r;
     r.ndiff = ndiff;
