@@ -4,24 +4,27 @@
 // chunk exactly once from HBM.  Per element pair (a = baseline, b = candidate
 // logit) it keeps, against a wave-uniform exp2 reference r2:
 //   s = sum e,  d = sum e*delta,  f = sum e*phi(delta)
-// with e = 2^(a*log2e - r2), delta = a - b and phi(delta) = delta + expm1(-delta).
-// The finalize forms KL(P||Q) = f/s - psi(E/s), E = f - d, from these sums
-// (teacher-forced full-vocabulary KL of the page "在 agent 时代如何快速验证 kernel
-// 对精度的影响", section 怎么比两个分布).  Along the way it tracks the candidate
-// argmax and the baseline top-k candidates (threshold filter into an LDS
-// buffer, radix-select flushes), and optionally the bitwise statistics of the
-// pair (differing patterns, first differing column, ULP distance, error norms;
-// page "Kestrel_VLLM - 18", section 二, and page "海光 DCU 实测", sections 1 and 7).
+// with e = 2^(a*log2e - r2), delta = a - b and phi(delta) = delta + expm1(-delta),
+// and the candidate's mass w = sum 2^(b*log2e - r2).  The finalize forms
+// KL(P||Q) = f/s - psi(E/s), E = f - d, from these sums, or d/s + ln(w/s) when
+// the two normalisers are far apart (teacher-forced full-vocabulary KL of the
+// page "在 agent 时代如何快速验证 kernel 对精度的影响", section 怎么比两个分布).
+// Along the way it tracks the candidate argmax and the baseline top-k
+// candidates (threshold filter into an LDS buffer, radix-select flushes), and
+// optionally the bitwise statistics of the pair (differing patterns, first
+// differing column, ULP distance, error norms; page "Kestrel_VLLM - 18",
+// section 二, and page "海光 DCU 实测", sections 1 and 7).
 //
 // Element mapping inside one wave step of 512 elements: when either side is
 // fp32, lane l takes elements [4l, 4l+4) and [256+4l, 256+4l+4), so each load
 // instruction of the wave covers one contiguous run; when both sides are bf16,
 // lane l takes [8l, 8l+8) with one 16-byte load per side.
 //
-// Code shape: the per-step work is instantiated once for the streaming loop
-// and once for the ragged last step.  Rare work (moving the exp2 reference,
-// exact treatment of special values, top-k buffer flushes, argmax updates)
-// sits behind wave-uniform branches so the common step is straight-line code.
+// Code shape: the per-step work is inlined into the streaming loop (twice when
+// it alternates two register sets), its remainder and the ragged last step.
+// Rare work (moving the exp2 reference, the exact fp64 path for special values
+// and large differences, top-k buffer flushes, argmax updates) sits behind
+// wave-uniform branches so the common step is straight-line code.
 #include "common.hpp"
 #include "dma.hpp"
 #include "launch.hpp"
@@ -380,12 +383,13 @@ __device__ __forceinline__ double phi_d(double d) {
   return d * d * p;
 }
 
-// Move the exp2 reference when a logit outgrows it (rare after the first step).
-// The reference and the gate stay wave-uniform, in scalar registers.  Below
-// 2^28 (log2 units) the reference is an integer, so moving it scales the sums
-// by an exact power of two; above, it is the float product plus its rounding
-// residual, and the fractional part of the shift goes through exp2 in float
-// (relative error near 1e-7, common to the three sums).
+// Move the exp2 reference when a logit outgrows it (rare after the first step),
+// or onto the chunk's first finite baseline logits.  The reference and the
+// gate stay wave-uniform, in scalar registers.  Below 2^28 (log2 units) the
+// reference is an integer, so moving it scales the sums by an exact power of
+// two; above, it is the float product plus its rounding residual, and the
+// fractional part of the shift goes through exp2 in float (relative error
+// near 1e-7, common to all the sums).
 __device__ __forceinline__ void rescale(WaveState &st, float gm) {
   const float wm = uniform(wave_max(gm));
   const float xh = wm * kL2E;
