@@ -169,8 +169,9 @@ def test_far_apart_normalisers():
     assert_compare_equal(g, o)
 
 
-@pytest.mark.parametrize("tb,tc", [("f32", "f32"), ("bf16", "bf16"), ("f32", "bf16")])
-def test_candidate_bucket_far_below(tb, tc):
+@pytest.mark.parametrize("tb,tc,k", [("f32", "f32", 20), ("bf16", "bf16", 20), ("f32", "bf16", 20),
+                                     ("f32", "f32", 1), ("f32", "bf16", 64)])
+def test_candidate_bucket_far_below(tb, tc, k):
     """The candidate keeps the baseline's top-20 and pushes everything else far
     down, so its "other" bucket is a tiny fraction of the baseline's, with the
     normalisers close (rows 0, 1) or far apart (rows 2, 3); rows 4 and 5 put a
@@ -178,7 +179,7 @@ def test_candidate_bucket_far_below(tb, tc):
     for such rows; strided rows exercise that pass's addressing."""
     import torch
     import logit_distribution_diffing_amd as L
-    _case(f"bucket far below {tb}/{tc}")
+    _case(f"bucket far below {tb}/{tc} k={k}")
     rng = np.random.default_rng(14)
     n, v, ld = 6, 20011, 20032
     a = (1.5 * rng.standard_normal((n, ld))).astype(np.float32)
@@ -207,8 +208,8 @@ def test_candidate_bucket_far_below(tb, tc):
         return x.cuda() if t == "f32" else x.view(torch.int16).view(torch.bfloat16).cuda()
 
     ca, cb = conv(tb, a), conv(tc, b)
-    o = oracle.compare(np.ascontiguousarray(ca[:, :v]), np.ascontiguousarray(cb[:, :v]), k=20)
-    out = L.lcmp_compare_logits(side(tb, ca), side(tc, cb), k=20, v=v)
+    o = oracle.compare(np.ascontiguousarray(ca[:, :v]), np.ascontiguousarray(cb[:, :v]), k=k)
+    out = L.lcmp_compare_logits(side(tb, ca), side(tc, cb), k=k, v=v)
     g = {kk: vv.cpu().numpy() for kk, vv in out.items()}
     assert_compare_equal(g, o)
 
