@@ -12,7 +12,7 @@ import pytest
 
 import oracle
 import synth
-from helpers import assert_bitdiff_equal, assert_compare_equal, to_device
+from helpers import assert_bitdiff_equal, assert_compare_equal, gpu_compare, to_device
 
 pytestmark = pytest.mark.gpu
 
@@ -111,6 +111,30 @@ def test_segment_all_rows():
     for f in ("sum_kl_topk", "sum_kl_full"):
         tol = 1e-7 * gb["count"] + 1e-4 * ob[f]
         assert np.all(np.abs(gb[f] - ob[f]) <= tol), f
+
+
+def test_corpus_rows_with_extreme_candidates():
+    """64 corpus rows at V = 151936 (16 chunks per row) whose candidates are
+    replaced on some rows by extreme ones: a spike of 40 on the baseline's top
+    token or outside its head, the head kept and the rest pushed down by 30,
+    shifts of +-40.  Exercises the far-apart finalize and the bucket pass over
+    38 column blocks per row."""
+    w = synth.WORKLOADS["corpus"]
+    _case("corpus rows with extreme candidates 64x151936 f32/f32")
+    n, v = 64, w["v"]
+    a, b16 = synth.corpus(w["seed"], 0, n, v, w["n"], w["swap_frac"])
+    b = (b16.astype(np.uint32) << 16).view(np.float32).copy()
+    top = np.argsort(a, axis=1)[:, -20:]
+    b[3, top[3, -1]] += 40.0
+    keep = np.zeros(v, bool)
+    keep[top[17]] = True
+    b[17, ~keep] -= 30.0
+    b[40] -= 40.0
+    b[41] += 40.0
+    b[50, int(np.argmin(a[50]))] = a[50].max() + 40.0
+    g = gpu_compare(a, b, k=w["k"], with_bitdiff=True)
+    assert_compare_equal(g, oracle.compare(a, b, k=w["k"]))
+    assert_bitdiff_equal(g["bitdiff"], oracle.bitdiff(a, b))
 
 
 @pytest.fixture(scope="module")
