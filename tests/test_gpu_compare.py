@@ -169,6 +169,29 @@ def test_far_apart_normalisers():
     assert_compare_equal(g, o)
 
 
+def test_baseline_masked_where_candidate_is_large():
+    """Chunks that open with baseline -inf columns while the candidate is
+    finite and far above the baseline's later values: the exp2 reference is
+    first taken from the candidate and then moves down onto the baseline."""
+    _case("baseline masked at chunk starts")
+    rng = np.random.default_rng(15)
+    v = 20011
+    a = (1.5 * rng.standard_normal((4, v))).astype(np.float32)
+    b = (a + 0.01 * rng.standard_normal(a.shape)).astype(np.float32)
+    a[0, :1000] = -np.inf
+    b[0, :1000] = 50.0 + rng.standard_normal(1000).astype(np.float32)
+    a[1, :1000] = -np.inf
+    b[1, :1000] = -np.inf
+    a[2, 10240:11000] = -np.inf                 # the start of the second chunk
+    b[2, 10240:11000] = 80.0
+    a[3, :700] = -np.inf
+    b[3, :700] = 400.0                         # 2^577 above: fp64 candidate weights
+    g = gpu_compare(a, b, k=20, with_bitdiff=True)
+    o = oracle.compare(a, b, k=20)
+    assert_compare_equal(g, o)
+    assert_bitdiff_equal(g["bitdiff"], oracle.bitdiff(a, b))
+
+
 @pytest.mark.parametrize("tb,tc,k", [("f32", "f32", 20), ("bf16", "bf16", 20), ("f32", "bf16", 20),
                                      ("f32", "f32", 1), ("f32", "bf16", 64)])
 def test_candidate_bucket_far_below(tb, tc, k):
