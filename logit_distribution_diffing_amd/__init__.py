@@ -205,6 +205,8 @@ def _check_out(out: dict, n: int, k: int, allowed=None):
 
 
 def _check_workspace(ws):
+    """A caller's workspace is passed on as given: one that is too small comes
+    back from the library as LCMP_EWORKSPACE instead of being replaced here."""
     if ws is not None:
         _check_buffer(ws, torch.uint8, 0, "workspace")
 
@@ -262,7 +264,7 @@ def lcmp_compare_logits(base: torch.Tensor, cand: torch.Tensor, k: int = 20,
     ws_bytes = int(_lib.lcmp_compare_workspace_bytes(n, v, k, flags))
     if ws_bytes == 0:
         raise LcmpError(-3, "lcmp_compare_workspace_bytes")
-    if workspace is None or workspace.numel() < ws_bytes:
+    if workspace is None:
         workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=base.device)
     ptrs = dict(out, target=target)
     ro = RowOut(*[_ptr(ptrs.get(f)) for f in ROW_OUT_FIELDS])
@@ -322,7 +324,7 @@ def lcmp_record_baseline(base: torch.Tensor, k_rec: int = 20, target: torch.Tens
     ws_bytes = int(_lib.lcmp_record_workspace_bytes(n, v, k_rec))
     if ws_bytes == 0:
         raise LcmpError(-3, "lcmp_record_workspace_bytes")
-    if workspace is None or workspace.numel() < ws_bytes:
+    if workspace is None:
         workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
     r = Record(*[_ptr(rec.get(f)) for f in RECORD_FIELDS])
     rc = _lib.lcmp_record_baseline(base.data_ptr(), _dtype_code(base), _ld(base), n, v, k_rec,
@@ -364,7 +366,7 @@ def lcmp_compare_record(record: dict, cand: torch.Tensor, k: int | None = None,
     ws_bytes = int(_lib.lcmp_compare_record_workspace_bytes(n, v))
     if ws_bytes == 0:
         raise LcmpError(-3, "lcmp_compare_record_workspace_bytes")
-    if workspace is None or workspace.numel() < ws_bytes:
+    if workspace is None:
         workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=cand.device)
     r = Record(*[_ptr(record.get(f)) for f in RECORD_FIELDS])
     ptrs = dict(out, target=target)
@@ -395,7 +397,7 @@ def lcmp_bitdiff(a: torch.Tensor, b: torch.Tensor, cols: int | None = None,
     ws_bytes = int(_lib.lcmp_bitdiff_workspace_bytes(rows, cols))
     if ws_bytes == 0:
         raise LcmpError(-3, "lcmp_bitdiff_workspace_bytes")
-    if workspace is None or workspace.numel() < ws_bytes:
+    if workspace is None:
         workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=a.device)
     rc = _lib.lcmp_bitdiff(a.data_ptr(), _dtype_code(a), _ld(a), b.data_ptr(), _dtype_code(b),
                            _ld(b), rows, cols, out.data_ptr(), workspace.data_ptr(),
@@ -432,7 +434,7 @@ def lcmp_bin_report(margin, flip, kl_topk, kl_full, edges, status=None, group=No
     ws_bytes = int(_lib.lcmp_bin_workspace_bytes(n, n_groups, ne))
     if ws_bytes == 0:
         raise LcmpError(-3, "lcmp_bin_workspace_bytes")
-    if workspace is None or workspace.numel() < ws_bytes:
+    if workspace is None:
         workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
     e_arr = (ctypes.c_double * ne)(*edges)
     rc = _lib.lcmp_bin_report(_ptr(margin), _ptr(flip), _ptr(kl_topk), _ptr(kl_full),

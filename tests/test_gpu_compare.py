@@ -282,6 +282,41 @@ def test_single_row_and_empty_batch():
     assert out["kl_full"].numel() == 0
 
 
+def test_short_workspaces_are_reported():
+    """A caller's workspace one byte short of the queried size is an error of
+    every entry point (nothing is launched); the queried size itself works."""
+    import torch
+    import logit_distribution_diffing_amd as L
+    _case("workspaces one byte short")
+    n, v, k = 4, 1000, 20
+    a = torch.randn(n, v, device="cuda")
+    u8 = dict(dtype=torch.uint8, device="cuda")
+
+    def short_then_exact(nbytes, call):
+        with pytest.raises(L.LcmpError) as ei:
+            call(torch.empty(nbytes - 1, **u8))
+        assert ei.value.status == -4
+        return call(torch.empty(nbytes, **u8))
+
+    out = short_then_exact(L.compare_workspace_bytes(n, v, k, True),
+                           lambda ws: L.lcmp_compare_logits(a, a, k=k, with_bitdiff=True,
+                                                            workspace=ws))
+    bits = short_then_exact(int(L.lib().lcmp_bitdiff_workspace_bytes(n, v)),
+                            lambda ws: L.lcmp_bitdiff(a, a, workspace=ws))
+    short_then_exact(int(L.lib().lcmp_bin_workspace_bytes(n, 1, 3)),
+                     lambda ws: L.lcmp_bin_report(out["margin"], out["flip"], out["kl_topk"],
+                                                  out["kl_full"], [0.5, 1.0, float("inf")],
+                                                  status=out["status"], workspace=ws))
+    rec = short_then_exact(int(L.lib().lcmp_record_workspace_bytes(n, v, k)),
+                           lambda ws: L.lcmp_record_baseline(a, k_rec=k, workspace=ws))
+    res = short_then_exact(int(L.lib().lcmp_compare_record_workspace_bytes(n, v)),
+                           lambda ws: L.lcmp_compare_record(rec, a, k=k, workspace=ws))
+    torch.cuda.synchronize()
+    assert (out["kl_full"] == 0).all() and (out["kl_topk"] == 0).all()
+    assert (res["kl_topk"] == 0).all()
+    assert (L.unpack_bitdiff(bits)["ndiff"] == 0).all()
+
+
 def test_repeated_runs_bit_identical():
     _case("determinism")
     a, b = synth.segment(synth.SEED_BASE + 1, 0, 64, 151936)
