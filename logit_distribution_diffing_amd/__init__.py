@@ -17,6 +17,7 @@ Entry points (same names as the C ABI):
 from __future__ import annotations
 
 import ctypes
+import functools
 import os
 
 import torch
@@ -34,11 +35,12 @@ STATUS_NAMES = {0: "LCMP_OK", -1: "LCMP_EINVAL", -2: "LCMP_EDTYPE", -3: "LCMP_ES
                 -4: "LCMP_EWORKSPACE", -5: "LCMP_EHIP", -6: "LCMP_EEDGES"}
 
 EXPORTED = ("lcmp_abi_version", "lcmp_strerror", "lcmp_compare_workspace_bytes",
+            "lcmp_workspace_bytes",
             "lcmp_compare_logits", "lcmp_compare_logits_timed", "lcmp_bitdiff_workspace_bytes",
             "lcmp_bitdiff", "lcmp_bin_workspace_bytes", "lcmp_bin_report", "lcmp_perturb",
             "lcmp_record_workspace_bytes", "lcmp_record_baseline",
             "lcmp_compare_record_workspace_bytes", "lcmp_compare_record",
-            "lcmp_compare_record_timed")
+            "lcmp_compare_record_timed", "lcmp_bitdiff_timed", "lcmp_read_probe")
 
 
 class LcmpError(RuntimeError):
@@ -88,6 +90,8 @@ def _load():
     lib.lcmp_strerror.argtypes = [ci]
     lib.lcmp_compare_workspace_bytes.restype = sz
     lib.lcmp_compare_workspace_bytes.argtypes = [i64, i64, ci, u32]
+    lib.lcmp_workspace_bytes.restype = sz
+    lib.lcmp_workspace_bytes.argtypes = [i64, i64, ci, u32]
     lib.lcmp_compare_logits.restype = ci
     lib.lcmp_compare_logits.argtypes = [vp, ci, i64, vp, ci, i64, i64, i64, ci, u32,
                                         ctypes.POINTER(RowOut), vp, vp, sz, vp]
@@ -97,6 +101,10 @@ def _load():
     lib.lcmp_bitdiff_workspace_bytes.argtypes = [i64, i64]
     lib.lcmp_bitdiff.restype = ci
     lib.lcmp_bitdiff.argtypes = [vp, ci, i64, vp, ci, i64, i64, i64, vp, vp, sz, vp]
+    lib.lcmp_bitdiff_timed.restype = ci
+    lib.lcmp_bitdiff_timed.argtypes = lib.lcmp_bitdiff.argtypes + [vp, vp]
+    lib.lcmp_read_probe.restype = ci
+    lib.lcmp_read_probe.argtypes = [vp, ci, i64, vp, ci, i64, i64, i64, vp, sz, vp, vp, vp]
     lib.lcmp_bin_workspace_bytes.restype = sz
     lib.lcmp_bin_workspace_bytes.argtypes = [i64, ci, ci]
     lib.lcmp_perturb.restype = ci
@@ -145,10 +153,35 @@ def _ld(t: torch.Tensor) -> int:
     return t.stride(0) if t.size(0) > 1 else max(t.stride(0), t.size(1))
 
 
-def _stream(stream) -> int:
+def _torch_stream(stream):
+    """The torch stream object of `stream`: None is the current stream, a raw
+    hipStream_t handle is wrapped without taking ownership."""
     if stream is None:
-        return torch.cuda.current_stream().cuda_stream
-    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+        return torch.cuda.current_stream()
+    if isinstance(stream, torch.cuda.Stream):
+        return stream
+    handle = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+    return torch.cuda.ExternalStream(handle)
+
+
+def _stream(stream) -> int:
+    return _torch_stream(stream).cuda_stream
+
+
+def _on_stream(fn):
+    """Run a binding call with its launch stream as torch's current stream, so
+    every tensor the call allocates (a workspace or outputs the caller did not
+    pass) belongs to the stream its kernels run on.  The caching allocator then
+    cannot hand such a block to work on another stream while the kernels still
+    use it, also after the call has dropped its own reference."""
+    @functools.wraps(fn)
+    def wrapper(*args, stream=None, **kw):
+        if not torch.cuda.is_available():  # the call's own checks reject host tensors
+            return fn(*args, stream=stream, **kw)
+        ts = _torch_stream(stream)
+        with torch.cuda.stream(ts):
+            return fn(*args, stream=ts, **kw)
+    return wrapper
 
 
 def _ptr(t):
@@ -234,6 +267,7 @@ def alloc_compare_outputs(n: int, k: int, device, with_bitdiff: bool = False,
     return out
 
 
+@_on_stream
 def lcmp_compare_logits(base: torch.Tensor, cand: torch.Tensor, k: int = 20,
                         with_bitdiff: bool = False, v: int | None = None, out: dict | None = None,
                         workspace: torch.Tensor | None = None, stream=None,
@@ -302,6 +336,7 @@ def _check_record(record: dict, n: int, k_rec: int):
         _check_buffer(t, _RECORD_SPEC[key], n * per, f"record[{key!r}]")
 
 
+@_on_stream
 def lcmp_record_baseline(base: torch.Tensor, k_rec: int = 20, target: torch.Tensor | None = None,
                          v: int | None = None, workspace: torch.Tensor | None = None,
                          stream=None) -> dict:
@@ -334,6 +369,7 @@ def lcmp_record_baseline(base: torch.Tensor, k_rec: int = 20, target: torch.Tens
     return rec
 
 
+@_on_stream
 def lcmp_compare_record(record: dict, cand: torch.Tensor, k: int | None = None,
                         target: torch.Tensor | None = None, v: int | None = None,
                         out: dict | None = None, workspace: torch.Tensor | None = None,
@@ -381,10 +417,13 @@ def lcmp_compare_record(record: dict, cand: torch.Tensor, k: int | None = None,
     return out
 
 
+@_on_stream
 def lcmp_bitdiff(a: torch.Tensor, b: torch.Tensor, cols: int | None = None,
                  out: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
-                 stream=None) -> torch.Tensor:
-    """Per-row bitwise / ULP statistics; returns a raw [rows, 88] uint8 record tensor."""
+                 stream=None, events: tuple | None = None) -> torch.Tensor:
+    """Per-row bitwise / ULP statistics; returns a raw [rows, 88] uint8 record
+    tensor.  `events`, a pair of raw hipEvent_t handles, selects
+    lcmp_bitdiff_timed."""
     rows = a.size(0)
     cols = a.size(1) if cols is None else cols
     _check_rows(a, rows, cols, "a")
@@ -399,13 +438,41 @@ def lcmp_bitdiff(a: torch.Tensor, b: torch.Tensor, cols: int | None = None,
         raise LcmpError(-3, "lcmp_bitdiff_workspace_bytes")
     if workspace is None:
         workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=a.device)
-    rc = _lib.lcmp_bitdiff(a.data_ptr(), _dtype_code(a), _ld(a), b.data_ptr(), _dtype_code(b),
-                           _ld(b), rows, cols, out.data_ptr(), workspace.data_ptr(),
-                           workspace.numel(), _stream(stream))
+    args = (a.data_ptr(), _dtype_code(a), _ld(a), b.data_ptr(), _dtype_code(b), _ld(b), rows,
+            cols, out.data_ptr(), workspace.data_ptr(), workspace.numel(), _stream(stream))
+    if events is None:
+        rc = _lib.lcmp_bitdiff(*args)
+    else:
+        rc = _lib.lcmp_bitdiff_timed(*args, events[0], events[1])
     _check(rc, "lcmp_bitdiff")
     return out
 
 
+@_on_stream
+def lcmp_read_probe(base: torch.Tensor, cand: torch.Tensor, v: int | None = None,
+                    workspace: torch.Tensor | None = None, stream=None,
+                    events: tuple | None = None) -> None:
+    """Read-only reference stream over the row pairs in the comparison's own
+    access pattern (measurement only; see lcmp.h)."""
+    n = base.size(0)
+    v = base.size(1) if v is None else v
+    _check_rows(base, n, v, "base")
+    _check_rows(cand, n, v, "cand")
+    _check_workspace(workspace)
+    _on_gpu(("base", base), ("cand", cand), ("workspace", workspace))
+    if workspace is None:
+        ws_bytes = int(_lib.lcmp_compare_workspace_bytes(n, v, 1, 0))
+        if ws_bytes == 0:
+            raise LcmpError(-3, "lcmp_compare_workspace_bytes")
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=base.device)
+    ev = (None, None) if events is None else events
+    rc = _lib.lcmp_read_probe(base.data_ptr(), _dtype_code(base), _ld(base), cand.data_ptr(),
+                              _dtype_code(cand), _ld(cand), n, v, workspace.data_ptr(),
+                              workspace.numel(), _stream(stream), ev[0], ev[1])
+    _check(rc, "lcmp_read_probe")
+
+
+@_on_stream
 def lcmp_bin_report(margin, flip, kl_topk, kl_full, edges, status=None, group=None,
                     n_groups: int = 1, big_margin: float = 1.0, workspace=None, stream=None,
                     bins=None, summary=None):
@@ -445,6 +512,7 @@ def lcmp_bin_report(margin, flip, kl_topk, kl_full, edges, status=None, group=No
     return bins, summ
 
 
+@_on_stream
 def lcmp_perturb(src: torch.Tensor, mode: int, param: int = 0, out: torch.Tensor | None = None,
                  out_dtype: torch.dtype | None = None, stream=None) -> torch.Tensor:
     """Precision perturbation of a [rows, cols] fp32 / bf16 device tensor (keep

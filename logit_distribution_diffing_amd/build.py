@@ -1,17 +1,25 @@
-"""Compile liblcmp.so (HIP, gfx950) in-tree with hipcc."""
+"""Compile liblcmp.so (HIP, gfx950) in-tree with hipcc.
+
+Each translation unit is compiled on its own (in parallel) into
+``_build/`` next to this file, then linked into ``liblcmp.so``.  Every kernel
+is launched from the unit that defines it, so no relocatable device code is
+needed.
+"""
 from __future__ import annotations
 
 import glob
 import os
 import subprocess
+from concurrent.futures import ThreadPoolExecutor
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
+OBJ = os.path.join(HERE, "_build")
 SO = os.path.join(HERE, "liblcmp.so")
 ARCH = os.environ.get("LCMP_OFFLOAD_ARCH", "gfx950")
 
 FLAGS = [
-    "-O3", "-std=c++17", "-fPIC", "-shared",
+    "-O3", "-std=c++17", "-fPIC",
     f"--offload-arch={ARCH}",
     # packed fp32 instructions are kept out of the device code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
@@ -23,23 +31,39 @@ def sources() -> list[str]:
     return sorted(glob.glob(os.path.join(CSRC, "*.hip")))
 
 
-def build(force: bool = False, verbose: bool = False) -> str:
+def _headers() -> list[str]:
+    return glob.glob(os.path.join(CSRC, "*.hpp")) + [os.path.join(HERE, "..", "include", "lcmp.h")]
+
+
+def build(force: bool = False, verbose: bool = False, jobs: int | None = None) -> str:
     """Build liblcmp.so unless it is present and newer than every source."""
     srcs = sources()
-    hdrs = glob.glob(os.path.join(CSRC, "*.hpp")) + [os.path.join(HERE, "..", "include", "lcmp.h")]
     if not force and os.path.exists(SO):
-        newest = max(os.path.getmtime(f) for f in srcs + hdrs)
+        newest = max(os.path.getmtime(f) for f in srcs + _headers())
         if os.path.getmtime(SO) >= newest:
             return SO
     hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+    os.makedirs(OBJ, exist_ok=True)
+    objs = [os.path.join(OBJ, os.path.basename(s)[:-4] + ".o") for s in srcs]
+
+    def compile_one(pair):
+        src, obj = pair
+        cmd = [hipcc, *FLAGS, "-c", "-o", obj, src]
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        subprocess.run(cmd, check=True, stderr=subprocess.PIPE if not verbose else None)
+
+    jobs = jobs or min(len(srcs), max(1, min(8, os.cpu_count() or 1)))
+    with ThreadPoolExecutor(jobs) as ex:
+        list(ex.map(compile_one, zip(srcs, objs)))
     tmp = SO + ".tmp"
-    cmd = [hipcc, *FLAGS, "-o", tmp, *srcs]
+    cmd = [hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     if verbose:
-        print(" ".join(cmd))
+        print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)
     os.replace(tmp, SO)
     return SO
 
 
 if __name__ == "__main__":
-    print(build(force=True, verbose=True))
+    print(build(force=True, verbose=False))

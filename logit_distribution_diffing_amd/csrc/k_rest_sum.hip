@@ -38,10 +38,7 @@ namespace lcmp {
 
 namespace {
 
-#ifndef LCMP_REST_RING
-#define LCMP_REST_RING 4  // LDS ring slots per wave: one processed, the rest in flight
-#endif
-constexpr int kRestR = LCMP_REST_RING;
+constexpr int kRestR = 4;  // LDS ring slots per wave: one processed, the rest in flight
 
 constexpr int kRestStepBytes = 2048;  // one wave step: two 1 KiB loads
 static_assert((kRestR - 1) * 2 <= 63, "vector-memory counter range");

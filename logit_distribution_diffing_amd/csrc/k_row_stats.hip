@@ -40,10 +40,7 @@ namespace lcmp {
 // kint <= 64 entries (64 + 256 <= kCapW), and after a step it is reduced
 // whenever it holds more than kFlushAt.
 constexpr int kCapW = 8 * kWave;  // 512
-#ifndef LCMP_FLUSH_AT
-#define LCMP_FLUSH_AT 128
-#endif
-constexpr int kFlushAt = LCMP_FLUSH_AT;
+constexpr int kFlushAt = 128;
 // threshold index meaning "no index bound yet": every element at or above
 // the threshold value passes
 constexpr int kTauOpen = 0x7fffffff;
@@ -287,36 +284,27 @@ struct Raw {
 // with a few microseconds of loaded HBM latency, 6 TB/s needs about 100 KB per
 // CU in flight, so the ring is deep and the blocks are small enough that the
 // 160 KB of LDS of a CU holds several of them.
-#ifndef LCMP_RING_FF
-#define LCMP_RING_FF 3  // fp32 / fp32: 4 KiB steps
-#endif
-#ifndef LCMP_RING_FH
-#define LCMP_RING_FH 3  // one fp32 side: 3 KiB steps
-#endif
-#ifndef LCMP_RING_HH
-#define LCMP_RING_HH 3  // bf16 / bf16: 2 KiB steps
-#endif
-#ifndef LCMP_RING_WAVES
-#define LCMP_RING_WAVES 4  // waves per block when staging through LDS
-#endif
-// Which pairs stage through LDS: measured on the corpus (fp32 / bf16) and
-// stream (bf16 / bf16) shapes, the register double buffer is faster when one
-// side is fp32 (more waves fit), the ring when both sides are bf16.
-#ifndef LCMP_RING_MASK
-#define LCMP_RING_MASK 8  // bit 2 * TA + TB set: that pair uses the ring (8: bf16 / bf16 only)
-#endif
+// Ring depths (measured: three slots, two steps in flight, for every pair)
+// and which pairs stage through LDS: on the corpus (fp32 / bf16) and stream
+// (bf16 / bf16) shapes the register double buffer is faster when one side is
+// fp32 (more waves fit), the ring when both sides are bf16.
+constexpr int kRingFF = 3;     // fp32 / fp32: 4 KiB steps
+constexpr int kRingFH = 3;     // one fp32 side: 3 KiB steps
+constexpr int kRingHH = 3;     // bf16 / bf16: 2 KiB steps
+constexpr int kRingWaves = 4;  // waves per block when staging through LDS
+constexpr int kRingMask = 8;   // bit 2 * TA + TB set: that pair uses the ring (bf16 / bf16 only)
 template <int TA, int TB, bool CMP, bool VEC>
 struct Shape {
-  static constexpr bool RING = VEC && CMP && ((LCMP_RING_MASK >> (2 * TA + TB)) & 1);
+  static constexpr bool RING = VEC && CMP && ((kRingMask >> (2 * TA + TB)) & 1);
   static constexpr int SA = TA == 1 ? 2 : 4, SB = TB == 1 ? 2 : 4;
   static constexpr int kStepA = kSpan * SA, kStepB = kSpan * SB;
   static constexpr int kStep = kStepA + kStepB;
   // ring slots: one step processed, R - 1 in flight
   static constexpr int R = !RING                  ? 1
-                           : (TA == 1 && TB == 1) ? LCMP_RING_HH
-                           : (TA == 0 && TB == 0) ? LCMP_RING_FF
-                                                  : LCMP_RING_FH;
-  static constexpr int W = RING ? LCMP_RING_WAVES : kWavesPerBlock;  // waves per block
+                           : (TA == 1 && TB == 1) ? kRingHH
+                           : (TA == 0 && TB == 0) ? kRingFF
+                                                  : kRingFH;
+  static constexpr int W = RING ? kRingWaves : kWavesPerBlock;  // waves per block
   static_assert((R - 1) * (kStep / 1024) <= 63, "vector-memory counter range");
 };
 
@@ -536,7 +524,11 @@ __device__ __forceinline__ void process_step(const uint32_t (&ua)[8], const uint
   // with the comparison, a NaN or inf on either side makes delta NaN or
   // infinite (sab, or dg alone), a huge baseline makes sum a^2 infinite, and
   // |delta| <= 1/8 bounds sum delta^2.
-  bool ok = true;
+  // In the ragged last step a lane whose columns all lie past the end holds
+  // only neutral pairs; before the chunk has a reference (every column so far
+  // -inf on both sides) their weight 2^(-FLT_MAX*log2e + inf) would be +inf,
+  // so such a step goes to the exact path, which skips masked columns.
+  bool ok = !tail || st.r2h > -INFINITY || !CMP;
   if (CMP && BITS)
     ok = ok && !st.huge && (dmax <= kPolyMax) && isfinite(sab + ssb);
   else if (CMP)

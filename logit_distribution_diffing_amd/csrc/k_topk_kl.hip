@@ -56,13 +56,7 @@ __global__ __launch_bounds__(kWave) void k_topk_kl(FinalArgs a) {
   const bool has = lane < C;
   ChunkStats cs;
   if (has) cs = a.stats[row * C + lane];
-  ChunkBits cb;
-  cb.ndiff = 0;
-  cb.first = -1;
-  cb.nfa = cb.nfb = 0;
-  cb.max_ulp = 0;
-  cb.max_abs = 0.0;
-  cb.sum_abs = cb.ssd = cb.ssb = 0.0;
+  ChunkBits cb = no_bits();
   if (a.bd && has) cb = a.bits[row * C + lane];
   const int64_t tb = row * (int64_t)mcap;
   float sv[kSlotRounds];
@@ -84,31 +78,7 @@ __global__ __launch_bounds__(kWave) void k_topk_kl(FinalArgs a) {
     sel_idx[lane] = 0x7fffffff;
   }
 
-  if (a.bd) {
-    const int64_t ndiff = lanes_sum(cb.ndiff, C);
-    const int64_t first = lanes_min(cb.first >= 0 ? cb.first : INT64_MAX, C);
-    const int64_t nfa = lanes_sum(cb.nfa, C), nfb = lanes_sum(cb.nfb, C);
-    const uint32_t mu = lanes_max(cb.max_ulp, C);
-    const double ma = lanes_max(cb.max_abs, C);
-    const double sab = lanes_sum(cb.sum_abs, C), ssd = lanes_sum(cb.ssd, C),
-                 ssb = lanes_sum(cb.ssb, C);
-    if (lane == 0) {
-      BitdiffRow r;
-      r.ndiff = ndiff;
-      r.first_diff = first == INT64_MAX ? -1 : first;
-      r.nonfinite_a = nfa;
-      r.nonfinite_b = nfb;
-      r.max_ulp = mu;
-      r.pad_ = 0;
-      r.max_abs = ma;
-      r.sum_abs = sab;
-      r.sum_sq_diff = ssd;
-      r.sum_sq_base = ssb;
-      r.mean_abs = sab / (double)a.v;
-      r.rel_l2 = ssb > 0.0 ? sqrt(ssd / ssb) : (ssd > 0.0 ? INFINITY : 0.0);
-      a.bd[row] = r;
-    }
-  }
+  if (a.bd) merge_bits_lanes(cb, C, a.v, a.bd + row);
 
   // ---- chunk sums, rescaled to the largest reference
   const double r2 = has ? cs.r2 : -INFINITY;
@@ -143,11 +113,14 @@ __global__ __launch_bounds__(kWave) void k_topk_kl(FinalArgs a) {
       for (int j = lane; j < a.k; j += kWave) a.topk_idx[row * a.k + j] = -1;
     return;
   }
-  const double sc = (has && r2 > -INFINITY) ? exp2(r2 - M2) : 0.0;
-  const double S = lanes_sum(has ? cs.s * sc : 0.0, C);
-  const double D = lanes_sum(has ? cs.d * sc : 0.0, C);
-  const double F = lanes_sum(has ? cs.f * sc : 0.0, C);
-  const double W = lanes_sum(has ? cs.w * sc : 0.0, C);
+  // a chunk without a reference held no finite logit on either side: it adds
+  // nothing (it is left out rather than scaled by 0)
+  const bool live = has && r2 > -INFINITY;
+  const double sc = live ? exp2(r2 - M2) : 0.0;
+  const double S = lanes_sum(live ? cs.s * sc : 0.0, C);
+  const double D = lanes_sum(live ? cs.d * sc : 0.0, C);
+  const double F = lanes_sum(live ? cs.f * sc : 0.0, C);
+  const double W = lanes_sum(live ? cs.w * sc : 0.0, C);
 
   // ---- candidate argmax across chunks: value descending, index ascending
   const float bm = has ? cs.bmax : -INFINITY;

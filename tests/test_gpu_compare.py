@@ -192,6 +192,40 @@ def test_baseline_masked_where_candidate_is_large():
     assert_bitdiff_equal(g["bitdiff"], oracle.bitdiff(a, b))
 
 
+def _bf16(x):
+    import torch
+    return torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+
+
+@pytest.mark.parametrize("tb,tc,v,masked", [
+    ("bf16", "bf16", 151936, 8000),   # 16 chunks; the ragged last step leaves lanes 48-63 empty
+    ("f32", "f32", 50257, 7000),      # V mod 512 = 81: lanes 21-63 of the last step are empty
+    ("f32", "bf16", 151936, 10000),
+])
+def test_last_chunk_masked_on_both_sides(tb, tc, v, masked):
+    """Rows whose trailing columns (more than a whole chunk, ragged last step
+    included) are -inf on both sides, with the bitwise statistics fused: the
+    last chunk holds no finite logit, so it has no exp2 reference, and its
+    masked tail lanes must add nothing.  Also rows masked only partly into the
+    last chunk, and fully finite rows."""
+    _case(f"last chunk -inf on both sides {tb}/{tc} v={v}")
+    rng = np.random.default_rng(v + masked)
+    n = 64
+    x = (1.5 * rng.standard_normal((n, v))).astype(np.float32)
+    y = (x + 0.02 * rng.standard_normal((n, v))).astype(np.float32)
+    x[: n // 2, v - masked:] = -np.inf
+    y[: n // 2, v - masked:] = -np.inf
+    x[n // 2: 3 * n // 4, v - 300:] = -np.inf   # only inside the ragged last step
+    y[n // 2: 3 * n // 4, v - 300:] = -np.inf
+    a = x if tb == "f32" else _bf16(x)
+    b = y if tc == "f32" else _bf16(y)
+    g = gpu_compare(a, b, k=20, with_bitdiff=True)
+    o = oracle.compare(a, b, k=20)
+    assert np.all(np.isfinite(o["kl_full"])) and np.all(o["status"] == 0)
+    assert_compare_equal(g, o)
+    assert_bitdiff_equal(g["bitdiff"], oracle.bitdiff(a, b))
+
+
 @pytest.mark.parametrize("tb,tc,k", [("f32", "f32", 20), ("bf16", "bf16", 20), ("f32", "bf16", 20),
                                      ("f32", "f32", 1), ("f32", "bf16", 64)])
 def test_candidate_bucket_far_below(tb, tc, k):

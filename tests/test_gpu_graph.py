@@ -154,3 +154,30 @@ def test_two_streams_with_their_own_workspaces():
         torch.cuda.synchronize()
         for i in range(2):
             _assert_same({kk: vv.cpu().numpy() for kk, vv in outs[i].items()}, ref[i])
+
+
+def test_side_stream_without_workspace():
+    """A call on a side stream that brings no workspace and no outputs: what the
+    binding allocates belongs to that stream, so memory allocated and filled on
+    the current stream right after the call (before any synchronisation) cannot
+    land on a block the side stream's kernels still use."""
+    import torch
+    import logit_distribution_diffing_amd as L
+    n, v, k = 1024, 151936, 20
+    _case(f"side stream, internal workspace {n}x{v}")
+    a, b = _inputs(11, n, v)
+    da, db = to_device(a), to_device(b)
+    ref = L.lcmp_compare_logits(da, db, k=k, with_bitdiff=True)
+    torch.cuda.synchronize()
+    ref = {kk: vv.cpu().numpy().copy() for kk, vv in ref.items()}
+    ws_bytes = L.compare_workspace_bytes(n, v, k, True)
+    side = torch.cuda.Stream()   # default priority
+    for rep in range(3):
+        torch.cuda.synchronize()
+        out = L.lcmp_compare_logits(da, db, k=k, with_bitdiff=True, stream=side)
+        junk = [torch.empty(ws_bytes, dtype=torch.uint8, device="cuda").fill_(0xA5)
+                for _ in range(4)]
+        junk += [torch.full((n, k), -7, dtype=torch.int32, device="cuda")]
+        torch.cuda.synchronize()
+        del junk
+        _assert_same({kk: vv.cpu().numpy() for kk, vv in out.items()}, ref)
