@@ -3,30 +3,46 @@
 
 One step = one pass of the whole path over one batch of synthetic positions:
 lcmp_compare_logits with the bitwise statistics fused (streaming pass + per-row
-finalize) followed by lcmp_bin_report (margin bins).  The default workload is
-the scored-corpus shape: N=10240 positions x V=151936, fp32 baseline, bf16
-candidate, k=20, six margin bins.  Inputs are generated on the host, copied to
-HBM once, and are resident before the timed region starts.
+finalize) followed by lcmp_bin_report (margin bins; on the corpus, per context
+depth x code/prose group).  The default workload is the scored-corpus shape:
+N=10240 positions x V=151936, fp32 baseline, bf16 candidate, k=20, six margin
+bins, ten row groups.  Inputs are generated on the host, copied to HBM once,
+and are resident before the timed region starts.
 
 Prints ONE JSON line on stdout (everything else goes to stderr):
   value      positions per second over the timed steps (whole job, one GPU)
   roofline   HBM roofline of the streaming kernel: algorithmic bytes per launch
              (N*V*(bytes per baseline + candidate element)) / its average
              duration, measured with HIP events recorded around that kernel on
-             its own stream; traffic = measured HBM bytes per launch from the
-             rocprofv3 FETCH_SIZE / WRITE_SIZE counters (copy-calibrated) when
-             they were taken on the current kernel source, else null
-  cpu_baseline  the double-precision CPU oracle on a bounded row sample
+             its own stream.  Also: the same bytes over the whole step, and over
+             the duration of a read-only stream of the same inputs in the same
+             access pattern (lcmp_read_probe), the read rate this pattern can
+             reach.  traffic = measured HBM bytes per launch from the rocprofv3
+             FETCH_SIZE / WRITE_SIZE counters (copy-calibrated), taken from the
+             committed counter summary when it was measured on the current
+             kernel source and workload (traffic_source says which file), else
+             null
+  cpu_baseline  the double-precision CPU oracle on a bounded row sample, with
+             the host's CPU model; on the tiny and segment workloads also on one
+             core
 
 With --path record the step is instead the comparison against a compact
 record of the baseline (lcmp_compare_record + lcmp_bin_report): the record is
 made once before the timed region, and the streaming kernel reads only the
 candidate rows (N*V*(bytes per candidate element) per launch).
 
+--workload sweep times the bitwise / ULP mode over a shape sweep instead: one
+step is lcmp_bitdiff over bf16 [T, 5120] for T in {1, 17, 65, 1024, 1502, 1777,
+4095, 4096} and over fp32 [512, 151936] logit rows (rows/s and GB/s).
+
+On the segment and sweep workloads (inputs below a few GB) the step rotates
+over several copies of the inputs (--copies), so a step never finds its
+inputs in the 256 MB last-level cache from the step before.
+
 Flags: --gpus N (only 1 is supported: this path runs on one GPU),
---steps K, --warmup W, --workload {corpus,segment,stream,tiny},
---path {compare,record},
---cpu-seconds S (budget of the oracle leg), --no-cpu-baseline,
+--steps K, --warmup W, --workload {corpus,segment,stream,tiny,sweep},
+--path {compare,record}, --copies C, --cpu-seconds S (budget of the oracle
+leg), --no-cpu-baseline, --no-read-probe,
 --copy-probe BYTES (run only a plain device copy of that size, for counter
 calibration under rocprofv3).
 """
@@ -46,14 +62,25 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
 METRIC = "logit positions/sec at V=151936 + achieved HBM GB/s vs MI355X peak"
-# per path: the dominant kernel, its committed counter summary and its sources
+SWEEP_METRIC = "bitwise rows/sec over the [T,5120] bf16 shape sweep and [512,151936] fp32 rows " \
+               "+ achieved HBM GB/s vs MI355X peak"
+# per path: the dominant kernel, its committed counter summaries (per workload)
+# and its sources
 PATHS = {
-    "compare": dict(kernel="k_row_stats",
-                    counters=os.path.join(ROOT, "profiles", "k_row_stats_corpus_counters.md"),
+    "compare": dict(kernel="k_row_stats", prefix="k_row_stats",
                     sources=("k_row_stats.hip", "common.hpp", "dma.hpp")),
-    "record": dict(kernel="k_rest_sum",
-                   counters=os.path.join(ROOT, "profiles", "k_rest_sum_corpus_counters.md"),
+    "record": dict(kernel="k_rest_sum", prefix="k_rest_sum",
                    sources=("k_rest_sum.hip", "common.hpp", "dma.hpp")),
+}
+COPIES = {"corpus": 1, "stream": 1, "tiny": 1, "segment": 4, "sweep": 4}
+WORKLOAD_DESC = {
+    "corpus": "scored corpus: 10240 positions (5 depths x 4 segments x 512) x V=151936, "
+              "fp32 baseline / bf16 candidate",
+    "segment": "decoded segment: 512 positions x V=151936, fp32 / fp32",
+    "stream": "large stream: 65536 positions x V=151936, bf16 / bf16",
+    "tiny": "tiny compare: 64 positions x V=1024, fp32 / fp32",
+    "sweep": "bitwise shape sweep: bf16 [T,5120] for T in {1,17,65,1024,1502,1777,4095,4096} "
+             "plus fp32 [512,151936] logit rows, 0.1% of elements moved by 1-3 ULP",
 }
 
 
@@ -69,20 +96,39 @@ def kernel_hash(path: str = "compare") -> str:
     return h.hexdigest()[:16]
 
 
+def counters_file(workload: str, path: str = "compare") -> str:
+    return os.path.join(ROOT, "profiles", f"{PATHS[path]['prefix']}_{workload}_counters.md")
+
+
 def stored_traffic(workload: str, path: str = "compare"):
-    """HBM bytes per launch of the path's streaming kernel from the committed
-    counter summary, if it was taken on this kernel source and workload."""
-    counters = PATHS[path]["counters"]
+    """(HBM bytes per launch of the path's streaming kernel, the summary file)
+    from the committed counter summary, if it was taken on this kernel source
+    and workload; else (None, None)."""
+    counters = counters_file(workload, path)
     if not os.path.exists(counters):
-        return None
+        return None, None
     text = open(counters).read()
     m = re.search(r"```json\n(.*?)\n```", text, re.S)
     if not m:
-        return None
+        return None, None
     rec = json.loads(m.group(1))
     if rec.get("kernel_hash") != kernel_hash(path) or rec.get("workload") != workload:
-        return None
-    return rec.get("traffic_bytes_per_launch")
+        return None, None
+    return rec.get("traffic_bytes_per_launch"), os.path.relpath(counters, ROOT)
+
+
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def oracle_threads() -> int:
+    return int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
 
 
 class Hip:
@@ -104,6 +150,12 @@ class Hip:
         ms = ctypes.c_float()
         assert self.lib.hipEventElapsedTime(ctypes.byref(ms), a, b) == 0
         return ms.value
+
+
+def stats_us(ms_list):
+    srt = sorted(ms_list)
+    return dict(mean=1e3 * sum(srt) / len(srt), median=1e3 * srt[len(srt) // 2],
+                min=1e3 * srt[0], max=1e3 * srt[-1])
 
 
 def make_inputs(workload: str, w: dict, torch):
@@ -139,30 +191,50 @@ def make_inputs(workload: str, w: dict, torch):
         for dst, src in ((base, a), (cand, b)):
             t = torch.from_numpy(src.view(np.int16) if src.dtype == np.uint16 else src)
             dst[r0:r0 + nr].view(torch.int16 if src.dtype == np.uint16 else dst.dtype).copy_(t)
+        if (r0 // blk) % 16 == 15:
+            log(f"[bench] generated {r0 + nr}/{n} rows")
     torch.cuda.synchronize()
     log(f"[bench] generated and uploaded {workload} {n}x{v} in {time.time() - t0:.1f}s")
     return base, cand, host_a, host_b
 
 
-def cpu_leg(host_a, host_b, k, edges, seconds: float):
+def _bounded_rows(run, rows_avail, seconds, probe):
+    """Rows of a sample that takes about `seconds`, from a timed probe of
+    `probe` rows."""
+    t0 = time.perf_counter()
+    run(probe)
+    per_row = (time.perf_counter() - t0) / probe
+    return int(max(probe, min(rows_avail, seconds / max(per_row, 1e-9))))
+
+
+def cpu_leg(host_a, host_b, k, edges, seconds: float, single_core: bool):
     """Time the oracle (compare + bitwise + bins) on a bounded sample of rows."""
     import oracle
-    threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    threads = oracle_threads()
+
+    def run(rows, nthreads):
+        o = oracle.compare(host_a[:rows], host_b[:rows], k=k, nthreads=nthreads)
+        oracle.bitdiff(host_a[:rows], host_b[:rows], nthreads=nthreads)
+        oracle.bin_report(o["margin"], o["flip"], o["kl_topk"], o["kl_full"], edges,
+                          status=o["status"])
+
     rows_avail = host_a.shape[0]
-    probe = min(rows_avail, max(threads, 16))
+    rows = _bounded_rows(lambda r: run(r, threads), rows_avail, seconds,
+                         min(rows_avail, max(threads, 16)))
     t0 = time.perf_counter()
-    oracle.compare(host_a[:probe], host_b[:probe], k=k, nthreads=threads)
-    per_row = (time.perf_counter() - t0) / probe
-    rows = int(max(probe, min(rows_avail, seconds / max(per_row, 1e-9))))
-    t0 = time.perf_counter()
-    o = oracle.compare(host_a[:rows], host_b[:rows], k=k, nthreads=threads)
-    oracle.bitdiff(host_a[:rows], host_b[:rows], nthreads=threads)
-    oracle.bin_report(o["margin"], o["flip"], o["kl_topk"], o["kl_full"], edges,
-                      status=o["status"])
+    run(rows, threads)
     dt = time.perf_counter() - t0
-    return dict(value=rows / dt, unit="positions/s", cores=threads, kind="oracle",
-                sample=f"first {rows} positions of the workload (compare + bitwise + bins), "
-                       f"{dt:.1f} s")
+    res = dict(value=rows / dt, unit="positions/s", cores=threads, kind="oracle",
+               sample=f"first {rows} positions of the workload (compare + bitwise + bins), "
+                      f"{dt:.1f} s", cpu=cpu_model())
+    if single_core:
+        rows1 = _bounded_rows(lambda r: run(r, 1), rows_avail, seconds / 3, min(rows_avail, 4))
+        t0 = time.perf_counter()
+        run(rows1, 1)
+        dt1 = time.perf_counter() - t0
+        res["single_core"] = dict(value=rows1 / dt1, unit="positions/s", cores=1,
+                                  sample=f"first {rows1} positions, {dt1:.1f} s")
+    return res
 
 
 def cpu_leg_record(host_a, host_b, k, edges, seconds: float):
@@ -170,7 +242,7 @@ def cpu_leg_record(host_a, host_b, k, edges, seconds: float):
     of rows; the sample's record is made first, outside the timing, as the
     record of a baseline is made once."""
     import oracle
-    threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    threads = oracle_threads()
     rows_avail = host_a.shape[0]
     probe = min(rows_avail, max(threads, 16))
     rec = oracle.record(host_a[:probe], k=k, nthreads=threads)
@@ -185,7 +257,7 @@ def cpu_leg_record(host_a, host_b, k, edges, seconds: float):
     dt = time.perf_counter() - t0
     return dict(value=rows / dt, unit="positions/s", cores=threads, kind="oracle",
                 sample=f"first {rows} positions of the workload (comparison against their "
-                       f"record + bins), {dt:.1f} s")
+                       f"record + bins), {dt:.1f} s", cpu=cpu_model())
 
 
 def copy_probe(nbytes: int):
@@ -199,16 +271,271 @@ def copy_probe(nbytes: int):
                       "dispatches": 5}), flush=True)
 
 
+def time_steps(step, steps, warmup, hip, torch, stream, nev=1):
+    """W untimed steps, then K timed steps between synchronisations; step(i, evs)
+    records the `nev` event pairs of `evs` around the step's streaming kernel(s)
+    (evs is None in the warm-up).  Returns the stream time of the K steps (ms),
+    the wall time (s) and, per event pair, the list of its K durations (ms)."""
+    for i in range(warmup):
+        step(i, None)
+    torch.cuda.synchronize()
+    evs = [[(hip.event(), hip.event()) for _ in range(nev)] for _ in range(steps)]
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_stop = torch.cuda.Event(enable_timing=True)
+    wall0 = time.perf_counter()
+    t_start.record(stream)
+    for i in range(steps):
+        step(warmup + i, evs[i])
+    t_stop.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    gpu_ms = t_start.elapsed_time(t_stop)
+    per = [[hip.elapsed_ms(a, b) for a, b in (evs[i][j] for i in range(steps))]
+           for j in range(nev)]
+    return gpu_ms, wall, per
+
+
+def read_ceiling(L, pairs, hip, torch, stream, reps=12):
+    """Median duration (us) of the read-only probe over the same inputs (the
+    copies in turn), after 3 untimed launches."""
+    ws = None
+    ms = []
+    for i in range(3 + reps):
+        base, cand = pairs[i % len(pairs)]
+        if ws is None:
+            ws = torch.empty(int(L.lib().lcmp_compare_workspace_bytes(base.size(0), base.size(1),
+                                                                         1, 0)),
+                             dtype=torch.uint8, device="cuda")
+        ev = (hip.event(), hip.event()) if i >= 3 else None
+        L.lcmp_read_probe(base, cand, workspace=ws, stream=stream, events=ev)
+        if ev is not None:
+            ms.append(ev)
+    torch.cuda.synchronize()
+    return stats_us([hip.elapsed_ms(a, b) for a, b in ms])
+
+
+def run_compare(args, torch, L, synth):
+    w = dict(synth.WORKLOADS[args.workload])
+    n, v, k = w["n"], w["v"], w["k"]
+    edges = list(synth.DEFAULT_EDGES)
+    base, cand, host_a, host_b = make_inputs(args.workload, w, torch)
+    copies = args.copies or COPIES[args.workload]
+    pairs = [(base, cand)] + [(base.clone(), cand.clone()) for _ in range(copies - 1)]
+    esize = {"f32": 4, "bf16": 2}
+    hip = Hip()
+    stream = torch.cuda.current_stream()
+    if args.workload == "corpus":
+        groups = torch.from_numpy(synth.corpus_groups(n)).cuda()
+        n_groups = synth.CORPUS_GROUPS
+    else:
+        groups, n_groups = None, 1
+    bws = torch.empty(int(L.lib().lcmp_bin_workspace_bytes(n, n_groups, len(edges))),
+                      dtype=torch.uint8, device="cuda")
+    bins = torch.empty((n_groups * len(edges), L.BIN_BYTES), dtype=torch.uint8, device="cuda")
+    summ = torch.empty((n_groups, L.GROUP_SUMMARY_BYTES), dtype=torch.uint8, device="cuda")
+
+    if args.path == "compare":
+        # the streaming kernel reads both rows once
+        bytes_per_launch = n * v * (esize[w["base"]] + esize[w["cand"]])
+        out = L.alloc_compare_outputs(n, k, base.device, with_bitdiff=True)
+        ws = torch.empty(L.compare_workspace_bytes(n, v, k, True), dtype=torch.uint8,
+                         device="cuda")
+
+        def step(i, evs=None):
+            b_, c_ = pairs[i % copies]
+            L.lcmp_compare_logits(b_, c_, k=k, with_bitdiff=True, out=out, workspace=ws,
+                                  stream=stream, events=evs and evs[0])
+            L.lcmp_bin_report(out["margin"], out["flip"], out["kl_topk"], out["kl_full"], edges,
+                              status=out["status"], group=groups, n_groups=n_groups,
+                              workspace=bws, stream=stream, bins=bins, summary=summ)
+    else:
+        # the baseline is recorded once; the timed steps read the candidate rows
+        # and the record only
+        record = L.lcmp_record_baseline(base, k_rec=k)
+        torch.cuda.synchronize()
+        bytes_per_launch = n * v * esize[w["cand"]]
+        out = L.alloc_compare_outputs(n, k, cand.device)
+        del out["kl_full"]
+        ws = torch.empty(int(L.lib().lcmp_compare_record_workspace_bytes(n, v)),
+                         dtype=torch.uint8, device="cuda")
+
+        def step(i, evs=None):
+            c_ = pairs[i % copies][1]
+            L.lcmp_compare_record(record, c_, k=k, out=out, workspace=ws, stream=stream,
+                                  events=evs and evs[0])
+            L.lcmp_bin_report(out["margin"], out["flip"], out["kl_topk"], None, edges,
+                              status=out["status"], group=groups, n_groups=n_groups,
+                              workspace=bws, stream=stream, bins=bins, summary=summ)
+
+    gpu_ms, wall, (kern_ms,) = time_steps(step, args.steps, args.warmup, hip, torch, stream)
+    ks = stats_us(kern_ms)
+    ms_per_step = gpu_ms / args.steps
+    log(f"[bench] {args.steps} steps: {gpu_ms:.3f} ms on the stream, {wall * 1e3:.3f} ms wall; "
+        f"streaming kernel mean {ks['mean']:.1f} us, median {ks['median']:.1f} (min "
+        f"{ks['min']:.1f}, max {ks['max']:.1f}); first five "
+        f"{[round(x * 1e3) for x in kern_ms[:5]]} us; input copies in turn: {copies}")
+    b_np, s_np = L.unpack_bins(bins, summ, n_groups)
+    log(f"[bench] bins count {b_np['count'].sum(axis=0).tolist()} flips "
+        f"{b_np['flips'].sum(axis=0).tolist()} big-margin flips "
+        f"{int(s_np['big_margin_flips'].sum())} over {n_groups} group(s)")
+
+    probe = None
+    if not args.no_read_probe and args.path == "compare":
+        probe = read_ceiling(L, pairs, hip, torch, stream)
+        log(f"[bench] read-only probe of the same pattern: median {probe['median']:.1f} us "
+            f"({bytes_per_launch / probe['median'] / 1e3:.1f} GB/s)")
+
+    gbs = lambda us: round(bytes_per_launch / us / 1e3, 1)  # noqa: E731
+    achieved = gbs(ks["mean"])
+    traffic, traffic_src = stored_traffic(args.workload, args.path)
+    roofline = dict(bound="hbm", achieved=achieved, peak=HBM_PEAK_GBS, unit="GB/s",
+                    frac=round(achieved / HBM_PEAK_GBS, 4), traffic=traffic,
+                    traffic_source=(f"{traffic_src}: rocprofv3 FETCH_SIZE + WRITE_SIZE of this "
+                                    "kernel source, copy-calibrated" if traffic_src else None),
+                    kernel=PATHS[args.path]["kernel"], bytes_per_launch=bytes_per_launch,
+                    kernel_us=dict((key, round(val, 1)) for key, val in ks.items()),
+                    achieved_median=gbs(ks["median"]),
+                    step_achieved=gbs(1e3 * ms_per_step),
+                    step_frac=round(gbs(1e3 * ms_per_step) / HBM_PEAK_GBS, 4))
+    if probe is not None:
+        roofline["read_ceiling"] = gbs(probe["median"])
+        roofline["frac_of_read_ceiling"] = round(achieved / gbs(probe["median"]), 4)
+
+    cpu = None
+    if not args.no_cpu_baseline and host_a is not None:
+        if args.path == "compare":
+            cpu = cpu_leg(host_a, host_b, k, edges, args.cpu_seconds,
+                          single_core=args.workload in ("tiny", "segment"))
+        else:
+            cpu = cpu_leg_record(host_a, host_b, k, edges, args.cpu_seconds)
+        log(f"[bench] cpu oracle: {cpu['value']:.1f} positions/s on {cpu['cores']} threads "
+            f"({cpu['cpu']})")
+
+    value = n * args.steps / (gpu_ms / 1e3)
+    return {
+        "metric": METRIC, "value": round(value, 1), "unit": "positions/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": WORKLOAD_DESC[args.workload], "path": args.path, "n": n, "v": v,
+                   "k": k, "base": w["base"], "cand": w["cand"],
+                   "arithmetic": "fp32 per element, fp64 sums and finalize",
+                   "bitwise_stats": args.path == "compare", "margin_edges": len(edges),
+                   "row_groups": n_groups, "input_copies": copies,
+                   "hbm_gbs_step": roofline["step_achieved"]},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+
+
+def run_sweep(args, torch, L, synth):
+    """Bitwise / ULP mode over the shape sweep: one step = lcmp_bitdiff over
+    every shape of the sweep, the fp32 logit rows last."""
+    import numpy as np
+    w = synth.WORKLOADS["sweep"]
+    cols, v, frac, seed = w["cols"], w["v"], w["frac"], w["seed"]
+    t0 = time.time()
+    host = []
+    for t in w["t_list"]:
+        a = synth.bf16_normal(seed, 0, t, cols)
+        b, _, _ = synth.inject_ulp(seed, t, a, frac)
+        host.append((a, b))
+    a = synth.logit_rows(seed, 0, w["logit_rows"], v)
+    b, _, _ = synth.inject_ulp(seed, 99, a, frac)
+    host.append((a, b))
+
+    def dev(x):
+        if x.dtype == np.uint16:
+            return torch.from_numpy(x.view(np.int16)).cuda().view(torch.bfloat16)
+        return torch.from_numpy(x).cuda()
+
+    copies = args.copies or COPIES["sweep"]
+    sets = [[(dev(a), dev(b)) for a, b in host] for _ in range(copies)]
+    torch.cuda.synchronize()
+    log(f"[bench] generated and uploaded the sweep ({len(host)} shapes, {copies} copies) in "
+        f"{time.time() - t0:.1f}s")
+    shape_bytes = [a.size * a.itemsize + b.size * b.itemsize for a, b in host]
+    rows_per_step = sum(a.shape[0] for a, _ in host)
+    outs = [torch.empty((a.shape[0], L.BITDIFF_ROW_BYTES), dtype=torch.uint8, device="cuda")
+            for a, _ in host]
+    wss = [torch.empty(int(L.lib().lcmp_bitdiff_workspace_bytes(a.shape[0], a.shape[1])),
+                       dtype=torch.uint8, device="cuda") for a, _ in host]
+    hip = Hip()
+    stream = torch.cuda.current_stream()
+
+    def step(i, evs=None):
+        for j, (da, db) in enumerate(sets[i % copies]):
+            L.lcmp_bitdiff(da, db, out=outs[j], workspace=wss[j], stream=stream,
+                           events=evs and evs[j])
+
+    gpu_ms, wall, per = time_steps(step, args.steps, args.warmup, hip, torch, stream,
+                                   nev=len(host))
+    ms_per_step = gpu_ms / args.steps
+    kstats = [stats_us(p) for p in per]
+    for (a, _), st, nb in zip(host, kstats, shape_bytes):
+        log(f"[bench] {list(a.shape)} {a.dtype}: streaming kernel mean {st['mean']:.1f} us, "
+            f"median {st['median']:.1f} us, {nb / st['mean'] / 1e3:.1f} GB/s")
+    # dominant kernel: the fp32 logit rows (70 % of the bytes)
+    big = kstats[-1]
+    gbs = lambda nb, us: round(nb / us / 1e3, 1)  # noqa: E731
+    achieved = gbs(shape_bytes[-1], big["mean"])
+    kern_total_us = sum(st["mean"] for st in kstats)
+    roofline = dict(bound="hbm", achieved=achieved, peak=HBM_PEAK_GBS, unit="GB/s",
+                    frac=round(achieved / HBM_PEAK_GBS, 4), traffic=None, traffic_source=None,
+                    kernel="k_row_stats (bitwise only, fp32 [512,151936])",
+                    bytes_per_launch=shape_bytes[-1],
+                    kernel_us=dict((key, round(val, 1)) for key, val in big.items()),
+                    all_kernels_achieved=gbs(sum(shape_bytes), kern_total_us),
+                    step_achieved=gbs(sum(shape_bytes), 1e3 * ms_per_step),
+                    step_frac=round(gbs(sum(shape_bytes), 1e3 * ms_per_step) / HBM_PEAK_GBS, 4))
+    if not args.no_read_probe:
+        a_, b_ = sets[0][-1]
+        probe = read_ceiling(L, [s_[-1] for s_ in sets], hip, torch, stream)
+        roofline["read_ceiling"] = gbs(shape_bytes[-1], probe["median"])
+        roofline["frac_of_read_ceiling"] = round(achieved / roofline["read_ceiling"], 4)
+        log(f"[bench] read-only probe of the fp32 rows: median {probe['median']:.1f} us")
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        threads = oracle_threads()
+        t1 = time.perf_counter()
+        for a, b in host:
+            oracle.bitdiff(a, b, nthreads=threads)
+        dt = time.perf_counter() - t1
+        cpu = dict(value=rows_per_step / dt, unit="rows/s", cores=threads, kind="oracle",
+                   sample=f"one whole sweep step ({rows_per_step} rows), {dt:.1f} s",
+                   cpu=cpu_model())
+        log(f"[bench] cpu oracle: {cpu['value']:.1f} rows/s on {threads} threads")
+    value = rows_per_step * args.steps / (gpu_ms / 1e3)
+    return {
+        "metric": SWEEP_METRIC, "value": round(value, 1), "unit": "rows/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "u32",
+        "data": "synthetic",
+        "config": {"workload": WORKLOAD_DESC["sweep"], "path": "bitdiff",
+                   "shapes": [list(a.shape) for a, _ in host],
+                   "types": ["bf16" if a.dtype == np.uint16 else "f32" for a, _ in host],
+                   "rows_per_step": rows_per_step, "bytes_per_step": sum(shape_bytes),
+                   "arithmetic": "integer pattern compares, fp32 differences, fp64 sums",
+                   "input_copies": copies,
+                   "hbm_gbs_step": roofline["step_achieved"]},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    # the first ~15 launches run while the clocks settle under the load, so
-    # the default warm-up covers them
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=30)
-    ap.add_argument("--workload", default="corpus", choices=["corpus", "segment", "stream", "tiny"])
+    ap.add_argument("--workload", default="corpus",
+                    choices=["corpus", "segment", "stream", "tiny", "sweep"])
+    ap.add_argument("--copies", type=int, default=0,
+                    help="input copies used in turn (default: 4 for segment and sweep, else 1)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-read-probe", action="store_true")
     ap.add_argument("--copy-probe", type=int, default=0)
     ap.add_argument("--path", default="compare", choices=["compare", "record"],
                     help="compare: baseline and candidate rows, full comparison (default); "
@@ -231,110 +558,10 @@ def main():
     import synth
     import logit_distribution_diffing_amd as L
 
-    w = dict(synth.WORKLOADS[args.workload])
-    n, v, k = w["n"], w["v"], w["k"]
-    edges = list(synth.DEFAULT_EDGES)
-    base, cand, host_a, host_b = make_inputs(args.workload, w, torch)
-    esize = {"f32": 4, "bf16": 2}
-    hip = Hip()
-    evs = [(hip.event(), hip.event()) for _ in range(args.steps)]
-    stream = torch.cuda.current_stream()
-    bws = torch.empty(int(L.lib().lcmp_bin_workspace_bytes(n, 1, len(edges))), dtype=torch.uint8,
-                      device="cuda")
-    bins = torch.empty((len(edges), L.BIN_BYTES), dtype=torch.uint8, device="cuda")
-    summ = torch.empty((1, L.GROUP_SUMMARY_BYTES), dtype=torch.uint8, device="cuda")
-
-    if args.path == "compare":
-        # the streaming kernel reads both rows once
-        bytes_per_launch = n * v * (esize[w["base"]] + esize[w["cand"]])
-        out = L.alloc_compare_outputs(n, k, base.device, with_bitdiff=True)
-        ws = torch.empty(L.compare_workspace_bytes(n, v, k, True), dtype=torch.uint8,
-                         device="cuda")
-
-        def step(ev=None):
-            L.lcmp_compare_logits(base, cand, k=k, with_bitdiff=True, out=out, workspace=ws,
-                                  stream=stream, events=ev)
-            L.lcmp_bin_report(out["margin"], out["flip"], out["kl_topk"], out["kl_full"], edges,
-                              status=out["status"], workspace=bws, stream=stream, bins=bins,
-                              summary=summ)
+    if args.workload == "sweep":
+        rec = run_sweep(args, torch, L, synth)
     else:
-        # the baseline is recorded once; the timed steps read the candidate rows
-        # and the record only
-        record = L.lcmp_record_baseline(base, k_rec=k)
-        torch.cuda.synchronize()
-        del base
-        torch.cuda.empty_cache()
-        bytes_per_launch = n * v * esize[w["cand"]]
-        out = L.alloc_compare_outputs(n, k, cand.device)
-        del out["kl_full"]
-        ws = torch.empty(int(L.lib().lcmp_compare_record_workspace_bytes(n, v)),
-                         dtype=torch.uint8, device="cuda")
-
-        def step(ev=None):
-            L.lcmp_compare_record(record, cand, k=k, out=out, workspace=ws, stream=stream,
-                                  events=ev)
-            L.lcmp_bin_report(out["margin"], out["flip"], out["kl_topk"], None, edges,
-                              status=out["status"], workspace=bws, stream=stream, bins=bins,
-                              summary=summ)
-
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    t_start = torch.cuda.Event(enable_timing=True)
-    t_stop = torch.cuda.Event(enable_timing=True)
-    wall0 = time.perf_counter()
-    t_start.record(stream)
-    for i in range(args.steps):
-        step(evs[i])
-    t_stop.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - wall0
-    gpu_ms = t_start.elapsed_time(t_stop)
-    kern_ms = [hip.elapsed_ms(a, b) for a, b in evs]
-    kern_avg_s = sum(kern_ms) / len(kern_ms) / 1e3
-    ms_per_step = gpu_ms / args.steps
-    srt = sorted(kern_ms)
-    log(f"[bench] {args.steps} steps: {gpu_ms:.3f} ms on the stream, {wall * 1e3:.3f} ms wall; "
-        f"streaming kernel avg {kern_avg_s * 1e6:.1f} us (min {srt[0] * 1e3:.1f}, median "
-        f"{srt[len(srt) // 2] * 1e3:.1f}, max {srt[-1] * 1e3:.1f} us; first five "
-        f"{[round(x * 1e3) for x in kern_ms[:5]]})")
-
-    b_np, s_np = L.unpack_bins(bins, summ)
-    log(f"[bench] bins count {list(b_np[0]['count'])} flips {list(b_np[0]['flips'])} "
-        f"big-margin flips {int(s_np[0]['big_margin_flips'])}")
-
-    achieved = bytes_per_launch / kern_avg_s / 1e9
-    traffic = stored_traffic(args.workload, args.path)
-    roofline = dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBS, unit="GB/s",
-                    frac=round(achieved / HBM_PEAK_GBS, 4), traffic=traffic,
-                    kernel=PATHS[args.path]["kernel"], bytes_per_launch=bytes_per_launch)
-
-    cpu = None
-    if not args.no_cpu_baseline and host_a is not None:
-        leg = cpu_leg if args.path == "compare" else cpu_leg_record
-        cpu = leg(host_a, host_b, k, edges, args.cpu_seconds)
-        log(f"[bench] cpu oracle: {cpu['value']:.1f} positions/s on {cpu['cores']} threads")
-
-    value = n * args.steps / (gpu_ms / 1e3)
-    wdesc = {
-        "corpus": "scored corpus: 10240 positions (5 depths x 4 segments x 512) x V=151936, "
-                  "fp32 baseline / bf16 candidate",
-        "segment": "decoded segment: 512 positions x V=151936, fp32 / fp32",
-        "stream": "large stream: 65536 positions x V=151936, bf16 / bf16",
-        "tiny": "tiny compare: 64 positions x V=1024, fp32 / fp32",
-    }[args.workload]
-    rec = {
-        "metric": METRIC, "value": round(value, 1), "unit": "positions/s", "n_gpus": 1,
-        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
-        "data": "synthetic",
-        "config": {"workload": wdesc, "path": args.path, "n": n, "v": v, "k": k,
-                   "base": w["base"], "cand": w["cand"],
-                   "bitwise_stats": args.path == "compare", "margin_edges": len(edges),
-                   "hbm_gbs_step": round(bytes_per_launch / (ms_per_step / 1e3) / 1e9, 1)},
-        "roofline": roofline,
-        "cpu_baseline": cpu,
-    }
+        rec = run_compare(args, torch, L, synth)
     print(json.dumps(rec), flush=True)
 
 

@@ -156,6 +156,10 @@ const char *lcmp_strerror(int status);
  * (0 on invalid sizes).  The workspace must be 16-byte aligned. */
 size_t lcmp_compare_workspace_bytes(int64_t n, int64_t v, int k, uint32_t flags);
 
+/* The same query under the short name of the problem statement's interface:
+ * identical arguments and result. */
+size_t lcmp_workspace_bytes(int64_t n, int64_t v, int k, uint32_t flags);
+
 /*
  * Compare n teacher-forced positions: baseline row i against candidate row i,
  * the first v columns of each ([logits] 看 logits，而不是 token and 怎么比两个分布).
@@ -200,6 +204,12 @@ size_t lcmp_bitdiff_workspace_bytes(int64_t rows, int64_t cols);
 int lcmp_bitdiff(const void *a, int ta, int64_t lda, const void *b, int tb, int64_t ldb,
                  int64_t rows, int64_t cols, lcmp_bitdiff_row *out, void *workspace,
                  size_t ws_bytes, void *stream);
+
+/* Instrumented form of lcmp_bitdiff: ev_before / ev_after (hipEvent_t, may be
+ * NULL) are recorded on `stream` around the streaming kernel. */
+int lcmp_bitdiff_timed(const void *a, int ta, int64_t lda, const void *b, int tb, int64_t ldb,
+                       int64_t rows, int64_t cols, lcmp_bitdiff_row *out, void *workspace,
+                       size_t ws_bytes, void *stream, void *ev_before, void *ev_after);
 
 /* ---------------------------------------------------------------- perturbations */
 
@@ -329,6 +339,25 @@ int lcmp_bin_report(const double *margin, const uint8_t *flip, const double *kl_
                     int n_groups, int64_t n, const double *edges, int n_edges, double big_margin,
                     lcmp_bin *bins, lcmp_group_summary *summary, void *workspace,
                     size_t ws_bytes, void *stream);
+
+/* ---------------------------------------------------------------- measurement */
+
+/*
+ * Read-only reference stream for measurement, not part of the comparison: it
+ * reads the first v columns of the n row pairs exactly as lcmp_compare_logits
+ * streams them (the same chunks of each row, steps of 512 elements of each
+ * side, the same 8-byte or 16-byte non-temporal loads per lane, the next
+ * step's loads in flight) and only XORs the words, so its duration is the
+ * read time this access pattern reaches on the device.  One 32-bit word per
+ * (row, chunk) is written to the workspace, which must hold at least
+ * lcmp_compare_workspace_bytes(n, v, 1, 0) bytes.  ev_before / ev_after
+ * (hipEvent_t, may be NULL) are recorded around the kernel.
+ * Errors as lcmp_compare_logits; LCMP_EINVAL also when a row start of either
+ * tensor is not 16-byte aligned (the comparison then takes its scalar-load path).
+ */
+int lcmp_read_probe(const void *base, int tb, int64_t ld_base, const void *cand, int tc,
+                    int64_t ld_cand, int64_t n, int64_t v, void *workspace, size_t ws_bytes,
+                    void *stream, void *ev_before, void *ev_after);
 
 #ifdef __cplusplus
 }

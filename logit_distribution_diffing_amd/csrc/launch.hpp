@@ -212,5 +212,7 @@ hipError_t launch_topk_kl(const FinalArgs &a, hipStream_t stream);
 hipError_t launch_bucket_fix(const FixArgs &a, int64_t max_rows, hipStream_t stream);
 hipError_t launch_bitdiff_final(const BitsFinalArgs &a, hipStream_t stream);
 hipError_t launch_bin_reduce(const BinArgs &a, hipStream_t stream);
+hipError_t launch_read_probe(const StreamArgs &a, int ta, int tb, uint32_t *sink,
+                             hipStream_t stream);
 
 }  // namespace lcmp

@@ -181,6 +181,10 @@ size_t lcmp_compare_workspace_bytes(int64_t n, int64_t v, int k, uint32_t flags)
   return compare_layout(n, v, k, flags).total;
 }
 
+size_t lcmp_workspace_bytes(int64_t n, int64_t v, int k, uint32_t flags) {
+  return lcmp_compare_workspace_bytes(n, v, k, flags);
+}
+
 }  // extern "C"
 
 static int compare_impl(const void *base, int tb, int64_t ld_base, const void *cand, int tc,
@@ -307,9 +311,9 @@ size_t lcmp_bitdiff_workspace_bytes(int64_t rows, int64_t cols) {
   return align_up((size_t)rows * (size_t)ch.nchunks * sizeof(ChunkBits));
 }
 
-int lcmp_bitdiff(const void *a, int ta, int64_t lda, const void *b, int tb, int64_t ldb,
-                 int64_t rows, int64_t cols, lcmp_bitdiff_row *out, void *workspace,
-                 size_t ws_bytes, void *stream) {
+static int bitdiff_impl(const void *a, int ta, int64_t lda, const void *b, int tb, int64_t ldb,
+                        int64_t rows, int64_t cols, lcmp_bitdiff_row *out, void *workspace,
+                        size_t ws_bytes, void *stream, void *ev_before, void *ev_after) {
   if (!dtype_ok(ta) || !dtype_ok(tb)) return LCMP_EDTYPE;
   if (rows < 0) return LCMP_EINVAL;
   if (cols < 1 || cols > kMaxCols || rows > kMaxRows || lda < cols || ldb < cols)
@@ -333,9 +337,11 @@ int lcmp_bitdiff(const void *a, int ta, int64_t lda, const void *b, int tb, int6
   sa.kint = 2;
   sa.bits = (ChunkBits *)workspace;
   hipStream_t s = (hipStream_t)stream;
+  if (ev_before && hipEventRecord((hipEvent_t)ev_before, s) != hipSuccess) return LCMP_EHIP;
   if (launch_row_stats(sa, ta, tb, false, true, vector_ok(a, ta, lda, b, tb, ldb), s) !=
       hipSuccess)
     return LCMP_EHIP;
+  if (ev_after && hipEventRecord((hipEvent_t)ev_after, s) != hipSuccess) return LCMP_EHIP;
   BitsFinalArgs fa;
   fa.bits = sa.bits;
   fa.rows = rows;
@@ -343,6 +349,49 @@ int lcmp_bitdiff(const void *a, int ta, int64_t lda, const void *b, int tb, int6
   fa.nchunks = ch.nchunks;
   fa.out = (BitdiffRow *)out;
   if (launch_bitdiff_final(fa, s) != hipSuccess) return LCMP_EHIP;
+  return LCMP_OK;
+}
+
+int lcmp_bitdiff(const void *a, int ta, int64_t lda, const void *b, int tb, int64_t ldb,
+                 int64_t rows, int64_t cols, lcmp_bitdiff_row *out, void *workspace,
+                 size_t ws_bytes, void *stream) {
+  return bitdiff_impl(a, ta, lda, b, tb, ldb, rows, cols, out, workspace, ws_bytes, stream,
+                      nullptr, nullptr);
+}
+
+int lcmp_bitdiff_timed(const void *a, int ta, int64_t lda, const void *b, int tb, int64_t ldb,
+                       int64_t rows, int64_t cols, lcmp_bitdiff_row *out, void *workspace,
+                       size_t ws_bytes, void *stream, void *ev_before, void *ev_after) {
+  return bitdiff_impl(a, ta, lda, b, tb, ldb, rows, cols, out, workspace, ws_bytes, stream,
+                      ev_before, ev_after);
+}
+
+int lcmp_read_probe(const void *base, int tb, int64_t ld_base, const void *cand, int tc,
+                    int64_t ld_cand, int64_t n, int64_t v, void *workspace, size_t ws_bytes,
+                    void *stream, void *ev_before, void *ev_after) {
+  if (!dtype_ok(tb) || !dtype_ok(tc)) return LCMP_EDTYPE;
+  if (n < 0) return LCMP_EINVAL;
+  if (v < 2 || v > kMaxCols || n > kMaxRows || ld_base < v || ld_cand < v) return LCMP_ESHAPE;
+  if (n == 0) return LCMP_OK;
+  if (!base || !cand || !vector_ok(base, tb, ld_base, cand, tc, ld_cand)) return LCMP_EINVAL;
+  const Chunking ch = choose_chunks(n, v);
+  if (!workspace || ws_bytes < (size_t)n * (size_t)ch.nchunks * sizeof(uint32_t))
+    return LCMP_EWORKSPACE;
+  if ((uintptr_t)workspace % 16 != 0) return LCMP_EINVAL;
+  StreamArgs sa;
+  memset(&sa, 0, sizeof sa);
+  sa.a = base;
+  sa.b = cand;
+  sa.lda = ld_base;
+  sa.ldb = ld_cand;
+  sa.n = n;
+  sa.v = v;
+  sa.chunk = ch.chunk;
+  sa.nchunks = ch.nchunks;
+  hipStream_t s = (hipStream_t)stream;
+  if (ev_before && hipEventRecord((hipEvent_t)ev_before, s) != hipSuccess) return LCMP_EHIP;
+  if (launch_read_probe(sa, tb, tc, (uint32_t *)workspace, s) != hipSuccess) return LCMP_EHIP;
+  if (ev_after && hipEventRecord((hipEvent_t)ev_after, s) != hipSuccess) return LCMP_EHIP;
   return LCMP_OK;
 }
 

@@ -156,6 +156,20 @@ def corpus(seed: int, r0: int, nr: int, v: int, n_total: int, frac: float = 0.00
     return a, b
 
 
+CORPUS_DEPTHS = 5
+CORPUS_GROUPS = 2 * CORPUS_DEPTHS
+
+
+def corpus_groups(n: int = 10240) -> np.ndarray:
+    """Row group of each corpus position, for per-group margin bins: context
+    depth * 2 + 1 for a prose segment (0 for code).  Row r is depth*2048 +
+    segment*512 + position; segments 0-1 are code-like, 2-3 prose-like."""
+    r = np.arange(n, dtype=np.int64)
+    depth = r // 2048
+    prose = ((r // 512) % 4) >= 2
+    return (2 * depth + prose).astype(np.int32)
+
+
 def stream(seed: int, r0: int, nr: int, v: int, out_a=None, out_b=None):
     a = _out((nr, v), np.uint16, out_a)
     b = _out((nr, v), np.uint16, out_b)

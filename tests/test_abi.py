@@ -44,6 +44,8 @@ def test_version_and_strerror(L):
 def test_workspace_queries(L):
     lib = L.lib()
     assert lib.lcmp_compare_workspace_bytes(10240, 151936, 20, 0) > 0
+    for args in ((10240, 151936, 20, 1), (7, 1000, 64, 0), (10, 1, 20, 0), (-1, 100, 20, 0)):
+        assert lib.lcmp_workspace_bytes(*args) == lib.lcmp_compare_workspace_bytes(*args)
     a = lib.lcmp_compare_workspace_bytes(512, 151936, 20, 0)
     b = lib.lcmp_compare_workspace_bytes(512, 151936, 20, 1)
     assert b > a

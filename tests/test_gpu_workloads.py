@@ -2,10 +2,11 @@
 bench.py times (compare with fused bitwise statistics, then the margin-bin
 report), plus the margin-bin reduction on its own.
 
-Full-size rows are checked against the oracle on a sample of positions the
-oracle computes one by one; properties that hold at any size (bin totals, the
-constructed big-margin flips, identical outputs for identical rows, bitwise
-repeatability) are checked on every row.
+Every row of the decoded segment and of the scored corpus is checked against
+the oracle, and so are their margin bins (per depth x code/prose group on the
+corpus).  The large stream is generated in full; three blocks of 1024 rows
+spread over it are checked row by row, and properties that hold at any size
+(bin totals, bitwise repeatability) on every row.
 """
 import numpy as np
 import pytest
@@ -59,8 +60,9 @@ def _upload(workload, w, rows_kept, n_gen=None, blk=1024):
     return base, cand, np.array(rows, dtype=np.int64), ha, hb
 
 
-def _bench_step(base, cand, k, edges):
-    """The timed step of bench.py: compare with bitwise statistics, then bins."""
+def _bench_step(base, cand, k, edges, group=None, n_groups=1):
+    """The timed step of bench.py: compare with bitwise statistics, then bins
+    (per row group when `group` is given)."""
     import torch
     import logit_distribution_diffing_amd as L
     n = base.size(0)
@@ -68,12 +70,13 @@ def _bench_step(base, cand, k, edges):
     ws = torch.empty(L.compare_workspace_bytes(n, base.size(1), k, True), dtype=torch.uint8,
                      device="cuda")
     L.lcmp_compare_logits(base, cand, k=k, with_bitdiff=True, out=out, workspace=ws)
+    dgroup = None if group is None else torch.from_numpy(group).cuda()
     bins, summ = L.lcmp_bin_report(out["margin"], out["flip"], out["kl_topk"], out["kl_full"],
-                                   edges, status=out["status"])
+                                   edges, status=out["status"], group=dgroup, n_groups=n_groups)
     torch.cuda.synchronize()
     g = {key: val.cpu().numpy() for key, val in out.items() if key != "bitdiff"}
     g["bitdiff"] = L.unpack_bitdiff(out["bitdiff"])
-    gb, gs = L.unpack_bins(bins, summ)
+    gb, gs = L.unpack_bins(bins, summ, n_groups)
     return g, gb, gs
 
 
@@ -93,6 +96,22 @@ def _bins_total(gb, gs):
     return int(gb["count"].sum() + gs["excluded"].sum() + gs["unbinned"].sum())
 
 
+def _assert_bins_match(gb, gs, ob, os_):
+    """GPU bins of GPU rows against the oracle's bins of oracle rows: counts
+    exact; each KL sum within the sum of the per-row bars of its rows."""
+    for f in ("count", "flips", "ties", "tie_flips"):
+        assert np.array_equal(gb[f], ob[f]), f
+    for f in ("big_margin_flips", "excluded", "unbinned"):
+        assert np.array_equal(gs[f], os_[f]), f
+    for f in ("sum_kl_topk", "sum_kl_full"):
+        tol = 1e-7 * gb["count"] + 1e-4 * np.abs(ob[f])
+        assert np.all(np.abs(gb[f] - ob[f]) <= tol), f
+
+
+def _concat(parts):
+    return {key: np.concatenate([p[key] for p in parts]) for key in parts[0]}
+
+
 def test_segment_all_rows():
     """512 x 151936 fp32/fp32, every row against the oracle, bins included."""
     w = synth.WORKLOADS["segment"]
@@ -103,14 +122,7 @@ def test_segment_all_rows():
     o = oracle.compare(ha, hb, k=w["k"])
     ob, os_ = oracle.bin_report(o["margin"], o["flip"], o["kl_topk"], o["kl_full"],
                                 synth.DEFAULT_EDGES, status=o["status"])
-    for f in ("count", "flips", "ties", "tie_flips"):
-        assert np.array_equal(gb[f], ob[f]), f
-    for f in ("big_margin_flips", "excluded", "unbinned"):
-        assert np.array_equal(gs[f], os_[f]), f
-    # KL sums of GPU and oracle rows agree as the rows do
-    for f in ("sum_kl_topk", "sum_kl_full"):
-        tol = 1e-7 * gb["count"] + 1e-4 * ob[f]
-        assert np.all(np.abs(gb[f] - ob[f]) <= tol), f
+    _assert_bins_match(gb, gs, ob, os_)
 
 
 def test_corpus_rows_with_extreme_candidates():
@@ -139,27 +151,57 @@ def test_corpus_rows_with_extreme_candidates():
 
 @pytest.fixture(scope="module")
 def corpus_run():
-    """Corpus scale, 10240 x 151936 fp32/bf16, generated in full on the device."""
-    w = synth.WORKLOADS["corpus"]
-    swaps = synth.swap_rows(w["seed"], w["n"], w["swap_frac"])
-    rng = np.random.default_rng(20240)
-    extra = rng.choice(w["n"], 192, replace=False)
-    edge_rows = [0, 1, 511, 512, 2047, 2048, 4095, 4096, w["n"] - 2, w["n"] - 1]
-    kept = set(int(r) for r in np.concatenate([swaps, extra, edge_rows]))
-    base, cand, rows, ha, hb = _upload("corpus", w, kept)
-    g, gb, gs = _bench_step(base, cand, w["k"], synth.DEFAULT_EDGES)
-    g2, gb2, gs2 = _bench_step(base, cand, w["k"], synth.DEFAULT_EDGES)
-    del base, cand
+    """Corpus scale, 10240 x 151936 fp32/bf16, generated in full on the host
+    block by block and uploaded; the oracle runs on every block as it is made,
+    so the host never holds more than one block of rows."""
     import torch
+    w = synth.WORKLOADS["corpus"]
+    n, v, k = w["n"], w["v"], w["k"]
+    swaps = synth.swap_rows(w["seed"], n, w["swap_frac"])
+    groups = synth.corpus_groups(n)
+    base = torch.empty((n, v), dtype=torch.float32, device="cuda")
+    cand = torch.empty((n, v), dtype=torch.bfloat16, device="cuda")
+    o_parts, bd_parts = [], []
+    blk = 1024
+    for r0 in range(0, n, blk):
+        nr = min(blk, n - r0)
+        a, b = synth.corpus(w["seed"], r0, nr, v, n, w["swap_frac"])
+        base[r0:r0 + nr].copy_(to_device(a))
+        cand[r0:r0 + nr].copy_(to_device(b))
+        o_parts.append(oracle.compare(a, b, k=k))
+        bd_parts.append(oracle.bitdiff(a, b))
+        print(f"[gen+oracle] corpus rows {r0 + nr}/{n}", flush=True)
+    o = _concat(o_parts)
+    obd = np.concatenate(bd_parts)
+    g, gb, gs = _bench_step(base, cand, k, synth.DEFAULT_EDGES, groups, synth.CORPUS_GROUPS)
+    g2, gb2, gs2 = _bench_step(base, cand, k, synth.DEFAULT_EDGES, groups, synth.CORPUS_GROUPS)
+    del base, cand
     torch.cuda.empty_cache()
-    return dict(w=w, swaps=swaps, rows=rows, ha=ha, hb=hb, g=g, gb=gb, gs=gs, g2=g2, gb2=gb2,
-                gs2=gs2)
+    return dict(w=w, swaps=swaps, groups=groups, o=o, obd=obd, g=g, gb=gb, gs=gs, g2=g2,
+                gb2=gb2, gs2=gs2)
 
 
-def test_corpus_sampled_rows(corpus_run):
+def test_corpus_every_row(corpus_run):
+    """All 10240 positions against the oracle, element by element."""
     c = corpus_run
-    _case(f"corpus 10240x151936 f32/bf16, {len(c['rows'])} sampled rows")
-    _check_rows(c["g"], c["rows"], c["ha"], c["hb"], c["w"]["k"])
+    _case(f"corpus 10240x151936 f32/bf16, all {c['w']['n']} rows")
+    assert_compare_equal(c["g"], c["o"])
+    assert_bitdiff_equal(c["g"]["bitdiff"], c["obd"])
+
+
+def test_corpus_bins_per_group_match_oracle(corpus_run):
+    """Margin bins per context depth x code/prose group (10 groups x 6 bins):
+    the GPU report over the GPU rows equals the oracle's report over the
+    oracle's rows, counts bit for bit."""
+    c = corpus_run
+    _case("corpus bins per depth x code/prose group against the oracle")
+    o = c["o"]
+    ob, os_ = oracle.bin_report(o["margin"], o["flip"], o["kl_topk"], o["kl_full"],
+                                synth.DEFAULT_EDGES, status=o["status"], group=c["groups"],
+                                n_groups=synth.CORPUS_GROUPS)
+    _assert_bins_match(c["gb"], c["gs"], ob, os_)
+    assert np.array_equal(c["gb"]["count"].sum(axis=1) + c["gs"]["unbinned"],
+                          np.bincount(c["groups"], minlength=synth.CORPUS_GROUPS))
 
 
 def test_corpus_big_margin_flips_by_construction(corpus_run):
@@ -169,12 +211,13 @@ def test_corpus_big_margin_flips_by_construction(corpus_run):
     _case("corpus big-margin flips")
     w, g, swaps = c["w"], c["g"], c["swaps"]
     assert swaps.size == 51
-    assert int(c["gs"]["big_margin_flips"][0]) == 51
+    assert int(c["gs"]["big_margin_flips"].sum()) == 51
     assert np.all(g["flip"][swaps] == 1) and np.all(g["margin"][swaps] > 1.0)
+    big = np.flatnonzero((g["flip"] == 1) & (g["margin"] > 1.0))
+    assert np.array_equal(big, swaps)
     assert _bins_total(c["gb"], c["gs"]) == w["n"]
-    assert int(c["gs"]["excluded"][0]) == 0
+    assert int(c["gs"]["excluded"].sum()) == 0
     assert int(c["gb"]["flips"].sum()) == int(g["flip"].sum())
-    assert int(c["gb"]["count"].sum()) + int(c["gs"]["unbinned"][0]) == w["n"]
 
 
 def test_corpus_repeatable_bit_for_bit(corpus_run):
@@ -189,35 +232,54 @@ def test_corpus_repeatable_bit_for_bit(corpus_run):
     assert c["gs"].tobytes() == c["gs2"].tobytes()
 
 
-def test_stream_full_size_tiled():
-    """65536 x 151936 bf16/bf16 (about 2 x 19.9 GB resident).  The first 1024
-    seeded rows are generated on the host and tiled over all positions, so
-    every position with the same row index mod 1024 must give bit-identical
-    outputs; sampled positions across the whole range are checked against the
-    oracle.  Row offsets pass 2^32 elements, so 64-bit addressing is exercised."""
+STREAM_CHECKED_BLOCKS = (0, 37, 63)  # rows [0, 1024), [37888, 38912), [64512, 65536)
+
+
+def test_stream_full_size_real_rows():
+    """65536 x 151936 bf16/bf16 (2 x 19.9 GB resident), every row generated
+    from its own seed position as bench.py times it.  Three blocks of 1024
+    rows -- the first, one in the upper half and the last -- are checked
+    against the oracle row by row, and their margin bins (GPU report over the
+    GPU rows against the oracle's report) bit for bit.  Row offsets pass 2^32
+    elements, so 64-bit addressing is exercised."""
     import torch
+    import logit_distribution_diffing_amd as L
     w = synth.WORKLOADS["stream"]
-    _case("stream 65536x151936 bf16/bf16 (1024 seeded rows tiled)")
+    n, v, k = w["n"], w["v"], w["k"]
+    _case("stream 65536x151936 bf16/bf16, real rows")
     blk = 1024
-    base, cand, rows0, ha0, hb0 = _upload("stream", w, range(blk), n_gen=blk)
-    for r0 in range(blk, w["n"], blk):
-        base[r0:r0 + blk].copy_(base[:blk])
-        cand[r0:r0 + blk].copy_(cand[:blk])
-    g, gb, gs = _bench_step(base, cand, w["k"], synth.DEFAULT_EDGES)
+    base = torch.empty((n, v), dtype=torch.bfloat16, device="cuda")
+    cand = torch.empty((n, v), dtype=torch.bfloat16, device="cuda")
+    kept = {}
+    for q, r0 in enumerate(range(0, n, blk)):
+        a, b = synth.stream(w["seed"], r0, blk, v)
+        base[r0:r0 + blk].copy_(to_device(a))
+        cand[r0:r0 + blk].copy_(to_device(b))
+        if q in STREAM_CHECKED_BLOCKS:
+            kept[q] = (a, b)
+        if q % 8 == 7:
+            print(f"[gen] stream rows {r0 + blk}/{n}", flush=True)
+    g, gb, gs = _bench_step(base, cand, k, synth.DEFAULT_EDGES)
     del base, cand
     torch.cuda.empty_cache()
-    pos = np.array([0, 1, 1023, 1024, 28270, 28271, 28272, 32768, 50000, 65534, 65535]
-                   + list(np.random.default_rng(7).choice(w["n"], 53, replace=False)))
-    pos = np.unique(pos)
-    _check_rows(g, pos, ha0[pos % blk], hb0[pos % blk], w["k"])
-    src = np.arange(w["n"]) % blk
-    for key in g:
-        if key == "bitdiff":
-            assert g[key].tobytes() == g[key][src].tobytes(), key
-        else:
-            assert np.array_equal(g[key].view(np.uint8).reshape(w["n"], -1),
-                                  g[key][src].view(np.uint8).reshape(w["n"], -1)), key
-    assert _bins_total(gb, gs) == w["n"]
+    assert _bins_total(gb, gs) == n
+    for q in STREAM_CHECKED_BLOCKS:
+        rows = np.arange(q * blk, (q + 1) * blk)
+        ha, hb = kept[q]
+        _case(f"stream rows {rows[0]}..{rows[-1]} against the oracle")
+        sub = _select(g, rows)
+        o = oracle.compare(ha, hb, k=k)
+        assert_compare_equal(sub, o)
+        assert_bitdiff_equal(sub["bitdiff"], oracle.bitdiff(ha, hb))
+        dev = {key: torch.from_numpy(np.ascontiguousarray(sub[key])).cuda()
+               for key in ("margin", "flip", "kl_topk", "kl_full", "status")}
+        bins, summ = L.lcmp_bin_report(dev["margin"], dev["flip"], dev["kl_topk"],
+                                       dev["kl_full"], synth.DEFAULT_EDGES, status=dev["status"])
+        torch.cuda.synchronize()
+        sb, ss = L.unpack_bins(bins, summ)
+        ob, os_ = oracle.bin_report(o["margin"], o["flip"], o["kl_topk"], o["kl_full"],
+                                    synth.DEFAULT_EDGES, status=o["status"])
+        _assert_bins_match(sb, ss, ob, os_)
 
 
 @pytest.mark.parametrize("t", synth.WORKLOADS["sweep"]["t_list"])
