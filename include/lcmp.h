@@ -24,7 +24,9 @@
  *     keeps no mutable global state, is reentrant, and calls on different
  *     streams may run concurrently if their workspaces differ.  A call enqueues
  *     kernels only (no memset, no copy), so it can be captured in a HIP graph
- *     and replayed on new contents of the same buffers.
+ *     and replayed on new contents of the same buffers.  The one exception is
+ *     lcmp_compare_logits_noalloc, whose workspace is a fixed array the library
+ *     holds on each device (see there).
  *   - Work is enqueued on `stream` (a hipStream_t; NULL = the default
  *     stream) and is asynchronous: results are valid once the caller has
  *     synchronised with that stream.
@@ -46,7 +48,7 @@
 extern "C" {
 #endif
 
-#define LCMP_ABI_VERSION 3
+#define LCMP_ABI_VERSION 4
 #define LCMP_MAX_K 64       /* largest top-k */
 #define LCMP_MAX_EDGES 32   /* largest number of margin-bin edges */
 #define LCMP_MAX_GROUPS 256 /* largest number of row groups in lcmp_bin_report */
@@ -191,6 +193,31 @@ int lcmp_compare_logits_timed(const void *base, int tb, int64_t ld_base, const v
                               int64_t ld_cand, int64_t n, int64_t v, int k, uint32_t flags,
                               const lcmp_row_out *out, lcmp_bitdiff_row *bd, void *workspace,
                               size_t ws_bytes, void *stream, void *ev_before, void *ev_after);
+
+/*
+ * Allocation-free form of lcmp_compare_logits, for callers that cannot
+ * allocate device memory: code being captured into a HIP graph, tight serving
+ * loops, harnesses that forbid hipMalloc.  Identical arguments and results,
+ * minus the workspace: the call uses a scratch array of
+ * LCMP_NOALLOC_SCRATCH_BYTES that the library keeps in device memory on each
+ * device it runs on until the process ends (its address is looked up once per
+ * device, on the first call there).  The caller still owns inputs and outputs.
+ * The call allocates and frees nothing.
+ *   Limits: sizes whose workspace (lcmp_compare_workspace_bytes(n, v, k, flags))
+ *   exceeds LCMP_NOALLOC_SCRATCH_BYTES return LCMP_EWORKSPACE, before anything
+ *   is launched (at V = 151936, k = 20 with bitwise statistics every n up to
+ *   20480 fits); split larger batches into row ranges.  LCMP_EHIP if the
+ *   array's address cannot be obtained.  Other errors as lcmp_compare_logits.
+ *   Every call on a device shares that device's array: calls that overlap in
+ *   time on one device (two streams, two threads) race and give wrong results;
+ *   serialise them.  Nothing needs clearing between calls (the kernels
+ *   initialise what they read).
+ */
+#define LCMP_NOALLOC_SCRATCH_BYTES (64ull << 20) /* 64 MiB per device */
+int lcmp_compare_logits_noalloc(const void *base, int tb, int64_t ld_base, const void *cand,
+                                int tc, int64_t ld_cand, int64_t n, int64_t v, int k,
+                                uint32_t flags, const lcmp_row_out *out, lcmp_bitdiff_row *bd,
+                                void *stream);
 
 /* ---------------------------------------------------------------- bitwise */
 

@@ -29,7 +29,8 @@ LCMP_F32, LCMP_BF16 = 0, 1
 LCMP_WITH_BITDIFF = 1
 LCMP_ROW_NONFINITE, LCMP_ROW_EMPTY = 1, 2
 LCMP_MAX_K = 64
-ABI_VERSION = 3
+LCMP_NOALLOC_SCRATCH_BYTES = 64 << 20
+ABI_VERSION = 4
 LCMP_PERTURB_MANTISSA, LCMP_PERTURB_E4M3, LCMP_PERTURB_E4M3_SCALED = 0, 1, 2
 STATUS_NAMES = {0: "LCMP_OK", -1: "LCMP_EINVAL", -2: "LCMP_EDTYPE", -3: "LCMP_ESHAPE",
                 -4: "LCMP_EWORKSPACE", -5: "LCMP_EHIP", -6: "LCMP_EEDGES"}
@@ -40,7 +41,8 @@ EXPORTED = ("lcmp_abi_version", "lcmp_strerror", "lcmp_compare_workspace_bytes",
             "lcmp_bitdiff", "lcmp_bin_workspace_bytes", "lcmp_bin_report", "lcmp_perturb",
             "lcmp_record_workspace_bytes", "lcmp_record_baseline",
             "lcmp_compare_record_workspace_bytes", "lcmp_compare_record",
-            "lcmp_compare_record_timed", "lcmp_bitdiff_timed", "lcmp_read_probe")
+            "lcmp_compare_record_timed", "lcmp_bitdiff_timed", "lcmp_read_probe",
+            "lcmp_compare_logits_noalloc")
 
 
 class LcmpError(RuntimeError):
@@ -97,6 +99,9 @@ def _load():
                                         ctypes.POINTER(RowOut), vp, vp, sz, vp]
     lib.lcmp_compare_logits_timed.restype = ci
     lib.lcmp_compare_logits_timed.argtypes = lib.lcmp_compare_logits.argtypes + [vp, vp]
+    lib.lcmp_compare_logits_noalloc.restype = ci
+    lib.lcmp_compare_logits_noalloc.argtypes = [vp, ci, i64, vp, ci, i64, i64, i64, ci, u32,
+                                                ctypes.POINTER(RowOut), vp, vp]
     lib.lcmp_bitdiff_workspace_bytes.restype = sz
     lib.lcmp_bitdiff_workspace_bytes.argtypes = [i64, i64]
     lib.lcmp_bitdiff.restype = ci
@@ -310,6 +315,35 @@ def lcmp_compare_logits(base: torch.Tensor, cand: torch.Tensor, k: int = 20,
     else:
         rc = _lib.lcmp_compare_logits_timed(*args, events[0], events[1])
     _check(rc, "lcmp_compare_logits")
+    return out
+
+
+@_on_stream
+def lcmp_compare_logits_noalloc(base: torch.Tensor, cand: torch.Tensor, out: dict, k: int = 20,
+                                with_bitdiff: bool = False, v: int | None = None,
+                                target: torch.Tensor | None = None, stream=None) -> dict:
+    """lcmp_compare_logits without a workspace and without any allocation: the
+    caller passes every output tensor in `out` (see alloc_compare_outputs), and
+    the library's per-device scratch array serves as the workspace.  Calls that
+    overlap on one device race; sizes beyond the array raise LCMP_EWORKSPACE."""
+    n = base.size(0)
+    v = base.size(1) if v is None else v
+    _check_rows(base, n, v, "base")
+    _check_rows(cand, n, v, "cand")
+    flags = LCMP_WITH_BITDIFF if with_bitdiff else 0
+    _check_target(target, n)
+    _check_out(out, n, k)
+    if with_bitdiff and "bitdiff" not in out:
+        raise ValueError("with_bitdiff needs out['bitdiff']")
+    _on_gpu(("base", base), ("cand", cand), ("target", target),
+            *[(f"out[{key!r}]", t) for key, t in out.items()])
+    ptrs = dict(out, target=target)
+    ro = RowOut(*[_ptr(ptrs.get(f)) for f in ROW_OUT_FIELDS])
+    rc = _lib.lcmp_compare_logits_noalloc(base.data_ptr(), _dtype_code(base), _ld(base),
+                                          cand.data_ptr(), _dtype_code(cand), _ld(cand), n, v, k,
+                                          flags, ctypes.byref(ro), _ptr(out.get("bitdiff")),
+                                          _stream(stream))
+    _check(rc, "lcmp_compare_logits_noalloc")
     return out
 
 

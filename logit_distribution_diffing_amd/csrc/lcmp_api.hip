@@ -5,6 +5,8 @@
 #include <math.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -302,6 +304,59 @@ int lcmp_compare_logits_timed(const void *base, int tb, int64_t ld_base, const v
                               size_t ws_bytes, void *stream, void *ev_before, void *ev_after) {
   return compare_impl(base, tb, ld_base, cand, tc, ld_cand, n, v, k, flags, out, bd, workspace,
                       ws_bytes, stream, ev_before, ev_after);
+}
+
+}  // extern "C"
+
+// ---------------------------------------------------------------- allocation-free compare
+
+// The workspace of lcmp_compare_logits_noalloc: one array per device, in
+// device memory for as long as the library is loaded.  Its name is only a
+// host-side stand-in for the symbol; host code uses the device address that
+// hipGetSymbolAddress returns for the current device, kept per device below.
+static __device__ __align__(256) unsigned char scratch[LCMP_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices];  // device address of `scratch` per device, set once
+
+// Device address of this device's scratch array (nullptr on a HIP error).
+// The first call on a device looks the symbol up with that device current.
+void *scratch_of_current_device() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void *p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return nullptr;
+    g_scratch_ptr[dev] = p;
+  }
+  return g_scratch_ptr[dev];
+}
+
+}  // namespace
+
+extern "C" {
+
+int lcmp_compare_logits_noalloc(const void *base, int tb, int64_t ld_base, const void *cand,
+                                int tc, int64_t ld_cand, int64_t n, int64_t v, int k,
+                                uint32_t flags, const lcmp_row_out *out, lcmp_bitdiff_row *bd,
+                                void *stream) {
+  // the size checks of compare_impl first, so a bad shape is reported as such
+  if (!dtype_ok(tb) || !dtype_ok(tc)) return LCMP_EDTYPE;
+  if (n < 0 || (flags & ~LCMP_WITH_BITDIFF) != 0 || !out) return LCMP_EINVAL;
+  if (v < 2 || v > kMaxCols || n > kMaxRows || k < 1 || k > LCMP_MAX_K || ld_base < v ||
+      ld_cand < v)
+    return LCMP_ESHAPE;
+  if (n == 0) return compare_impl(base, tb, ld_base, cand, tc, ld_cand, n, v, k, flags, out, bd,
+                                  nullptr, 0, stream, nullptr, nullptr);
+  if (compare_layout(n, v, k, flags).total > LCMP_NOALLOC_SCRATCH_BYTES) return LCMP_EWORKSPACE;
+  void *ws = scratch_of_current_device();
+  if (!ws) return LCMP_EHIP;
+  return compare_impl(base, tb, ld_base, cand, tc, ld_cand, n, v, k, flags, out, bd, ws,
+                      LCMP_NOALLOC_SCRATCH_BYTES, stream, nullptr, nullptr);
 }
 
 size_t lcmp_bitdiff_workspace_bytes(int64_t rows, int64_t cols) {

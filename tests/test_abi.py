@@ -35,7 +35,7 @@ def test_every_declared_symbol_is_exported(L):
 
 def test_version_and_strerror(L):
     lib = L.lib()
-    assert lib.lcmp_abi_version() == 3
+    assert lib.lcmp_abi_version() == 4
     for st in (0, -1, -2, -3, -4, -5, -6):
         assert len(lib.lcmp_strerror(st)) > 0
     assert lib.lcmp_strerror(-99) == b"unknown status"
