@@ -173,9 +173,9 @@ size_t lcmp_workspace_bytes(int64_t n, int64_t v, int k, uint32_t flags);
  *   out           host struct of device output pointers (see lcmp_row_out).
  * One pass reads each row pair once.  Rows whose "other"-bucket term is
  * ill-conditioned in the one-pass sums (the candidate keeps nearly all of its
- * mass inside the baseline's top-k) are listed on the device and their two
- * buckets are summed again directly, so such rows read their pair once more;
- * ordinary rows never are.
+ * mass inside the baseline's top-k) have their two buckets summed again
+ * directly by the wave that finishes the row, so such rows read their pair
+ * once more; ordinary rows never are.
  * Returns LCMP_OK or a negative lcmp_status.
  */
 int lcmp_compare_logits(const void *base, int tb, int64_t ld_base, const void *cand, int tc,
@@ -206,7 +206,7 @@ int lcmp_compare_logits_timed(const void *base, int tb, int64_t ld_base, const v
  *   Limits: sizes whose workspace (lcmp_compare_workspace_bytes(n, v, k, flags))
  *   exceeds LCMP_NOALLOC_SCRATCH_BYTES return LCMP_EWORKSPACE, before anything
  *   is launched (at V = 151936, k = 20 with bitwise statistics every n up to
- *   20480 fits); split larger batches into row ranges.  LCMP_EHIP if the
+ *   73728 fits); split larger batches into row ranges.  LCMP_EHIP if the
  *   array's address cannot be obtained.  Other errors as lcmp_compare_logits.
  *   Every call on a device shares that device's array: calls that overlap in
  *   time on one device (two streams, two threads) race and give wrong results;

@@ -3,7 +3,7 @@
 // flips are judged per margin bin, and a flip at a large margin is a stop).
 //
 // Two levels with a fixed order, so repeated calls are bit-identical:
-//   level 1: one wave per block of 64..2048 rows (more with more bins);
+//   level 1: one wave per block of 64 rows (more for reports over 262144 rows);
 //            each 64-row batch is split by bin, every bin's values are
 //            summed with a fixed-order wave reduction and added to the block's LDS
 //            accumulator in batch order; integer counts go through LDS

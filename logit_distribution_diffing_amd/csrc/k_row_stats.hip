@@ -721,8 +721,6 @@ __attribute__((amdgpu_waves_per_eu(4, 8))) void k_row_stats(StreamArgs args) {
   const int lane = lane_id();
   const int64_t item = (int64_t)blockIdx.x * W + wid;
   if (item >= args.n * args.nchunks) return;
-  // the finalize of the same call appends to this list after the pass
-  if (item == 0 && lane == 0 && args.fix_count) *args.fix_count = 0u;
   const int64_t row = item / args.nchunks;
   const int chunk = (int)(item - row * args.nchunks);
   // column indices fit in 32 bits (the vocabulary is below 2^31)

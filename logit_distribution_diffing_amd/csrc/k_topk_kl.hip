@@ -17,8 +17,8 @@
 //   full KL    = d/s + L
 //   top-k KL   = sum_S p_i (delta_i + L) + p_o (ln(s_o / w_o) + L)
 // with s_o and w_o the two masses outside S.  When w_o is itself a small
-// difference of large sums, the row is listed for k_bucket_fix, which forms
-// s_o and w_o by summing the two buckets directly.
+// difference of large sums, the same wave sums both buckets again directly
+// over the row (bucket_direct).
 #include "common.hpp"
 #include "launch.hpp"
 #include "merge.hpp"
@@ -30,6 +30,59 @@ namespace lcmp {
 __device__ __forceinline__ void wave_fence2() {
   __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
   __builtin_amdgcn_wave_barrier();
+}
+
+__device__ __forceinline__ float load_elem(const void *p, int t, int64_t off) {
+  if (t == 1) return __uint_as_float((uint32_t)((const uint16_t *)p)[off] << 16);
+  return ((const float *)p)[off];
+}
+
+// The two masses outside the head set H (keff columns listed in h[], in any
+// order) of one row, summed directly: per side the largest value outside H
+// (log2 units: ra2, rb2), then the sum of 2^(x*kL2E - r2) in double over the
+// columns outside H.  Lane l takes columns l, l + 64, ... (ascending) and
+// walks the head, sorted ascending into hs[], alongside; the lanes are
+// combined in a fixed order.  Whole wave; returns false when a side has no
+// finite value outside H.  Rare: only rows whose one-pass bucket term is
+// ill-conditioned come here, and each reads its row pair once more.
+__device__ inline bool bucket_direct(const void *base, int tb, int64_t ldb, const void *cand,
+                                     int tc, int64_t ldc, int64_t row, int64_t v,
+                                     const int32_t *h, int keff, int32_t *hs, double &sa,
+                                     double &sb, float &ra2, float &rb2) {
+  const int lane = lane_id();
+  // sort the head indices ascending: lane j ranks its index among the keff
+  const int hj = lane < keff ? h[lane] : 0x7fffffff;
+  int rank = 0;
+  for (int i = 0; i < keff; ++i) rank += __shfl(hj, i, kWave) < hj ? 1 : 0;
+  wave_fence2();
+  if (lane < keff) hs[rank] = hj;
+  wave_fence2();
+  const int64_t ra = row * ldb, rb = row * ldc;
+  float ma = -INFINITY, mb = -INFINITY;
+  int hp = 0;
+  for (int64_t c = lane; c < v; c += kWave) {
+    while (hp < keff && hs[hp] < c) ++hp;
+    if (hp < keff && hs[hp] == c) continue;
+    ma = fmaxf(ma, load_elem(base, tb, ra + c));
+    mb = fmaxf(mb, load_elem(cand, tc, rb + c));
+  }
+  ma = uniform(wave_max(ma));
+  mb = uniform(wave_max(mb));
+  if (!(ma > -INFINITY) || !(mb > -INFINITY)) return false;
+  ra2 = ma * kL2E;
+  rb2 = mb * kL2E;  // every term below is at most 1
+  double xa = 0.0, xb = 0.0;
+  hp = 0;
+  for (int64_t c = lane; c < v; c += kWave) {
+    while (hp < keff && hs[hp] < c) ++hp;
+    if (hp < keff && hs[hp] == c) continue;
+    const float x = load_elem(base, tb, ra + c), y = load_elem(cand, tc, rb + c);
+    if (x > -INFINITY) xa += (double)__builtin_amdgcn_exp2f(fmaf(x, kL2E, -ra2));
+    if (y > -INFINITY) xb += (double)__builtin_amdgcn_exp2f(fmaf(y, kL2E, -rb2));
+  }
+  sa = wave_sum(xa);
+  sb = wave_sum(xb);
+  return true;
 }
 
 // The row's top-k slots (C * kint of them, C <= kMaxMergeChunks) are held in
@@ -224,9 +277,7 @@ __global__ __launch_bounds__(kWave) void k_topk_kl(FinalArgs a) {
   // every chunk stores min(kint, its length) entries, so the merged head is
   // full; the index test only keeps a damaged record from reading outside the row
   if (in_head && s_i[lane] >= 0 && (int64_t)s_i[lane] < a.v) {
-    const int64_t off = row * a.ldc + s_i[lane];
-    hb = a.tc == 1 ? __uint_as_float((uint32_t)((const uint16_t *)a.cand)[off] << 16)
-                   : ((const float *)a.cand)[off];
+    hb = load_elem(a.cand, a.tc, row * a.ldc + s_i[lane]);
   }
   // the normalisers' log-ratio L (uniform: every lane computes it)
   const double u = (F - D) / S;
@@ -265,67 +316,60 @@ __global__ __launch_bounds__(kWave) void k_topk_kl(FinalArgs a) {
   if (a.topk_idx)
     for (int j = lane; j < a.k; j += kWave) a.topk_idx[row * a.k + j] = j < keff ? s_i[j] : -1;
 
-  int fix_slot = -1;
-  if (lane == 0) {
-    const double lse_b = M2 * kLn2 + log(S);
-    const double kl_full = nq > 0 ? INFINITY : near ? F / S - psi(u) : D / S + L;
-    double klk;
-    if (any_head_inf) {
-      klk = INFINITY;
-    } else {
-      klk = near ? sum_pphi - psi(u) : sum_pl;
-      const int64_t n_other = a.v - keff;
-      const int64_t o_fin_a = n_other - ((int64_t)na - n_sa);
-      const int64_t o_fin_b = n_other - ((int64_t)nbi - n_sb);
-      if (o_fin_a > 0) {
-        if (o_fin_b == 0) {
-          klk = INFINITY;
-        } else {
-          const double s_o = S - sum_e;
-          const double p_o = fmax(0.0, s_o / S);
-          if (p_o > 0.0) {
-            // The bucket term needs the candidate's mass outside S, here a
-            // difference of the one-pass sums.  When that difference is
-            // small against its terms it is ill-conditioned: with the
-            // normalisers close, when the candidate keeps all but 2^-10 of
-            // the baseline's bucket share inside S (its float-accumulated
-            // parts then dominate the error); with them far apart, when the
-            // candidate's mass outside S is below 2^-30 of its total (a
-            // large head weight swamps it in double).  Such rows go to
-            // k_bucket_fix, which sums both buckets directly; the value
-            // written here stands until then.
-            bool ill;
-            if (near) {
-              double x = (u - sum_pg) / p_o;
-              ill = !(x > -1.0 + 0x1p-10);
-              if (!(x > -1.0)) x = -1.0 + 0x1p-52;
-              klk += p_o * psi(x);
-            } else {
-              ill = !(W - sum_eb > W * 0x1p-30);
-              const double w_o = fmax(W - sum_eb, W * 0x1p-52);
-              klk += p_o * (log(s_o / w_o) * units + L);
-            }
-            if (ill && a.fix && a.kl_topk) {
-              const uint32_t slot = atomicAdd(a.fix_count, 1u);
-              // the streaming pass cleared the count, so at most n rows
-              // arrive; a slot past n is dropped rather than written
-              fix_slot = (int64_t)slot < a.n ? (int)slot : -1;
-            }
-            if (fix_slot >= 0) {
-              FixEntry fe;
-              fe.row = row;
-              fe.m2 = M2;
-              fe.s = S;
-              fe.head = sum_pl;
-              fe.l = L;
-              fe.keff = keff;
-              fe.done = 0u;
-              a.fix[fix_slot] = fe;
-            }
+  // the top-k KL with its bucket term (uniform: every lane computes it)
+  const double kl_full = nq > 0 ? INFINITY : near ? F / S - psi(u) : D / S + L;
+  double klk;
+  bool ill = false;  // the bucket term must be summed directly
+  if (any_head_inf) {
+    klk = INFINITY;
+  } else {
+    klk = near ? sum_pphi - psi(u) : sum_pl;
+    const int64_t n_other = a.v - keff;
+    const int64_t o_fin_a = n_other - ((int64_t)na - n_sa);
+    const int64_t o_fin_b = n_other - ((int64_t)nbi - n_sb);
+    if (o_fin_a > 0) {
+      if (o_fin_b == 0) {
+        klk = INFINITY;
+      } else {
+        const double s_o = S - sum_e;
+        const double p_o = fmax(0.0, s_o / S);
+        if (p_o > 0.0) {
+          // The bucket term needs the candidate's mass outside S, here a
+          // difference of the one-pass sums.  When that difference is small
+          // against its terms it is ill-conditioned: with the normalisers
+          // close, when the candidate keeps all but 2^-10 of the baseline's
+          // bucket share inside S (its float-accumulated parts then dominate
+          // the error); with them far apart, when the candidate's mass
+          // outside S is below 2^-30 of its total (a large head weight swamps
+          // it in double).  Such rows sum both buckets again directly.
+          if (near) {
+            double x = (u - sum_pg) / p_o;
+            ill = !(x > -1.0 + 0x1p-10);
+            if (!(x > -1.0)) x = -1.0 + 0x1p-52;
+            klk += p_o * psi(x);
+          } else {
+            ill = !(W - sum_eb > W * 0x1p-30);
+            const double w_o = fmax(W - sum_eb, W * 0x1p-52);
+            klk += p_o * (log(s_o / w_o) * units + L);
           }
         }
       }
     }
+  }
+  if (ill && a.kl_topk) {
+    // KL_k = sum_S p_i (delta_i + L) + p_o (ln(s_o / w_o) + L), with s_o and
+    // w_o summed over the row outside S (s_i holds S; sel_idx is free now)
+    double Sa, Sb;
+    float Ma, Mb;
+    if (bucket_direct(a.base, a.tb, a.ldb, a.cand, a.tc, a.ldc, row, a.v, s_i, keff, sel_idx,
+                      Sa, Sb, Ma, Mb)) {
+      const double po = Sa * exp2((double)Ma - M2) / S;
+      const double lr = log(Sa) - log(Sb) + ((double)Ma - (double)Mb) * kLn2;
+      klk = sum_pl + po * (lr * units + L);
+    }
+  }
+  if (lane == 0) {
+    const double lse_b = M2 * kLn2 + log(S);
     if (a.kl_topk) a.kl_topk[row] = klk;
     if (a.kl_full) a.kl_full[row] = kl_full;
     if (a.margin) a.margin[row] = (double)s_a[0] - (double)s_a[1];
@@ -341,20 +385,13 @@ __global__ __launch_bounds__(kWave) void k_topk_kl(FinalArgs a) {
       const int t = a.target[row];
       double lpb = NAN, lpc = NAN;
       if (t >= 0 && (int64_t)t < a.v) {
-        const int64_t ob = row * a.ldb + t, oc = row * a.ldc + t;
-        const float xb = a.tb == 1 ? __uint_as_float((uint32_t)((const uint16_t *)a.base)[ob] << 16)
-                                   : ((const float *)a.base)[ob];
-        const float xc = a.tc == 1 ? __uint_as_float((uint32_t)((const uint16_t *)a.cand)[oc] << 16)
-                                   : ((const float *)a.cand)[oc];
-        lpb = (double)xb - lse_b;
-        lpc = (double)xc - (lse_b + L);
+        lpb = (double)load_elem(a.base, a.tb, row * a.ldb + t) - lse_b;
+        lpc = (double)load_elem(a.cand, a.tc, row * a.ldc + t) - (lse_b + L);
       }
       if (a.logp_base) a.logp_base[row] = lpb;
       if (a.logp_cand) a.logp_cand[row] = lpc;
     }
   }
-  fix_slot = __shfl(fix_slot, 0, kWave);
-  if (fix_slot >= 0 && lane < keff) a.fix_head[(int64_t)fix_slot * a.k + lane] = s_i[lane];
 }
 
 hipError_t launch_topk_kl(const FinalArgs &a, hipStream_t stream) {
@@ -370,148 +407,6 @@ hipError_t launch_topk_kl(const FinalArgs &a, hipStream_t stream) {
     hipLaunchKernelGGL((k_topk_kl<4>), grid, dim3(kWave), 0, stream, a);
   else
     hipLaunchKernelGGL((k_topk_kl<16>), grid, dim3(kWave), 0, stream, a);
-  return hipGetLastError();
-}
-
-// ---------------------------------------------------------------- exact buckets
-
-// The rows listed by k_topk_kl are cut into blocks of kFixCols columns, one
-// 256-thread block each (a strided loop over the list, whose length every
-// block reads the same way).  A block loads its 16 columns per thread at
-// once, drops the head columns, and sums 2^(x*kL2E - max) on each side
-// against the block's maxima.  The block that finishes a row last (a counter
-// per row, after a fence) merges the row's blocks in column order and
-// completes the top-k KL: sum_S p_i (delta_i + L) + p_o (ln(s_o / w_o) + L),
-// the last logarithm brought to natural units.
-constexpr int kFixBlock = 256;
-constexpr int kFixPer = kFixCols / kFixBlock;
-
-__device__ __forceinline__ float fix_load(const void *p, int t, int64_t off) {
-  if (t == 1) return __uint_as_float((uint32_t)((const uint16_t *)p)[off] << 16);
-  return ((const float *)p)[off];
-}
-
-__global__ __launch_bounds__(kFixBlock) void k_bucket_fix(FixArgs f) {
-  constexpr int kW = kFixBlock / kWave;
-  __shared__ int32_t head[kMaxK];  // ascending
-  __shared__ float red_f[2][kW];
-  __shared__ double red_d[2][kW];
-  __shared__ int s_last;
-  const int tid = threadIdx.x, lane = lane_id(), wid = tid / kWave;
-  // the list never holds more than n rows; an entry that does not name a row
-  // of the call, or a head larger than k, is skipped (every block reads the
-  // same bounds, so the loop and its barriers stay uniform)
-  const int64_t count = min((int64_t)(*f.fix_count), f.n);
-  const int64_t items = count * f.ncb;
-  for (int64_t it = blockIdx.x; it < items; it += gridDim.x) {
-    const int64_t e = it / f.ncb;
-    const int cb = (int)(it - e * f.ncb);
-    const FixEntry fe = f.fix[e];
-    if (fe.row < 0 || fe.row >= f.n || fe.keff < 1 || fe.keff > f.k) continue;
-    const int keff = fe.keff;
-    if (wid == 0) {  // order the head indices: lane j ranks its index
-      const int hj = lane < keff ? f.fix_head[e * f.k + lane] : 0x7fffffff;
-      int rank = 0;
-      for (int i = 0; i < keff; ++i) rank += __shfl(hj, i, kWave) < hj ? 1 : 0;
-      if (lane < keff) head[rank] = hj;
-    }
-    __syncthreads();
-    // this thread's columns c0 + tid + 256 j ascend with j, and so does its
-    // position in the sorted head
-    const int64_t c0 = (int64_t)cb * kFixCols + tid;
-    const int64_t ra = fe.row * f.ldb, rb = fe.row * f.ldc;
-    float xa[kFixPer], xb[kFixPer];
-#pragma unroll
-    for (int j = 0; j < kFixPer; ++j) {
-      const int64_t c = c0 + (int64_t)j * kFixBlock;
-      xa[j] = c < f.v ? fix_load(f.base, f.tb, ra + c) : -INFINITY;
-      xb[j] = c < f.v ? fix_load(f.cand, f.tc, rb + c) : -INFINITY;
-    }
-    float ma = -INFINITY, mb = -INFINITY;
-    int hp = 0;
-#pragma unroll
-    for (int j = 0; j < kFixPer; ++j) {
-      const int64_t c = c0 + (int64_t)j * kFixBlock;
-      while (hp < keff && head[hp] < c) ++hp;
-      if (hp < keff && head[hp] == c) xa[j] = xb[j] = -INFINITY;
-      ma = fmaxf(ma, xa[j]);
-      mb = fmaxf(mb, xb[j]);
-    }
-    ma = wave_max(ma);
-    mb = wave_max(mb);
-    if (lane == 0) {
-      red_f[0][wid] = ma;
-      red_f[1][wid] = mb;
-    }
-    __syncthreads();
-    ma = red_f[0][0];
-    mb = red_f[1][0];
-    for (int w = 1; w < kW; ++w) {
-      ma = fmaxf(ma, red_f[0][w]);
-      mb = fmaxf(mb, red_f[1][w]);
-    }
-    const float ra2 = ma * kL2E, rb2 = mb * kL2E;  // every term below is at most 1
-    double sa = 0.0, sb = 0.0;
-#pragma unroll
-    for (int j = 0; j < kFixPer; ++j) {
-      if (xa[j] > -INFINITY) sa += (double)__builtin_amdgcn_exp2f(fmaf(xa[j], kL2E, -ra2));
-      if (xb[j] > -INFINITY) sb += (double)__builtin_amdgcn_exp2f(fmaf(xb[j], kL2E, -rb2));
-    }
-    sa = wave_sum(sa);
-    sb = wave_sum(sb);
-    if (lane == 0) {
-      red_d[0][wid] = sa;
-      red_d[1][wid] = sb;
-    }
-    __syncthreads();
-    if (tid == 0) {
-      sa = red_d[0][0];
-      sb = red_d[1][0];
-      for (int w = 1; w < kW; ++w) {
-        sa += red_d[0][w];
-        sb += red_d[1][w];
-      }
-      FixPart pt;
-      pt.ra2 = ra2;
-      pt.rb2 = rb2;
-      pt.sa = sa;
-      pt.sb = sb;
-      f.part[e * f.ncb + cb] = pt;
-      __threadfence();
-      s_last = atomicAdd(&f.fix[e].done, 1u) == (uint32_t)(f.ncb - 1);
-    }
-    __syncthreads();
-    if (s_last && tid == 0) {
-      __threadfence();
-      // the row's blocks in column order, against the largest maxima
-      double Ma = -INFINITY, Mb = -INFINITY;
-      for (int q = 0; q < f.ncb; ++q) {
-        const FixPart pq = f.part[e * f.ncb + q];
-        if (pq.sa > 0.0) Ma = fmax(Ma, (double)pq.ra2);
-        if (pq.sb > 0.0) Mb = fmax(Mb, (double)pq.rb2);
-      }
-      double Sa = 0.0, Sb = 0.0;
-      for (int q = 0; q < f.ncb; ++q) {
-        const FixPart pq = f.part[e * f.ncb + q];
-        if (pq.sa > 0.0) Sa += pq.sa * exp2((double)pq.ra2 - Ma);
-        if (pq.sb > 0.0) Sb += pq.sb * exp2((double)pq.rb2 - Mb);
-      }
-      // s_o = Sa 2^(Ma - m2) and w_o = Sb 2^(Mb - m2) against the row reference
-      const double units = 1.0 / ((double)kL2E * kLn2);
-      const double p_o = Sa * exp2(Ma - fe.m2) / fe.s;
-      const double lr = log(Sa) - log(Sb) + (Ma - Mb) * kLn2;
-      if (f.kl_topk) f.kl_topk[fe.row] = fe.head + p_o * (lr * units + fe.l);
-    }
-    __syncthreads();  // head[], the partials and s_last are reused
-  }
-}
-
-hipError_t launch_bucket_fix(const FixArgs &a, int64_t max_rows, hipStream_t stream) {
-  if (max_rows == 0) return hipSuccess;
-  const int64_t most = max_rows * a.ncb;
-  // one block per CU loops over the list: an empty list costs one small launch
-  const unsigned blocks = (unsigned)(most < 256 ? most : 256);
-  hipLaunchKernelGGL(k_bucket_fix, dim3(blocks), dim3(kFixBlock), 0, stream, a);
   return hipGetLastError();
 }
 

@@ -21,29 +21,7 @@ struct StreamArgs {
   ChunkBits *bits;    // [n * nchunks]  (bitwise)
   float *ta;          // [n * nchunks * kint] top-k candidate values and indices
   int32_t *ti;
-  uint32_t *fix_count;  // cleared by the first wave (NULL: none)
 };
-
-// A row whose "other"-bucket term of the top-k KL is ill-conditioned in the
-// one-pass sums (the candidate keeps almost all of its mass inside the
-// baseline's top-k): k_bucket_fix recomputes both bucket masses directly.
-struct FixEntry {
-  int64_t row;
-  double m2;     // the row's exp2 reference (log2 units)
-  double s;      // the baseline's mass relative to m2
-  double head;   // the top-k KL without the bucket term: sum_S p_i (delta_i + L)
-  double l;      // L = lse_cand - lse_base
-  int32_t keff;  // head size
-  uint32_t done; // column blocks of k_bucket_fix finished so far
-};
-
-// One column block of a listed row: the maxima of both sides outside the head
-// (log2 units) and the sums of 2^(x*kL2E - max) there.
-struct FixPart {
-  float ra2, rb2;
-  double sa, sb;
-};
-constexpr int kFixCols = 4096;  // columns per block of k_bucket_fix
 
 // per-row merge and finalize (k_topk_kl)
 struct FinalArgs {
@@ -66,25 +44,6 @@ struct FinalArgs {
   uint8_t *flip, *status;
   int32_t *topk_idx;
   BitdiffRow *bd;
-  FixEntry *fix;      // [n] rows for k_bucket_fix (NULL: none)
-  int32_t *fix_head;  // [n * k] their head indices
-  uint32_t *fix_count;
-};
-
-// exact bucket masses of the rows listed by k_topk_kl (k_bucket_fix)
-struct FixArgs {
-  FixEntry *fix;
-  const int32_t *fix_head;
-  const uint32_t *fix_count;
-  FixPart *part;  // [n * ncb]
-  int32_t ncb;    // column blocks per row
-  int64_t n;      // rows of the call: the list holds at most n entries
-  const void *base, *cand;
-  int32_t tb, tc;
-  int64_t ldb, ldc;
-  int64_t v;
-  int32_t k;
-  double *kl_topk;
 };
 
 // per-row merge of bitwise chunks (k_bitdiff)
@@ -107,13 +66,13 @@ struct GroupAcc {
 // Largest row count of a bin report (level-1 block count stays in 32 bits).
 constexpr int64_t kMaxBinRows = (int64_t)1 << 36;  // LCMP_MAX_BIN_ROWS
 
-// Rows of one level-1 block (one wave): small blocks spread short reports over
-// many CUs; with many bins the block grows so the partials it writes stay
-// smaller than the rows it reads.
-__host__ __device__ inline int bin_rows_per_block(int nbins) {
-  int r = 64;
-  while (r < 3 * nbins && r < 2048) r *= 2;
-  return r;
+// Rows of one level-1 block (one wave): 64-row blocks spread a report over
+// many CUs; for long reports the block grows so that there are at most 4096
+// blocks (their partials stay a small fraction of the rows read).
+__host__ __device__ inline int bin_rows_per_block(int64_t n) {
+  int64_t r = 64;
+  while ((n + r - 1) / r > 4096 && r < ((int64_t)1 << 24)) r *= 2;
+  return (int)r;
 }
 constexpr int kMaxBins = 256;           // n_groups * n_edges
 constexpr int kMaxGroups = 256;
@@ -209,7 +168,6 @@ hipError_t launch_perturb(const PerturbArgs &a, hipStream_t stream);
 hipError_t launch_row_stats(const StreamArgs &a, int ta, int tb, bool cmp, bool bits, bool vec,
                             hipStream_t stream);
 hipError_t launch_topk_kl(const FinalArgs &a, hipStream_t stream);
-hipError_t launch_bucket_fix(const FixArgs &a, int64_t max_rows, hipStream_t stream);
 hipError_t launch_bitdiff_final(const BitsFinalArgs &a, hipStream_t stream);
 hipError_t launch_bin_reduce(const BinArgs &a, hipStream_t stream);
 hipError_t launch_read_probe(const StreamArgs &a, int ta, int tb, uint32_t *sink,

@@ -74,8 +74,7 @@ int kint_of(int64_t v, int k) {
 struct CompareLayout {
   Chunking ch;
   int kint;
-  size_t off_stats, off_bits, off_ta, off_ti, off_fix_count, off_fix, off_fix_head, off_fix_part;
-  int32_t fix_ncb;
+  size_t off_stats, off_bits, off_ta, off_ti;
   size_t total;
 };
 
@@ -93,16 +92,6 @@ CompareLayout compare_layout(int64_t n, int64_t v, int k, uint32_t flags) {
   o = align_up(o + items * (size_t)L.kint * sizeof(float));
   L.off_ti = o;
   o = align_up(o + items * (size_t)L.kint * sizeof(int32_t));
-  // rows whose top-k bucket is summed again (at most every row)
-  L.off_fix_count = o;
-  o = align_up(o + sizeof(uint32_t));
-  L.off_fix = o;
-  o = align_up(o + (size_t)n * sizeof(FixEntry));
-  L.off_fix_head = o;
-  o = align_up(o + (size_t)n * (size_t)k * sizeof(int32_t));
-  L.fix_ncb = (int32_t)((v + kFixCols - 1) / kFixCols);
-  L.off_fix_part = o;
-  o = align_up(o + (size_t)n * (size_t)L.fix_ncb * sizeof(FixPart));
   L.total = o;
   return L;
 }
@@ -222,7 +211,6 @@ static int compare_impl(const void *base, int tb, int64_t ld_base, const void *c
   sa.bits = with_bits ? (ChunkBits *)(ws + L.off_bits) : nullptr;
   sa.ta = (float *)(ws + L.off_ta);
   sa.ti = (int32_t *)(ws + L.off_ti);
-  sa.fix_count = (uint32_t *)(ws + L.off_fix_count);
   hipStream_t s = (hipStream_t)stream;
   if (ev_before && hipEventRecord((hipEvent_t)ev_before, s) != hipSuccess) return LCMP_EHIP;
   if (launch_row_stats(sa, tb, tc, true, with_bits, vector_ok(base, tb, ld_base, cand, tc, ld_cand),
@@ -262,29 +250,7 @@ static int compare_impl(const void *base, int tb, int64_t ld_base, const void *c
   fa.status = out->status;
   fa.topk_idx = out->topk_idx;
   fa.bd = with_bits ? (BitdiffRow *)bd : nullptr;
-  fa.fix = (FixEntry *)(ws + L.off_fix);
-  fa.fix_head = (int32_t *)(ws + L.off_fix_head);
-  fa.fix_count = sa.fix_count;
   if (launch_topk_kl(fa, s) != hipSuccess) return LCMP_EHIP;
-  if (out->kl_topk) {
-    FixArgs xa;
-    xa.fix = fa.fix;
-    xa.fix_head = fa.fix_head;
-    xa.fix_count = fa.fix_count;
-    xa.part = (FixPart *)(ws + L.off_fix_part);
-    xa.ncb = L.fix_ncb;
-    xa.n = n;
-    xa.base = base;
-    xa.cand = cand;
-    xa.tb = tb;
-    xa.tc = tc;
-    xa.ldb = ld_base;
-    xa.ldc = ld_cand;
-    xa.v = v;
-    xa.k = k;
-    xa.kl_topk = out->kl_topk;
-    if (launch_bucket_fix(xa, n, s) != hipSuccess) return LCMP_EHIP;
-  }
   return LCMP_OK;
 }
 
@@ -454,7 +420,7 @@ size_t lcmp_bin_workspace_bytes(int64_t n, int n_groups, int n_edges) {
   if (n < 0 || n > kMaxBinRows || n_groups < 1 || n_groups > kMaxGroups || n_edges < 1 || n_edges > kMaxEdges ||
       n_groups * n_edges > kMaxBins)
     return 0;
-  const int rows = bin_rows_per_block(n_groups * n_edges);
+  const int rows = bin_rows_per_block(n);
   const int64_t nblk = (n + rows - 1) / rows;
   return align_up((size_t)nblk * (size_t)n_groups * n_edges * sizeof(BinAcc)) +
          align_up((size_t)nblk * (size_t)n_groups * sizeof(GroupAcc)) + kAlign;
@@ -512,7 +478,7 @@ int lcmp_bin_report(const double *margin, const uint8_t *flip, const double *kl_
   const size_t need = lcmp_bin_workspace_bytes(n, n_groups, n_edges);
   if (!workspace || ws_bytes < need) return LCMP_EWORKSPACE;
   if ((uintptr_t)workspace % 16 != 0) return LCMP_EINVAL;
-  const int rows = bin_rows_per_block(n_groups * n_edges);
+  const int rows = bin_rows_per_block(n);
   const int64_t nblk = (n + rows - 1) / rows;
   BinArgs ba;
   memset(&ba, 0, sizeof ba);

@@ -62,11 +62,11 @@ def test_noalloc_rejects_sizes_beyond_the_array():
     import ctypes
     import logit_distribution_diffing_amd as L
     lib = L.lib()
-    n, v, k = 65536, 151936, 20
+    n, v, k = 262144, 151936, 20
     assert lib.lcmp_compare_workspace_bytes(n, v, k, 1) > L.LCMP_NOALLOC_SCRATCH_BYTES
     fake = 0x10000   # never dereferenced: the size check comes first
     rc = lib.lcmp_compare_logits_noalloc(fake, 1, v, fake, 1, v, n, v, k, 1,
                                          ctypes.byref(L.RowOut()), fake, None)
     assert rc == -4
-    assert lib.lcmp_compare_logits_noalloc(fake, 1, v, fake, 1, v, 20480, v, k, 1,
+    assert lib.lcmp_compare_logits_noalloc(fake, 1, v, fake, 1, v, 73728, v, k, 1,
                                            None, fake, None) == -1   # no out struct
