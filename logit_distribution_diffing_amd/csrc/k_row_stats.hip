@@ -72,11 +72,39 @@ struct WaveState {
   int n_bad, n_ainf, n_binf, n_qzero;
   // bitwise statistics
   int ndiff, first;  // uniform (a chunk holds fewer than 2^31 elements)
-  uint32_t max_ulp;
+  uint32_t max_ulp;  // exact path (and, without the comparison, every pair)
   float max_abs;
   double max_abs_d, sab, ssd, ssb;
   int nfa, nfb;  // uniform, as the counters above
+  // fast path with the comparison: signed differences of the ordered images,
+  // their running maximum and minimum (|difference| < 2^31 there; bf16 pairs
+  // keep one 16-bit lane per half of a word), and the per-lane count of
+  // differing patterns of bf16 pairs
+  int omax, omin;
+  s16x2 hmax, hmin;
+  uint32_t ndl;
+  // float partial sums of the fast path, added into the double sums every
+  // kFold steps, before the reference moves and at the end of the chunk
+  float ps, pd, pf, pab, psd, psb;
+  int nstep;  // steps since the last fold (uniform)
+  // one threshold below the reference gate, the top-k threshold and the
+  // candidate maximum less a margin above kPolyMax: a step whose baseline
+  // values all lie below it touches none of the three (uniform)
+  float low;
 };
+
+constexpr int kFold = 4;
+
+__device__ __forceinline__ void fold_partials(WaveState &st) {
+  st.s += (double)st.ps;
+  st.d += (double)st.pd;
+  st.f += (double)st.pf;
+  st.sab += (double)st.pab;
+  st.ssd += (double)st.psd;
+  st.ssb += (double)st.psb;
+  st.ps = st.pd = st.pf = st.pab = st.psd = st.psb = 0.0f;
+  st.nstep = 0;
+}
 
 __device__ __forceinline__ void wave_fence() {
   __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
@@ -277,6 +305,24 @@ struct Raw {
   }
 };
 
+// The four words of each side of a bf16 / bf16 step (element 2i in the low
+// half of word i, element 2i + 1 in the high half); other pairs have none.
+template <int TA, int TB>
+__device__ __forceinline__ void raw_words(const Raw<TA, TB> &r, uint32_t (&wa)[4], uint32_t (&wb)[4]) {
+  if constexpr (TA == 1 && TB == 1) {
+    wa[0] = r.a.p0.x; wa[1] = r.a.p0.y; wa[2] = r.a.p0.z; wa[3] = r.a.p0.w;
+    wb[0] = r.b.p0.x; wb[1] = r.b.p0.y; wb[2] = r.b.p0.z; wb[3] = r.b.p0.w;
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) wa[i] = wb[i] = 0u;
+  }
+}
+// The same words rebuilt from the element patterns of a checked load.
+__device__ __forceinline__ void pack_words(const uint32_t (&u)[8], uint32_t (&w)[4]) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) w[i] = (u[2 * i] >> 16) | (u[2 * i + 1] & 0xffff0000u);
+}
+
 // ---------------------------------------------------------------- LDS staging ring
 
 // Launch shape of one instantiation.  With the LDS ring, the bytes a CU keeps
@@ -379,6 +425,7 @@ __device__ __forceinline__ double phi_d(double d) {
 // fractional part of the shift goes through exp2 in float (relative error
 // near 1e-7, common to all the sums).
 __device__ __forceinline__ void rescale(WaveState &st, float gm) {
+  fold_partials(st);
   const float wm = uniform(wave_max(gm));
   const float xh = wm * kL2E;
   const bool huge = fabsf(xh) >= 268435456.0f && isfinite(xh);
@@ -428,51 +475,70 @@ __device__ __forceinline__ uint32_t ulp_exact(uint32_t ua, uint32_t ub) {
   return (int32_t)(ua ^ ub) < 0 ? cross : same;
 }
 
-// The same distance for a pair with |a - b| <= 1/8 (both finite): then a pair
-// of opposite signs has both magnitudes at most 1/8 (patterns <= 0x3e000000),
-// so |ua - ub| >= 0x42000000, while a pair of equal signs stays below
-// 0x3e000001; the size of |ua - ub| tells the two cases apart.
-template <bool W16>
-__device__ __forceinline__ uint32_t ulp_close(uint32_t ua, uint32_t ub) {
-  const uint32_t same = sad_u32(ua, ub);
-  const uint32_t cross = ua + ub + (W16 ? 0x80010000u : 0x80000001u);
-  return same >= 0x42000000u ? cross : same;
+// Signed ordered image of a pattern: magnitudes stay, negative patterns map
+// to -(magnitude + one unit), so -0 sits one unit below +0 and the distance
+// above is the absolute difference of two images.  For a pair with
+// |a - b| <= 1/8 (both finite) a pair of opposite signs has both magnitudes
+// at most 1/8, so the difference stays far inside 32 bits (and, for bf16,
+// inside 16 bits).
+__device__ __forceinline__ int32_t order32(uint32_t u) {
+  return (int32_t)(u ^ ((uint32_t)((int32_t)u >> 31) & 0x7fffffffu));
+}
+// The same for the two bf16 patterns of one word, one 16-bit lane each.
+__device__ __forceinline__ s16x2 order16x2(uint32_t w) {
+  const s16x2 t = __builtin_bit_cast(s16x2, w) >> (s16x2)15;
+  return __builtin_bit_cast(s16x2, w ^ (__builtin_bit_cast(uint32_t, t) & 0x7fff7fffu));
+}
+// Number of nonzero 16-bit lanes of a word: (x & 0x7fff) + 0x7fff carries
+// into bit 15 of its lane exactly when the low 15 bits are not all zero.
+__device__ __forceinline__ uint32_t nonzero16x2(uint32_t x) {
+  const uint32_t t = (x & 0x7fff7fffu) + 0x7fff7fffu;
+  return (uint32_t)__builtin_popcount((t | x) & 0x80008000u);
 }
 
 // ---------------------------------------------------------------- one wave step
 
 template <bool CMP, bool BITS, bool W16, bool MAPB>
 __device__ __forceinline__ void process_step(const uint32_t (&ua)[8], const uint32_t (&ub)[8],
+                                             const uint32_t (&wa)[4], const uint32_t (&wb)[4],
                                              uint32_t valid, bool tail, int base, int lane,
                                              int kint, WaveState &st, float *ba, int *bi) {
+  // bf16 pairs with the comparison: element 2i is the low half of word i of
+  // wa / wb, element 2i + 1 the high half
+  constexpr bool PACK = CMP && BITS && W16;
+  constexpr bool ORD = CMP && BITS && !W16;
   float xa[8], xb[8];
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
     xa[j] = __uint_as_float(ua[j]);
     xb[j] = __uint_as_float(ub[j]);
   }
-  float ga = 0.0f, gb = 0.0f;
+  float ga = 0.0f;
+  bool hot = false;
   if (CMP) {
     ga = max8(xa);
-    gb = max8(xb);
     // The reference follows the baseline, so its weights e never underflow
     // because the candidate runs far above it; the candidate's weights, in
     // the exact path only, are formed in double.  Before the chunk's first
     // finite baseline logit the candidate sets the reference, which then
-    // moves to the baseline, down if need be.
-    // (one call site: the sums stay in place on the common path)
-    bool need;
-    float gsel = ga;
-    if (st.seen) {
-      need = ballot(ga > st.gate) != 0;
-    } else if (ballot(ga > -INFINITY)) {
-      need = true;
-      st.seen = 1;
-    } else {
-      need = ballot(gb > st.gate) != 0;
-      gsel = gb;
+    // moves to the baseline, down if need be.  A step below st.low (always
+    // passed before the first finite baseline logit) needs none of this.
+    hot = ballot(ga >= st.low) != 0;
+    if (hot) {
+      const float gb = max8(xb);
+      bool need;
+      float gsel = ga;
+      if (st.seen) {
+        need = ballot(ga > st.gate) != 0;
+      } else if (ballot(ga > -INFINITY)) {
+        need = true;
+        st.seen = 1;
+      } else {
+        need = ballot(gb > st.gate) != 0;
+        gsel = gb;
+      }
+      if (need) rescale(st, gsel);
     }
-    if (need) rescale(st, gsel);
   }
 
   // fast path: every element finite, |delta| <= 1/8.  In the ragged last
@@ -523,42 +589,82 @@ __device__ __forceinline__ void process_step(const uint32_t (&ua)[8], const uint
   // Every special value reaches a NaN or an infinity in the checked sums:
   // with the comparison, a NaN or inf on either side makes delta NaN or
   // infinite (sab, or dg alone), a huge baseline makes sum a^2 infinite, and
-  // |delta| <= 1/8 bounds sum delta^2.
+  // |delta| <= 1/8 bounds sum delta^2.  With the bitwise statistics the one
+  // test dmax * 2^127 + (sab + ssb) <= 2^124 holds only when |delta| <= 1/8
+  // and sum a^2 <= 2^124, so kFold steps of float partials stay finite.
   // In the ragged last step a lane whose columns all lie past the end holds
   // only neutral pairs; before the chunk has a reference (every column so far
   // -inf on both sides) their weight 2^(-FLT_MAX*log2e + inf) would be +inf,
   // so such a step goes to the exact path, which skips masked columns.
-  bool ok = !tail || st.r2h > -INFINITY || !CMP;
+  // (the wave-uniform part apart, so that the ballot is the compare's own mask)
+  const bool uok = (!tail || st.r2h > -INFINITY || !CMP) && !(CMP && st.huge);
+  bool okv = true;
   if (CMP && BITS)
-    ok = ok && !st.huge && (dmax <= kPolyMax) && isfinite(sab + ssb);
+    okv = fmaf(dmax, 0x1p127f, sab + ssb) <= 0x1p124f;
   else if (CMP)
-    ok = ok && !st.huge && (dmax <= kPolyMax) && (dg == dg);
+    okv = (dmax <= kPolyMax) && (dg == dg);
   else if (BITS)
-    ok = ok && isfinite(sab + ssd + ssb);
+    okv = isfinite(sab + ssd + ssb);
+  const bool ok = uok && okv;
+  const uint64_t badm = ballot(!okv);
+  const bool any_bad = !uok || badm != 0;
+
+  // signed differences of the ordered images (bf16 pairs: two per word) and
+  // their differing-pattern count, for every lane
+  s16x2 od[4];
+  if (PACK) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      od[i] = order16x2(wa[i]) - order16x2(wb[i]);
+      st.ndl += nonzero16x2(__builtin_bit_cast(uint32_t, od[i]));
+    }
+  }
 
   if (ok) {
-    if (CMP) {
+    if (CMP && BITS) {
+      st.ps += sg;
+      st.pd += dg;
+      st.pf += fg;
+      st.pab += sab;
+      st.psd += ssd;
+      st.psb += ssb;
+    } else if (CMP) {
       st.s += (double)sg;
       st.d += (double)dg;
       st.f += (double)fg;
-    }
-    if (BITS) {
+    } else if (BITS) {
       st.sab += (double)sab;
       st.ssd += (double)ssd;
       st.ssb += (double)ssb;
-      st.max_abs = max3f(st.max_abs, dmax, dmax);
     }
-    if (CMP && BITS) {
+    if (BITS) st.max_abs = max3f(st.max_abs, dmax, dmax);
+    if (PACK) {
+      const s16x2 m0 = __builtin_elementwise_max(od[0], od[1]);
+      const s16x2 m1 = __builtin_elementwise_max(od[2], od[3]);
+      const s16x2 n0 = __builtin_elementwise_min(od[0], od[1]);
+      const s16x2 n1 = __builtin_elementwise_min(od[2], od[3]);
+      st.hmax = __builtin_elementwise_max(st.hmax, __builtin_elementwise_max(m0, m1));
+      st.hmin = __builtin_elementwise_min(st.hmin, __builtin_elementwise_min(n0, n1));
+    }
+    if (ORD) {
 #pragma unroll
-      for (int j = 0; j < 8; ++j) st.max_ulp = max(st.max_ulp, ulp_close<W16>(ua[j], ub[j]));
+      for (int j = 0; j < 8; j += 2) {
+        const int32_t o0 = (int32_t)((uint32_t)order32(ua[j]) - (uint32_t)order32(ub[j]));
+        const int32_t o1 = (int32_t)((uint32_t)order32(ua[j + 1]) - (uint32_t)order32(ub[j + 1]));
+        st.omax = max(st.omax, max(o0, o1));
+        st.omin = min(st.omin, min(o0, o1));
+      }
     }
+  }
+  if (CMP && BITS) {
+    if (++st.nstep == kFold) fold_partials(st);
   }
   // exact element-by-element path for the lanes that are not ok: special
   // values, large differences, huge logits, ragged tails.  The branch is
   // taken by the whole wave (the lanes that are ok do nothing), so the
   // counters stay wave-uniform: ballots over the lanes at work.  The weights
   // are formed in double, where neither side under- or overflows.
-  if (ballot(!ok)) {
+  if (any_bad) {
     if (CMP && BITS && !ok) {
 #pragma unroll
       for (int j = 0; j < 8; ++j) st.max_ulp = max(st.max_ulp, ulp_exact<W16>(ua[j], ub[j]));
@@ -625,7 +731,8 @@ __device__ __forceinline__ void process_step(const uint32_t (&ua)[8], const uint
     }
   }
 
-  if (CMP) {
+  if (CMP && (hot || any_bad)) {
+    const float gb = max8(xb);
     // top-k candidates: keys above the threshold go to the LDS buffer
     if (ballot(ga >= st.tau_a)) {
       // first full step: the kint-th largest of the 64 lane maxima bounds the
@@ -676,25 +783,44 @@ __device__ __forceinline__ void process_step(const uint32_t (&ua)[8], const uint
       st.bmax = wm;
       st.bidx = uniform(wave_min(li));
     }
+    // A fast-path lane's candidate values stay within kPolyMax (plus the
+    // rounding of delta) of its baseline values; a quarter covers both.
+    st.low = st.seen ? fminf(fminf(st.gate, st.tau_a), st.bmax - 0.25f) : -INFINITY;
   }
 
   if (BITS) {
-    // differing patterns (and, without the comparison, the ULP distance)
-    uint64_t any = 0;
+    if (PACK) {
+      // first differing column, until one is found
+      if (st.first < 0) {
+        const uint32_t any = __builtin_bit_cast(uint32_t, od[0]) | __builtin_bit_cast(uint32_t, od[1]) |
+                             __builtin_bit_cast(uint32_t, od[2]) | __builtin_bit_cast(uint32_t, od[3]);
+        if (ballot(any != 0)) {
+          int js = 8;  // first differing element of this lane
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const uint64_t m = ballot(ua[j] != ub[j]);
-      st.ndiff += __popcll(m);
-      any |= m;
-      if (!CMP) st.max_ulp = max(st.max_ulp, ulp_exact<W16>(ua[j], ub[j]));
-    }
-    if (st.first < 0 && any) {
-      int js = 8;  // first differing element of this lane
+          for (int j = 7; j >= 0; --j)
+            if (ua[j] != ub[j]) js = j;
+          const int li = js < 8 ? base + lane_offset_dyn<MAPB>(lane, js) : 0x7fffffff;
+          st.first = uniform(wave_min(li));
+        }
+      }
+    } else {
+      // differing patterns (and, without the comparison, the ULP distance)
+      uint64_t any = 0;
 #pragma unroll
-      for (int j = 7; j >= 0; --j)
-        if (ua[j] != ub[j]) js = j;
-      const int li = js < 8 ? base + lane_offset_dyn<MAPB>(lane, js) : 0x7fffffff;
-      st.first = uniform(wave_min(li));
+      for (int j = 0; j < 8; ++j) {
+        const uint64_t m = ballot(ua[j] != ub[j]);
+        st.ndiff += __popcll(m);
+        any |= m;
+        if (!CMP) st.max_ulp = max(st.max_ulp, ulp_exact<W16>(ua[j], ub[j]));
+      }
+      if (st.first < 0 && any) {
+        int js = 8;  // first differing element of this lane
+#pragma unroll
+        for (int j = 7; j >= 0; --j)
+          if (ua[j] != ub[j]) js = j;
+        const int li = js < 8 ? base + lane_offset_dyn<MAPB>(lane, js) : 0x7fffffff;
+        st.first = uniform(wave_min(li));
+      }
     }
   }
 }
@@ -754,6 +880,12 @@ __attribute__((amdgpu_waves_per_eu(4, 8))) void k_row_stats(StreamArgs args) {
   st.max_abs_d = 0.0;
   st.sab = st.ssd = st.ssb = 0.0;
   st.nfa = st.nfb = 0;
+  st.omax = st.omin = 0;
+  st.hmax = st.hmin = (s16x2)0;
+  st.ndl = 0u;
+  st.ps = st.pd = st.pf = st.pab = st.psd = st.psb = 0.0f;
+  st.nstep = 0;
+  st.low = -INFINITY;
 
   const int nfull = (hi - lo) / kSpan;
   if constexpr (RING) {
@@ -796,11 +928,12 @@ __attribute__((amdgpu_waves_per_eu(4, 8))) void k_row_stats(StreamArgs args) {
       Raw<TA, TB> cur;
       const char *slot = ring + rd * kStep;
       cur.load_lds(slot, slot + kStepA, (uint32_t)lane);
-      uint32_t ua[8], ub[8];
+      uint32_t ua[8], ub[8], wa[4], wb[4];
       cur.a.decode(ua);
       cur.b.decode(ub);
-      process_step<CMP, BITS, W16, MAPB>(ua, ub, 0xffu, false, lo + sp * kSpan, lane, kint, st,
-                                            ba, bi);
+      raw_words(cur, wa, wb);
+      process_step<CMP, BITS, W16, MAPB>(ua, ub, wa, wb, 0xffu, false, lo + sp * kSpan, lane, kint,
+                                         st, ba, bi);
       rd = rd + 1 == R ? 0 : rd + 1;
       wr = wr + 1 == R ? 0 : wr + 1;
     }
@@ -816,11 +949,12 @@ __attribute__((amdgpu_waves_per_eu(4, 8))) void k_row_stats(StreamArgs args) {
       r.load(pa + (int64_t)s * kStepA, pb + (int64_t)s * kStepB, (uint32_t)lane);
     };
     auto step = [&](const Raw<TA, TB> &r, int s) {
-      uint32_t ua[8], ub[8];
+      uint32_t ua[8], ub[8], wa[4], wb[4];
       r.a.decode(ua);
       r.b.decode(ub);
-      process_step<CMP, BITS, W16, MAPB>(ua, ub, 0xffu, false, lo + s * kSpan, lane, kint, st, ba,
-                                         bi);
+      raw_words(r, wa, wb);
+      process_step<CMP, BITS, W16, MAPB>(ua, ub, wa, wb, 0xffu, false, lo + s * kSpan, lane, kint, st,
+                                         ba, bi);
     };
     if (nfull > 0) fetch(r0, 0);
     int sp = 0;
@@ -836,17 +970,22 @@ __attribute__((amdgpu_waves_per_eu(4, 8))) void k_row_stats(StreamArgs args) {
 #pragma unroll 1
     for (int sp = 0; sp < nfull; ++sp) {
       const int base = lo + sp * kSpan;
-      uint32_t ua[8], ub[8];
+      uint32_t ua[8], ub[8], wa[4], wb[4];
       const uint32_t valid = load_checked<TA, TB, MAPB>(ua, ub, ra, rb, base, hi, lane);
-      process_step<CMP, BITS, W16, MAPB>(ua, ub, valid, false, base, lane, kint, st, ba, bi);
+      pack_words(ua, wa);
+      pack_words(ub, wb);
+      process_step<CMP, BITS, W16, MAPB>(ua, ub, wa, wb, valid, false, base, lane, kint, st, ba, bi);
     }
   }
   if (lo + nfull * kSpan < hi) {
     const int base = lo + nfull * kSpan;
-    uint32_t ua[8], ub[8];
+    uint32_t ua[8], ub[8], wa[4], wb[4];
     const uint32_t valid = load_checked<TA, TB, MAPB>(ua, ub, ra, rb, base, hi, lane);
-    process_step<CMP, BITS, W16, MAPB>(ua, ub, valid, true, base, lane, kint, st, ba, bi);
+    pack_words(ua, wa);
+    pack_words(ub, wb);
+    process_step<CMP, BITS, W16, MAPB>(ua, ub, wa, wb, valid, true, base, lane, kint, st, ba, bi);
   }
+  if (CMP && BITS) fold_partials(st);
 
   // ---- wave totals, fixed order.  The output pointers are read from the
   // argument segment here rather than held in scalar registers through the loop.
@@ -884,11 +1023,21 @@ __attribute__((amdgpu_waves_per_eu(4, 8))) void k_row_stats(StreamArgs args) {
   if (BITS) {
     const double sab = wave_sum(st.sab), ssd = wave_sum(st.ssd), ssb = wave_sum(st.ssb);
     const int nfa = st.nfa, nfb = st.nfb;
-    const uint32_t mu = wave_max(st.max_ulp) >> (W16 ? 16 : 0);
+    // fast-path ULP distances: the larger of the maximum and minus the minimum
+    // of the image differences (0 without the comparison)
+    uint32_t close;
+    if (W16) {
+      const int m = max(max((int)st.hmax.x, (int)st.hmax.y), -min((int)st.hmin.x, (int)st.hmin.y));
+      close = (uint32_t)m;
+    } else {
+      close = (uint32_t)max(st.omax, -st.omin);
+    }
+    const uint32_t mu = max(wave_max(st.max_ulp) >> (W16 ? 16 : 0), wave_max(close));
+    const int ndiff = st.ndiff + wave_sum((int)st.ndl);
     const double ma = wave_max(fmax((double)st.max_abs, st.max_abs_d));
     if (lane == 0) {
       ChunkBits cb;
-      cb.ndiff = st.ndiff;
+      cb.ndiff = ndiff;
       cb.first = st.first;
       cb.nfa = nfa;
       cb.nfb = nfb;
