@@ -17,7 +17,10 @@ Prints ONE JSON line on stdout (everything else goes to stderr):
              its own stream.  Also: the same bytes over the whole step, and over
              the duration of a read-only stream of the same inputs in the same
              access pattern (lcmp_read_probe), the read rate this pattern can
-             reach.  traffic = measured HBM bytes per launch from the rocprofv3
+             reach.  The probe runs before the warm-up steps; its untimed
+             launches (at least 0.2 s) also take the clocks from idle to their
+             loaded state, so the first timed steps do not run on ramping
+             clocks.  traffic = measured HBM bytes per launch from the rocprofv3
              FETCH_SIZE / WRITE_SIZE counters (copy-calibrated), taken from the
              committed counter summary when it was measured on the current
              kernel source and workload (traffic_source says which file), else
@@ -295,21 +298,28 @@ def time_steps(step, steps, warmup, hip, torch, stream, nev=1):
     return gpu_ms, wall, per
 
 
-def read_ceiling(L, pairs, hip, torch, stream, reps=12):
+def read_ceiling(L, pairs, hip, torch, stream, reps=12, settle_s=0.2):
     """Median duration (us) of the read-only probe over the same inputs (the
-    copies in turn), after 3 untimed launches."""
-    ws = None
+    copies in turn).  Untimed launches come first, for at least settle_s
+    seconds of wall time: the probe runs before the timed steps, and these
+    launches also bring the GPU clocks from idle to their loaded state."""
+    base0, cand0 = pairs[0]
+    ws = torch.empty(int(L.lib().lcmp_compare_workspace_bytes(base0.size(0), base0.size(1), 1, 0)),
+                     dtype=torch.uint8, device="cuda")
+    i = 0
+    t0 = time.perf_counter()
+    while i < 3 or time.perf_counter() - t0 < settle_s:
+        for _ in range(4):
+            base, cand = pairs[i % len(pairs)]
+            L.lcmp_read_probe(base, cand, workspace=ws, stream=stream)
+            i += 1
+        torch.cuda.synchronize()
     ms = []
-    for i in range(3 + reps):
-        base, cand = pairs[i % len(pairs)]
-        if ws is None:
-            ws = torch.empty(int(L.lib().lcmp_compare_workspace_bytes(base.size(0), base.size(1),
-                                                                         1, 0)),
-                             dtype=torch.uint8, device="cuda")
-        ev = (hip.event(), hip.event()) if i >= 3 else None
+    for j in range(reps):
+        base, cand = pairs[(i + j) % len(pairs)]
+        ev = (hip.event(), hip.event())
         L.lcmp_read_probe(base, cand, workspace=ws, stream=stream, events=ev)
-        if ev is not None:
-            ms.append(ev)
+        ms.append(ev)
     torch.cuda.synchronize()
     return stats_us([hip.elapsed_ms(a, b) for a, b in ms])
 
@@ -367,6 +377,10 @@ def run_compare(args, torch, L, synth):
                               status=out["status"], group=groups, n_groups=n_groups,
                               workspace=bws, stream=stream, bins=bins, summary=summ)
 
+    # the read-only probe first: its untimed launches settle the clocks
+    probe = None
+    if not args.no_read_probe and args.path == "compare":
+        probe = read_ceiling(L, pairs, hip, torch, stream)
     gpu_ms, wall, (kern_ms,) = time_steps(step, args.steps, args.warmup, hip, torch, stream)
     ks = stats_us(kern_ms)
     ms_per_step = gpu_ms / args.steps
@@ -379,9 +393,7 @@ def run_compare(args, torch, L, synth):
         f"{b_np['flips'].sum(axis=0).tolist()} big-margin flips "
         f"{int(s_np['big_margin_flips'].sum())} over {n_groups} group(s)")
 
-    probe = None
-    if not args.no_read_probe and args.path == "compare":
-        probe = read_ceiling(L, pairs, hip, torch, stream)
+    if probe is not None:
         log(f"[bench] read-only probe of the same pattern: median {probe['median']:.1f} us "
             f"({bytes_per_launch / probe['median'] / 1e3:.1f} GB/s)")
 
@@ -468,6 +480,10 @@ def run_sweep(args, torch, L, synth):
             L.lcmp_bitdiff(da, db, out=outs[j], workspace=wss[j], stream=stream,
                            events=evs and evs[j])
 
+    # the read-only probe first: its untimed launches settle the clocks
+    probe = None
+    if not args.no_read_probe:
+        probe = read_ceiling(L, [s_[-1] for s_ in sets], hip, torch, stream)
     gpu_ms, wall, per = time_steps(step, args.steps, args.warmup, hip, torch, stream,
                                    nev=len(host))
     ms_per_step = gpu_ms / args.steps
@@ -488,9 +504,7 @@ def run_sweep(args, torch, L, synth):
                     all_kernels_achieved=gbs(sum(shape_bytes), kern_total_us),
                     step_achieved=gbs(sum(shape_bytes), 1e3 * ms_per_step),
                     step_frac=round(gbs(sum(shape_bytes), 1e3 * ms_per_step) / HBM_PEAK_GBS, 4))
-    if not args.no_read_probe:
-        a_, b_ = sets[0][-1]
-        probe = read_ceiling(L, [s_[-1] for s_ in sets], hip, torch, stream)
+    if probe is not None:
         roofline["read_ceiling"] = gbs(shape_bytes[-1], probe["median"])
         roofline["frac_of_read_ceiling"] = round(achieved / roofline["read_ceiling"], 4)
         log(f"[bench] read-only probe of the fp32 rows: median {probe['median']:.1f} us")

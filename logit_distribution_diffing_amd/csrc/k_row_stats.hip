@@ -41,10 +41,8 @@ namespace lcmp {
 // whenever it holds more than kFlushAt.
 constexpr int kCapW = 8 * kWave;  // 512
 constexpr int kFlushAt = 128;
-// threshold index meaning "no index bound yet": every element at or above
-// the threshold value passes
-constexpr int kTauOpen = 0x7fffffff;
-constexpr int kTauLaneMax = 0x7ffffffe;  // same, after the lane-maxima bound was taken
+// Appends test the value alone: every element at or above the threshold
+// value passes.
 
 struct WaveState {
   // softmax sums of the fast path (per lane, double across 8-element runs)
@@ -67,7 +65,7 @@ struct WaveState {
   int bidx;
   // top-k threshold key (uniform) and buffer fill
   float tau_a;
-  int tau_i, cnt;
+  int tau_set, cnt;  // tau_set: the first full step has set a threshold
   // counters (uniform: ballot counts over the exact path)
   int n_bad, n_ainf, n_binf, n_qzero;
   // bitwise statistics
@@ -199,12 +197,11 @@ __device__ __forceinline__ void flush_candidates(float *ba, int *bi, WaveState &
   // compaction in entry order; all entries are in registers, so the buffer
   // can be overwritten freely
   wave_fence();
-  int fill = 0, tie_hi = -1;
+  int fill = 0;
 #pragma unroll
   for (int q = 0; q < kRounds; ++q) {
     if (q < per) {
       const bool keep = key[q] > T || (key[q] == T && idx[q] <= isel);
-      if (keep && key[q] == T) tie_hi = max(tie_hi, idx[q]);
       const uint64_t m = ballot(keep);
       if (keep) {
         const int pos = fill + prefix_count(m);
@@ -217,7 +214,7 @@ __device__ __forceinline__ void flush_candidates(float *ba, int *bi, WaveState &
   wave_fence();
   st.cnt = fill;
   st.tau_a = rank_key_inv(T);
-  st.tau_i = uniform(wave_max(tie_hi));
+  st.tau_set = 1;
 }
 
 // ---------------------------------------------------------------- element mapping
@@ -737,7 +734,7 @@ __device__ __forceinline__ void process_step(const uint32_t (&ua)[8], const uint
     if (ballot(ga >= st.tau_a)) {
       // first full step: the kint-th largest of the 64 lane maxima bounds the
       // chunk's kint-th key from below
-      if (st.tau_i == kTauOpen && !tail) {
+      if (!st.tau_set && !tail) {
         const uint32_t kg = rank_key(ga);
         uint32_t T = 0;
 #pragma unroll 1
@@ -746,7 +743,7 @@ __device__ __forceinline__ void process_step(const uint32_t (&ua)[8], const uint
           if (__popcll(ballot(kg >= c)) >= kint) T = c;
         }
         st.tau_a = rank_key_inv(T);
-        st.tau_i = kTauLaneMax;
+        st.tau_set = 1;
       }
       // at most 4 appends per passing lane and half step: make room first if
       // that could overflow
@@ -755,17 +752,16 @@ __device__ __forceinline__ void process_step(const uint32_t (&ua)[8], const uint
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         if (j == 4 && st.cnt + 4 * npass > kCapW) flush_candidates(ba, bi, st, kint);
-        // value test first; the index test at equal values only when some
-        // lane reaches the threshold with element j
-        if (ballot(((valid >> j) & 1u) && xa[j] >= st.tau_a)) {
-          const int idx = base + lane_offset<MAPB>(lane, j);
-          const bool pass = ((valid >> j) & 1u) &&
-                            (xa[j] > st.tau_a || (xa[j] == st.tau_a && idx < st.tau_i));
-          const uint64_t m = ballot(pass);
+        // the value test alone: an element equal to the threshold value that
+        // ranks below the threshold entry (a higher index) rides along and
+        // loses in the next reduction
+        const bool pass = ((valid >> j) & 1u) && xa[j] >= st.tau_a;
+        const uint64_t m = ballot(pass);
+        if (m) {
           if (pass) {
             const int pos = st.cnt + prefix_count(m);
             ba[pos] = xa[j];
-            bi[pos] = idx;
+            bi[pos] = base + lane_offset<MAPB>(lane, j);
           }
           st.cnt += __popcll(m);
         }
@@ -870,7 +866,7 @@ __attribute__((amdgpu_waves_per_eu(4, 8))) void k_row_stats(StreamArgs args) {
   st.bmax = -INFINITY;
   st.bidx = -1;
   st.tau_a = -INFINITY;
-  st.tau_i = kTauOpen;
+  st.tau_set = 0;
   st.cnt = 0;
   st.n_bad = st.n_ainf = st.n_binf = st.n_qzero = 0;
   st.ndiff = 0;

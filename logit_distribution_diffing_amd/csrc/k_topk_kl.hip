@@ -94,8 +94,10 @@ __global__ __launch_bounds__(kWave) void k_topk_kl(FinalArgs a) {
   constexpr int kSlotRounds = R;
   __shared__ uint32_t sel_key[kMaxK];  // the kint selected slots, in slot order
   __shared__ int32_t sel_idx[kMaxK];
+  __shared__ float sel_cv[kMaxK];      // the candidate logit at each selected index
   __shared__ float s_a[kMaxK];         // the same, value descending, index ascending
   __shared__ int32_t s_i[kMaxK];
+  __shared__ float s_b[kMaxK];
   const int lane = lane_id();
   const int64_t row = blockIdx.x;
   const int C = a.nchunks;
@@ -127,8 +129,49 @@ __global__ __launch_bounds__(kWave) void k_topk_kl(FinalArgs a) {
   if (lane < kMaxK) {
     s_a[lane] = -INFINITY;
     s_i[lane] = -1;
+    s_b[lane] = -INFINITY;
     sel_key[lane] = 0u;
     sel_idx[lane] = 0x7fffffff;
+    sel_cv[lane] = -INFINITY;
+  }
+
+  // ---- the row's top-k slots as keys.  Slot e holds entry (e mod kint) of
+  // chunk e / kint; empty slots get key 0, below every stored key.  Keys are
+  // distinct through the index, and at least kint slots are filled (every
+  // chunk stores min(kint, its length) entries).  The candidate logit at
+  // every filled slot's index is fetched here, before the selection, so its
+  // latency overlaps the merge; the index test only keeps a damaged record
+  // from reading outside the row.
+  uint32_t key[kSlotRounds];
+  int idx[kSlotRounds];
+  float cv[kSlotRounds];
+#pragma unroll
+  for (int q = 0; q < kSlotRounds; ++q) {
+    key[q] = 0u;
+    idx[q] = 0x7fffffff;
+    cv[q] = -INFINITY;
+    if (q < rounds) {
+      const int e = lane + kWave * q;
+      const int c = e / kint;
+      // chunk c's entry count, from lane c
+      const int cnt_c = __builtin_amdgcn_ds_bpermute(min(c, kWave - 1) << 2, has ? cs.cnt : 0);
+      if (e < mcap && e - c * kint < cnt_c) {
+        key[q] = rank_key(sv[q]);
+        idx[q] = sx[q];
+        if (sx[q] >= 0 && (int64_t)sx[q] < a.v) cv[q] = load_elem(a.cand, a.tc, row * a.ldc + sx[q]);
+      }
+    }
+  }
+
+  // the teacher-forced token's logits on both sides, also fetched early
+  int tgt = -1;
+  float tgt_a = NAN, tgt_b = NAN;
+  if (a.target && lane == 0) {
+    tgt = a.target[row];
+    if (tgt >= 0 && (int64_t)tgt < a.v) {
+      tgt_a = load_elem(a.base, a.tb, row * a.ldb + tgt);
+      tgt_b = load_elem(a.cand, a.tc, row * a.ldc + tgt);
+    }
   }
 
   if (a.bd) merge_bits_lanes(cb, C, a.v, a.bd + row);
@@ -181,28 +224,7 @@ __global__ __launch_bounds__(kWave) void k_topk_kl(FinalArgs a) {
   const int bx = lanes_min((has && cs.bidx >= 0 && bm == BM) ? cs.bidx : 0x7fffffff, C);
   const int top1_cand = bx == 0x7fffffff ? -1 : bx;
 
-  // ---- the row's top kint slots.  Slot e holds entry (e mod kint) of chunk
-  // e / kint; empty slots get key 0, below every stored key.  Keys are
-  // distinct through the index, and at least kint slots are filled (every
-  // chunk stores min(kint, its length) entries).
-  uint32_t key[kSlotRounds];
-  int idx[kSlotRounds];
-#pragma unroll
-  for (int q = 0; q < kSlotRounds; ++q) {
-    key[q] = 0u;
-    idx[q] = 0x7fffffff;
-    if (q < rounds) {
-      const int e = lane + kWave * q;
-      const int c = e / kint;
-      // chunk c's entry count, from lane c
-      const int cnt_c = __builtin_amdgcn_ds_bpermute(min(c, kWave - 1) << 2, has ? cs.cnt : 0);
-      if (e < mcap && e - c * kint < cnt_c) {
-        key[q] = rank_key(sv[q]);
-        idx[q] = sx[q];
-      }
-    }
-  }
-  // kint-th largest key T, one bit at a time from the top; then the ties at T
+  // ---- the row's top kint slots: the kint-th largest key T, one bit at a time from the top; then the ties at T
   // that are kept, lowest indices first
   uint32_t T = 0;
 #pragma unroll 1
@@ -249,6 +271,7 @@ __global__ __launch_bounds__(kWave) void k_topk_kl(FinalArgs a) {
       if (keep && pos < kint) {  // exactly kint are kept when kint slots are filled
         sel_key[pos] = key[q];
         sel_idx[pos] = idx[q];
+        sel_cv[pos] = cv[q];
       }
       fill += __popcll(m);
     }
@@ -256,6 +279,7 @@ __global__ __launch_bounds__(kWave) void k_topk_kl(FinalArgs a) {
   wave_fence2();
   const uint32_t kj = lane < kint ? sel_key[lane] : 0u;
   const int ij = lane < kint ? sel_idx[lane] : 0x7fffffff;
+  const float cj = lane < kint ? sel_cv[lane] : -INFINITY;
   int rank = 0;
   for (int i = 0; i < kint; ++i) {
     const uint32_t ki = (uint32_t)__builtin_amdgcn_readlane((int)kj, i);
@@ -265,6 +289,7 @@ __global__ __launch_bounds__(kWave) void k_topk_kl(FinalArgs a) {
   if (lane < kint && kj != 0u) {
     s_a[rank] = rank_key_inv(kj);
     s_i[rank] = ij;
+    s_b[rank] = cj;
   }
   wave_fence2();
 
@@ -272,13 +297,8 @@ __global__ __launch_bounds__(kWave) void k_topk_kl(FinalArgs a) {
   const int keff = (int)min((int64_t)a.k, a.v);
   const bool in_head = lane < keff;
   const float ha = in_head ? s_a[lane] : -INFINITY;
-  // gather the candidate logit at each head index
-  float hb = -INFINITY;
-  // every chunk stores min(kint, its length) entries, so the merged head is
-  // full; the index test only keeps a damaged record from reading outside the row
-  if (in_head && s_i[lane] >= 0 && (int64_t)s_i[lane] < a.v) {
-    hb = load_elem(a.cand, a.tc, row * a.ldc + s_i[lane]);
-  }
+  // the candidate logit at each head index, fetched with the slots
+  const float hb = in_head ? s_b[lane] : -INFINITY;
   // the normalisers' log-ratio L (uniform: every lane computes it)
   const double u = (F - D) / S;
   const bool near = u > -0.5 && u < 1.0;
@@ -382,11 +402,10 @@ __global__ __launch_bounds__(kWave) void k_topk_kl(FinalArgs a) {
     if (a.status) a.status[row] = 0;
     if (a.target) {
       // log-probability of the teacher-forced next token on each side
-      const int t = a.target[row];
       double lpb = NAN, lpc = NAN;
-      if (t >= 0 && (int64_t)t < a.v) {
-        lpb = (double)load_elem(a.base, a.tb, row * a.ldb + t) - lse_b;
-        lpc = (double)load_elem(a.cand, a.tc, row * a.ldc + t) - (lse_b + L);
+      if (tgt >= 0 && (int64_t)tgt < a.v) {
+        lpb = (double)tgt_a - lse_b;
+        lpc = (double)tgt_b - (lse_b + L);
       }
       if (a.logp_base) a.logp_base[row] = lpb;
       if (a.logp_cand) a.logp_cand[row] = lpc;
