@@ -56,8 +56,13 @@ def build(force: bool = False) -> str:
 def _L():
     global _lib
     if _lib is None:
-        build()
-        lib = ctypes.CDLL(_SO)
+        # SYNTH_LIB names another build of synth.c (the sanitizer test loads an
+        # instrumented one through it); by default the in-tree build
+        path = os.environ.get("SYNTH_LIB")
+        if not path:
+            build()
+            path = _SO
+        lib = ctypes.CDLL(path)
         u64, i64, vp = ctypes.c_uint64, ctypes.c_int64, ctypes.c_void_p
         lib.synth_key.restype = u64
         lib.synth_key.argtypes = [u64, u64]
