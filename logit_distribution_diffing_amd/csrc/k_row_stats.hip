@@ -135,13 +135,20 @@ __device__ __forceinline__ uint32_t sad_u32(uint32_t a, uint32_t b) {
 
 // ---------------------------------------------------------------- top-k buffer
 
-// Reduce the wave's candidate buffer (cnt > kint entries of value ba[] and
-// index bi[] in LDS) to exactly the kint largest keys -- value descending,
+// One candidate buffer entry; value and column side by side, so an append or
+// a read is one 8-byte LDS access.
+struct Cand {
+  float v;
+  int i;
+};
+
+// Reduce the wave's candidate buffer (cnt > kint (value, column) entries in
+// LDS) to exactly the kint largest keys -- value descending,
 // index ascending -- and raise the threshold to the kint-th key.  Whole wave,
 // uniform control flow.  The entries are read into registers once (lane l
 // holds entries l, l + 64, ...); the selection is a bitwise radix search with
 // one ballot per entry round and bit.
-__device__ __forceinline__ void flush_candidates(float *ba, int *bi, WaveState &st, int kint) {
+__device__ __forceinline__ void flush_candidates(Cand *cb, WaveState &st, int kint) {
   constexpr int kRounds = kCapW / kWave;
   wave_fence();
   const int lane = lane_id();
@@ -155,8 +162,9 @@ __device__ __forceinline__ void flush_candidates(float *ba, int *bi, WaveState &
     key[q] = 0u;  // below every stored key (the smallest, -inf, maps to 0x007fffff)
     idx[q] = 0x7fffffff;
     if (q < per && e < cnt) {
-      key[q] = rank_key(ba[e]);
-      idx[q] = bi[e];
+      const Cand c = cb[e];
+      key[q] = rank_key(c.v);
+      idx[q] = c.i;
     }
   }
   // kint-th largest value key, one bit at a time from the top
@@ -205,8 +213,7 @@ __device__ __forceinline__ void flush_candidates(float *ba, int *bi, WaveState &
       const uint64_t m = ballot(keep);
       if (keep) {
         const int pos = fill + prefix_count(m);
-        ba[pos] = rank_key_inv(key[q]);
-        bi[pos] = idx[q];
+        cb[pos] = Cand{rank_key_inv(key[q]), idx[q]};
       }
       fill += __popcll(m);
     }
@@ -499,7 +506,7 @@ template <bool CMP, bool BITS, bool W16, bool MAPB>
 __device__ __forceinline__ void process_step(const uint32_t (&ua)[8], const uint32_t (&ub)[8],
                                              const uint32_t (&wa)[4], const uint32_t (&wb)[4],
                                              uint32_t valid, bool tail, int base, int lane,
-                                             int kint, WaveState &st, float *ba, int *bi) {
+                                             int kint, WaveState &st, Cand *cb) {
   // bf16 pairs with the comparison: element 2i is the low half of word i of
   // wa / wb, element 2i + 1 the high half
   constexpr bool PACK = CMP && BITS && W16;
@@ -748,10 +755,10 @@ __device__ __forceinline__ void process_step(const uint32_t (&ua)[8], const uint
       // at most 4 appends per passing lane and half step: make room first if
       // that could overflow
       const int npass = __popcll(ballot(ga >= st.tau_a));
-      if (st.cnt + 4 * npass > kCapW) flush_candidates(ba, bi, st, kint);
+      if (st.cnt + 4 * npass > kCapW) flush_candidates(cb, st, kint);
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        if (j == 4 && st.cnt + 4 * npass > kCapW) flush_candidates(ba, bi, st, kint);
+        if (j == 4 && st.cnt + 4 * npass > kCapW) flush_candidates(cb, st, kint);
         // the value test alone: an element equal to the threshold value that
         // ranks below the threshold entry (a higher index) rides along and
         // loses in the next reduction
@@ -760,13 +767,12 @@ __device__ __forceinline__ void process_step(const uint32_t (&ua)[8], const uint
         if (m) {
           if (pass) {
             const int pos = st.cnt + prefix_count(m);
-            ba[pos] = xa[j];
-            bi[pos] = base + lane_offset<MAPB>(lane, j);
+            cb[pos] = Cand{xa[j], base + lane_offset<MAPB>(lane, j)};
           }
           st.cnt += __popcll(m);
         }
       }
-      if (st.cnt > kFlushAt) flush_candidates(ba, bi, st, kint);
+      if (st.cnt > kFlushAt) flush_candidates(cb, st, kint);
     }
     // candidate argmax, lowest index on ties (steps of a wave ascend in index)
     if (ballot(gb > st.bmax)) {
@@ -834,8 +840,7 @@ __attribute__((amdgpu_waves_per_eu(4, 8))) void k_row_stats(StreamArgs args) {
   constexpr bool RING = SH::RING;
   constexpr int R = SH::R, W = SH::W;
   constexpr int kRingBytes = RING ? R * SH::kStep : 16;
-  __shared__ float s_ba[W][CMP ? kCapW : 1];
-  __shared__ int s_bi[W][CMP ? kCapW : 1];
+  __shared__ Cand s_cand[W][CMP ? kCapW : 1];
   __shared__ __attribute__((aligned(16))) char s_ring[W][kRingBytes];
 
   // every quantity derived from the wave id is uniform: keep it scalar
@@ -850,8 +855,7 @@ __attribute__((amdgpu_waves_per_eu(4, 8))) void k_row_stats(StreamArgs args) {
   const int hi = (int)min(args.v, (int64_t)lo + args.chunk);
   const char *ra = (const char *)args.a + row * args.lda * SA;
   const char *rb = (const char *)args.b + row * args.ldb * SB;
-  float *ba = s_ba[wid];
-  int *bi = s_bi[wid];
+  Cand *cb = s_cand[wid];
   const int kint = args.kint;
 
   WaveState st;
@@ -929,7 +933,7 @@ __attribute__((amdgpu_waves_per_eu(4, 8))) void k_row_stats(StreamArgs args) {
       cur.b.decode(ub);
       raw_words(cur, wa, wb);
       process_step<CMP, BITS, W16, MAPB>(ua, ub, wa, wb, 0xffu, false, lo + sp * kSpan, lane, kint,
-                                         st, ba, bi);
+                                         st, cb);
       rd = rd + 1 == R ? 0 : rd + 1;
       wr = wr + 1 == R ? 0 : wr + 1;
     }
@@ -950,7 +954,7 @@ __attribute__((amdgpu_waves_per_eu(4, 8))) void k_row_stats(StreamArgs args) {
       r.b.decode(ub);
       raw_words(r, wa, wb);
       process_step<CMP, BITS, W16, MAPB>(ua, ub, wa, wb, 0xffu, false, lo + s * kSpan, lane, kint, st,
-                                         ba, bi);
+                                         cb);
     };
     if (nfull > 0) fetch(r0, 0);
     int sp = 0;
@@ -970,7 +974,7 @@ __attribute__((amdgpu_waves_per_eu(4, 8))) void k_row_stats(StreamArgs args) {
       const uint32_t valid = load_checked<TA, TB, MAPB>(ua, ub, ra, rb, base, hi, lane);
       pack_words(ua, wa);
       pack_words(ub, wb);
-      process_step<CMP, BITS, W16, MAPB>(ua, ub, wa, wb, valid, false, base, lane, kint, st, ba, bi);
+      process_step<CMP, BITS, W16, MAPB>(ua, ub, wa, wb, valid, false, base, lane, kint, st, cb);
     }
   }
   if (lo + nfull * kSpan < hi) {
@@ -979,7 +983,7 @@ __attribute__((amdgpu_waves_per_eu(4, 8))) void k_row_stats(StreamArgs args) {
     const uint32_t valid = load_checked<TA, TB, MAPB>(ua, ub, ra, rb, base, hi, lane);
     pack_words(ua, wa);
     pack_words(ub, wb);
-    process_step<CMP, BITS, W16, MAPB>(ua, ub, wa, wb, valid, true, base, lane, kint, st, ba, bi);
+    process_step<CMP, BITS, W16, MAPB>(ua, ub, wa, wb, valid, true, base, lane, kint, st, cb);
   }
   if (CMP && BITS) fold_partials(st);
 
@@ -987,12 +991,13 @@ __attribute__((amdgpu_waves_per_eu(4, 8))) void k_row_stats(StreamArgs args) {
   // argument segment here rather than held in scalar registers through the loop.
   const StreamArgs &late = *(const StreamArgs *)__builtin_amdgcn_kernarg_segment_ptr();
   if (CMP) {
-    if (st.cnt > kint) flush_candidates(ba, bi, st, kint);
+    if (st.cnt > kint) flush_candidates(cb, st, kint);
     wave_fence();
     const int64_t tk = item * kint;
     if (lane < st.cnt) {
-      late.ta[tk + lane] = ba[lane];
-      late.ti[tk + lane] = bi[lane];
+      const Cand c = cb[lane];
+      late.ta[tk + lane] = c.v;
+      late.ti[tk + lane] = c.i;
     }
     const double S = wave_sum(st.s + st.sx), D = wave_sum(st.d + st.dx),
                  F = wave_sum(st.f + st.fx);
