@@ -65,6 +65,12 @@ struct WaveState {
   int bidx;
   // top-k threshold key (uniform) and buffer fill
   float tau_a;
+  // value an element must reach to be appended: tau_a itself in the step that
+  // set it, the next float above it in later steps (later steps hold higher
+  // columns only, so an element equal to tau_a ranks below the threshold
+  // entry); tau_fresh marks a threshold set by a flush in the current step
+  float tau_cmp;
+  int tau_fresh;
   int tau_set, cnt;  // tau_set: the first full step has set a threshold
   // counters (uniform: ballot counts over the exact path)
   int n_bad, n_ainf, n_binf, n_qzero;
@@ -134,6 +140,15 @@ __device__ __forceinline__ uint32_t sad_u32(uint32_t a, uint32_t b) {
 }
 
 // ---------------------------------------------------------------- top-k buffer
+
+// The least float above x (x itself for NaN and +inf; above either zero, the
+// least positive subnormal).
+__device__ __forceinline__ float next_up(float x) {
+  if (!(x < INFINITY)) return x;
+  if (x == 0.0f) return __uint_as_float(1u);
+  const uint32_t u = __float_as_uint(x);
+  return __uint_as_float(x > 0.0f ? u + 1u : u - 1u);
+}
 
 // One candidate buffer entry; value and column side by side, so an append or
 // a read is one 8-byte LDS access.
@@ -221,6 +236,8 @@ __device__ __forceinline__ void flush_candidates(Cand *cb, WaveState &st, int ki
   wave_fence();
   st.cnt = fill;
   st.tau_a = rank_key_inv(T);
+  st.tau_cmp = st.tau_a;
+  st.tau_fresh = 1;
   st.tau_set = 1;
 }
 
@@ -750,7 +767,12 @@ __device__ __forceinline__ void process_step(const uint32_t (&ua)[8], const uint
           if (__popcll(ballot(kg >= c)) >= kint) T = c;
         }
         st.tau_a = rank_key_inv(T);
+        st.tau_cmp = st.tau_a;  // no column bound: equal values pass
         st.tau_set = 1;
+      }
+      if (st.tau_fresh) {
+        st.tau_fresh = 0;
+        st.tau_cmp = next_up(st.tau_a);
       }
       // at most 4 appends per passing lane and half step: make room first if
       // that could overflow
@@ -759,10 +781,10 @@ __device__ __forceinline__ void process_step(const uint32_t (&ua)[8], const uint
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         if (j == 4 && st.cnt + 4 * npass > kCapW) flush_candidates(cb, st, kint);
-        // the value test alone: an element equal to the threshold value that
-        // ranks below the threshold entry (a higher index) rides along and
-        // loses in the next reduction
-        const bool pass = ((valid >> j) & 1u) && xa[j] >= st.tau_a;
+        // the value test alone: in the step of a flush an element equal to
+        // the threshold value that ranks below the threshold entry (a higher
+        // column) may ride along and lose in the next reduction
+        const bool pass = ((valid >> j) & 1u) && xa[j] >= st.tau_cmp;
         const uint64_t m = ballot(pass);
         if (m) {
           if (pass) {
@@ -870,6 +892,8 @@ __attribute__((amdgpu_waves_per_eu(4, 8))) void k_row_stats(StreamArgs args) {
   st.bmax = -INFINITY;
   st.bidx = -1;
   st.tau_a = -INFINITY;
+  st.tau_cmp = -INFINITY;
+  st.tau_fresh = 0;
   st.tau_set = 0;
   st.cnt = 0;
   st.n_bad = st.n_ainf = st.n_binf = st.n_qzero = 0;

@@ -226,6 +226,35 @@ def test_last_chunk_masked_on_both_sides(tb, tc, v, masked):
     assert_bitdiff_equal(g["bitdiff"], oracle.bitdiff(a, b))
 
 
+@pytest.mark.parametrize("tb,tc", [("f32", "f32"), ("bf16", "bf16"), ("f32", "bf16")])
+@pytest.mark.parametrize("k", [1, 20, 64])
+def test_rows_with_few_finite_logits(tb, tc, k):
+    """Top-k filtered rows: only m logits of each row are finite (m from 1 to
+    200, the same columns on both sides), the rest -inf on both sides, over
+    the full vocabulary.  Most chunks then hold fewer than k finite values, so
+    the top-k threshold stays at -inf and the buffer takes -inf entries, which
+    must rank by column; ties of -inf entries decide the tail of the top-k."""
+    _case(f"few finite logits {tb}/{tc} k={k}")
+    rng = np.random.default_rng(1000 + k)
+    v = 151936
+    ms = [1, 2, 5, 19, 20, 21, 63, 64, 65, 200]
+    n = len(ms)
+    x = np.full((n, v), -np.inf, dtype=np.float32)
+    y = np.full((n, v), -np.inf, dtype=np.float32)
+    for r, m in enumerate(ms):
+        cols = rng.choice(v, m, replace=False)
+        vals = (2.0 * rng.standard_normal(m)).astype(np.float32)
+        x[r, cols] = vals
+        y[r, cols] = vals + (0.05 * rng.standard_normal(m)).astype(np.float32)
+    a = x if tb == "f32" else _bf16(x)
+    b = y if tc == "f32" else _bf16(y)
+    g = gpu_compare(a, b, k=k, with_bitdiff=True)
+    o = oracle.compare(a, b, k=k)
+    assert np.all(o["status"] == 0)
+    assert_compare_equal(g, o)
+    assert_bitdiff_equal(g["bitdiff"], oracle.bitdiff(a, b))
+
+
 @pytest.mark.parametrize("tb,tc,k", [("f32", "f32", 20), ("bf16", "bf16", 20), ("f32", "bf16", 20),
                                      ("f32", "f32", 1), ("f32", "bf16", 64)])
 def test_candidate_bucket_far_below(tb, tc, k):
