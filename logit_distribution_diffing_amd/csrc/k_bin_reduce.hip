@@ -10,6 +10,8 @@
 //            atomics (exact, order-free).
 //   level 2: one wave per bin (and per group) adds the block partials in a
 //            fixed lane-then-wave-reduction order.
+// Reports of at most 64 blocks, 64 bins and 16 groups run both levels in one
+// launch of one block (k_bin_small), with the same per-block code.
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -17,22 +19,32 @@
 
 namespace lcmp {
 
-__global__ __launch_bounds__(kWave) void k_bin_partial(BinArgs a) {
-  __shared__ double acc_kt[kMaxBins], acc_kf[kMaxBins], acc_mx[kMaxBins];
-  __shared__ unsigned long long cnt[kMaxBins][4];
-  __shared__ unsigned long long grp[kMaxGroups][3];
+// LDS accumulators of one level-1 block (one wave), for up to NB bins and NG
+// groups.
+template <int NB, int NG>
+struct BlockAcc {
+  double kt[NB], kf[NB], mx[NB];
+  unsigned long long cnt[NB][4];
+  unsigned long long grp[NG][3];
+};
+
+// Level 1 for block `blk`: its rows in batches of 64, then its partials to
+// the workspace.  One wave, all 64 lanes.
+template <int NB, int NG>
+__device__ __forceinline__ void bin_block(const BinArgs &a, int64_t blk, BlockAcc<NB, NG> &acc) {
   const int lane = lane_id();
   const int nbins = a.n_groups * a.n_edges;
   for (int t = lane; t < nbins; t += kWave) {
-    acc_kt[t] = 0.0;
-    acc_kf[t] = 0.0;
-    acc_mx[t] = -INFINITY;
-    cnt[t][0] = cnt[t][1] = cnt[t][2] = cnt[t][3] = 0ull;
+    acc.kt[t] = 0.0;
+    acc.kf[t] = 0.0;
+    acc.mx[t] = -INFINITY;
+    acc.cnt[t][0] = acc.cnt[t][1] = acc.cnt[t][2] = acc.cnt[t][3] = 0ull;
   }
-  for (int g = lane; g < a.n_groups; g += kWave) grp[g][0] = grp[g][1] = grp[g][2] = 0ull;
-  __syncthreads();
+  for (int g = lane; g < a.n_groups; g += kWave) acc.grp[g][0] = acc.grp[g][1] = acc.grp[g][2] = 0ull;
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+  __builtin_amdgcn_wave_barrier();
 
-  const int64_t r0 = (int64_t)blockIdx.x * a.rows;
+  const int64_t r0 = blk * a.rows;
   const int64_t r1 = min(a.n, r0 + a.rows);
   for (int64_t base = r0; base < r1; base += kWave) {
     const int64_t r = base + lane;
@@ -43,24 +55,24 @@ __global__ __launch_bounds__(kWave) void k_bin_partial(BinArgs a) {
       const int g = a.group ? a.group[r] : 0;
       if (g >= 0 && g < a.n_groups) {
         if (a.status && a.status[r] != 0) {
-          atomicAdd(&grp[g][1], 1ull);
+          atomicAdd(&acc.grp[g][1], 1ull);
         } else {
           const double m = a.margin[r];
           fl = a.flip[r] != 0;
-          if (fl && m > a.big_margin) atomicAdd(&grp[g][0], 1ull);
+          if (fl && m > a.big_margin) atomicAdd(&acc.grp[g][0], 1ull);
           int j = 0;
           while (j < a.n_edges && !(m < a.edges[j])) ++j;
           if (j == a.n_edges) {
-            atomicAdd(&grp[g][2], 1ull);
+            atomicAdd(&acc.grp[g][2], 1ull);
           } else {
             bin = g * a.n_edges + j;
             kt = a.kl_topk[r];
             kf = a.kl_full ? a.kl_full[r] : NAN;
             tie = (m == 0.0);
-            atomicAdd(&cnt[bin][0], 1ull);
-            if (fl) atomicAdd(&cnt[bin][1], 1ull);
-            if (tie) atomicAdd(&cnt[bin][2], 1ull);
-            if (tie && fl) atomicAdd(&cnt[bin][3], 1ull);
+            atomicAdd(&acc.cnt[bin][0], 1ull);
+            if (fl) atomicAdd(&acc.cnt[bin][1], 1ull);
+            if (tie) atomicAdd(&acc.cnt[bin][2], 1ull);
+            if (tie && fl) atomicAdd(&acc.cnt[bin][3], 1ull);
           }
         }
       }
@@ -76,41 +88,42 @@ __global__ __launch_bounds__(kWave) void k_bin_partial(BinArgs a) {
       const double skf = wave_sum(mine ? kf : 0.0);
       const double mx = wave_max(mine ? kt : -INFINITY);
       if (lane == 0) {
-        acc_kt[b] += skt;
-        acc_kf[b] += skf;
-        acc_mx[b] = fmax(acc_mx[b], mx);
+        acc.kt[b] += skt;
+        acc.kf[b] += skf;
+        acc.mx[b] = fmax(acc.mx[b], mx);
       }
     }
   }
-  __syncthreads();
-  BinAcc *pb = a.part_bins + (int64_t)blockIdx.x * nbins;
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  BinAcc *pb = a.part_bins + blk * nbins;
   for (int t = lane; t < nbins; t += kWave) {
     BinAcc o;
-    o.count = (int64_t)cnt[t][0];
-    o.flips = (int64_t)cnt[t][1];
-    o.ties = (int64_t)cnt[t][2];
-    o.tie_flips = (int64_t)cnt[t][3];
-    o.sum_kl_topk = acc_kt[t];
-    o.sum_kl_full = acc_kf[t];
-    o.max_kl_topk = acc_mx[t];
+    o.count = (int64_t)acc.cnt[t][0];
+    o.flips = (int64_t)acc.cnt[t][1];
+    o.ties = (int64_t)acc.cnt[t][2];
+    o.tie_flips = (int64_t)acc.cnt[t][3];
+    o.sum_kl_topk = acc.kt[t];
+    o.sum_kl_full = acc.kf[t];
+    o.max_kl_topk = acc.mx[t];
     pb[t] = o;
   }
-  GroupAcc *pg = a.part_groups + (int64_t)blockIdx.x * a.n_groups;
+  GroupAcc *pg = a.part_groups + blk * a.n_groups;
   for (int g = lane; g < a.n_groups; g += kWave) {
     GroupAcc o;
-    o.big_margin_flips = (int64_t)grp[g][0];
-    o.excluded = (int64_t)grp[g][1];
-    o.unbinned = (int64_t)grp[g][2];
+    o.big_margin_flips = (int64_t)acc.grp[g][0];
+    o.excluded = (int64_t)acc.grp[g][1];
+    o.unbinned = (int64_t)acc.grp[g][2];
     pg[g] = o;
   }
 }
 
-// One wave per bin (then per group): lane l adds partials l, l+64, ... in order,
-// then the fixed-order wave reduction combines the lanes.
-__global__ __launch_bounds__(kWave) void k_bin_final(BinArgs a) {
+// Level 2 for output t: bin t (t < nbins) or group t - nbins.  Lane l adds
+// partials l, l+64, ... in order, then the fixed-order wave reduction
+// combines the lanes.  One wave, all 64 lanes.
+__device__ __forceinline__ void bin_final(const BinArgs &a, int t) {
   const int lane = lane_id();
   const int nbins = a.n_groups * a.n_edges;
-  const int t = blockIdx.x;
   if (t < nbins) {
     int64_t c0 = 0, c1 = 0, c2 = 0, c3 = 0;
     double s0 = 0.0, s1 = 0.0, mx = -INFINITY;
@@ -150,7 +163,36 @@ __global__ __launch_bounds__(kWave) void k_bin_final(BinArgs a) {
   }
 }
 
+__global__ __launch_bounds__(kWave) void k_bin_partial(BinArgs a) {
+  __shared__ BlockAcc<kMaxBins, kMaxGroups> acc;
+  bin_block(a, blockIdx.x, acc);
+}
+
+// One wave per bin (then per group).
+__global__ __launch_bounds__(kWave) void k_bin_final(BinArgs a) { bin_final(a, blockIdx.x); }
+
+// Small reports in one launch: kSmallWaves waves take the level-1 blocks in
+// turn, each with its own LDS accumulators, then, after the block barrier,
+// the level-2 outputs in turn.  The same per-block and per-output code as the
+// two kernels above, so the results are the same bits.
+constexpr int kSmallWaves = 16;
+constexpr int kSmallBins = 64, kSmallGroups = 16, kSmallBlocks = 64;
+__global__ __launch_bounds__(kSmallWaves * kWave) void k_bin_small(BinArgs a) {
+  __shared__ BlockAcc<kSmallBins, kSmallGroups> acc[kSmallWaves];
+  const int w = __builtin_amdgcn_readfirstlane((int)(threadIdx.x / kWave));
+  for (int blk = w; blk < a.nblk; blk += kSmallWaves) bin_block(a, blk, acc[w]);
+  __threadfence_block();
+  __syncthreads();
+  const int nout = a.n_groups * a.n_edges + a.n_groups;
+  for (int t = w; t < nout; t += kSmallWaves) bin_final(a, t);
+}
+
 hipError_t launch_bin_reduce(const BinArgs &a, hipStream_t stream) {
+  if (a.nblk <= kSmallBlocks && a.n_groups * a.n_edges <= kSmallBins &&
+      a.n_groups <= kSmallGroups) {
+    hipLaunchKernelGGL(k_bin_small, dim3(1), dim3(kSmallWaves * kWave), 0, stream, a);
+    return hipGetLastError();
+  }
   if (a.nblk > 0) {
     hipLaunchKernelGGL(k_bin_partial, dim3((unsigned)a.nblk), dim3(kWave), 0, stream, a);
     const hipError_t e = hipGetLastError();

@@ -8,6 +8,7 @@ corpus).  The large stream is generated in full; three blocks of 1024 rows
 spread over it are checked row by row, and properties that hold at any size
 (bin totals, bitwise repeatability) on every row.
 """
+import math
 import numpy as np
 import pytest
 
@@ -355,7 +356,7 @@ def _bin_inputs(n, n_groups, edges, seed):
     return m, flip, kt, kf, status, group
 
 
-@pytest.mark.parametrize("n", [0, 1, 63, 64, 65, 255, 256, 257, 10240, 65536, 1 << 20])
+@pytest.mark.parametrize("n", [0, 1, 63, 64, 65, 255, 256, 257, 4096, 4097, 10240, 65536, 1 << 20])
 @pytest.mark.parametrize("n_groups,edges", [
     (1, synth.DEFAULT_EDGES),
     (5, synth.DEFAULT_EDGES),
@@ -388,6 +389,29 @@ def test_bin_report_parity(n, n_groups, edges):
         assert np.all(np.abs(gb[f][~inf] - ob[f][~inf]) <= BIN_SUM_REL * ob[f][~inf]), f
     assert bins.cpu().numpy().tobytes() == bins2.cpu().numpy().tobytes()
     assert summ.cpu().numpy().tobytes() == summ2.cpu().numpy().tobytes()
+
+
+def test_bin_report_one_launch_matches_two():
+    """Small reports (at most 64 blocks of rows, 64 bins, 16 groups) take a
+    one-launch path; adding a group that holds no row moves the same rows onto
+    the two-launch path.  The bins they share must be the same bits."""
+    import torch
+    import logit_distribution_diffing_amd as L
+    edges = (0.25, 0.5, 1.0, math.inf)
+    for n in (1, 700, 4096):
+        _case(f"bins one launch vs two n={n}")
+        m, flip, kt, kf, status, group = _bin_inputs(n, 16, edges, seed=n + 5)
+        group[(group < 0) | (group >= 16)] = 0
+        dev = {name: torch.from_numpy(x).cuda() for name, x in
+               (("m", m), ("flip", flip), ("kt", kt), ("kf", kf), ("st", status), ("gr", group))}
+        out = {}
+        for ng in (16, 17):
+            bins, summ = L.lcmp_bin_report(dev["m"], dev["flip"], dev["kt"], dev["kf"], edges,
+                                           status=dev["st"], group=dev["gr"], n_groups=ng)
+            out[ng] = (bins.cpu().numpy(), summ.cpu().numpy())
+        nb = 16 * len(edges)
+        assert out[16][0].tobytes() == out[17][0][:nb].tobytes()
+        assert out[16][1].tobytes() == out[17][1][:16].tobytes()
 
 
 def test_bin_report_without_full_kl():
