@@ -72,6 +72,7 @@ struct WaveState {
   float tau_cmp;
   int tau_fresh;
   int tau_set, cnt;  // tau_set: the first full step has set a threshold
+  int cbit;          // highest bit a column of the row can have
   // counters (uniform: ballot counts over the exact path)
   int n_bad, n_ainf, n_binf, n_qzero;
   // bitwise statistics
@@ -158,11 +159,18 @@ struct Cand {
 };
 
 // Reduce the wave's candidate buffer (cnt > kint (value, column) entries in
-// LDS) to exactly the kint largest keys -- value descending,
-// index ascending -- and raise the threshold to the kint-th key.  Whole wave,
-// uniform control flow.  The entries are read into registers once (lane l
-// holds entries l, l + 64, ...); the selection is a bitwise radix search with
-// one ballot per entry round and bit.
+// LDS) to exactly the kint largest keys -- value descending, index ascending
+// -- and raise the threshold to at most the kint-th key.  Whole wave, uniform
+// control flow.  The entries are read into registers once (lane l holds
+// entries l, l + 64, ...); the selection is a bitwise radix search from the
+// top bit, one ballot per entry round and bit, which stops as soon as exactly
+// kint keys lie at or above its prefix: those are the kint largest, and the
+// prefix serves as the threshold (later elements have higher columns than
+// every entry, so any value with kint entries at or above it will do).
+// A16: the values are bf16, so every key ends in 16 zero bits (positive) or
+// 16 one bits (negative) and the search stops at bit 16.
+constexpr uint32_t kKeyFinite = 0x00800000u;  // rank_key(-FLT_MAX): the lowest finite value
+template <bool A16>
 __device__ __forceinline__ void flush_candidates(Cand *cb, WaveState &st, int kint) {
   constexpr int kRounds = kCapW / kWave;
   wave_fence();
@@ -182,40 +190,56 @@ __device__ __forceinline__ void flush_candidates(Cand *cb, WaveState &st, int ki
       idx[q] = c.i;
     }
   }
-  // kint-th largest value key, one bit at a time from the top
+  // kint-th largest value key, one bit at a time from the top; early exit
+  // once the prefix T (a finite value, so that the threshold is one) has
+  // exactly kint keys at or above it
   uint32_t T = 0;
+  int nT = cnt;  // keys >= T: every stored key is above 0
+  bool early = false;
 #pragma unroll 1
-  for (int bit = 31; bit >= 0; --bit) {
+  for (int bit = 31; bit >= (A16 ? 16 : 0); --bit) {
     const uint32_t c = T | (1u << bit);
     int n = 0;
 #pragma unroll
     for (int q = 0; q < kRounds; ++q)
       if (q < per) n += __popcll(ballot(key[q] >= c));
-    if (n >= kint) T = c;
-  }
-  int ngt = 0, neq = 0;
-#pragma unroll
-  for (int q = 0; q < kRounds; ++q) {
-    if (q < per) {
-      ngt += __popcll(ballot(key[q] > T));
-      neq += __popcll(ballot(key[q] == T));
+    if (n >= kint) {
+      T = c;
+      nT = n;
+    }
+    if (nT == kint && T >= kKeyFinite) {
+      early = true;
+      break;
     }
   }
-  const int need = kint - ngt;  // >= 1 entries taken among the ties at T
-  int isel = 0x7fffffff;
-  if (neq > need) {
-    // need-th smallest index among the ties
-    uint32_t I = 0;
+  if (A16 && !early && T < 0x80000000u) T |= 0xffffu;
+  // After a full search T is the kint-th key; when more than kint entries lie
+  // at or above it, the ties at T are cut by column.
+  int isel = 0x7fffffff;  // ties at T are kept up to this column
+  if (nT > kint) {
+    int ngt = 0, neq = 0;
+#pragma unroll
+    for (int q = 0; q < kRounds; ++q) {
+      if (q < per) {
+        ngt += __popcll(ballot(key[q] > T));
+        neq += __popcll(ballot(key[q] == T));
+      }
+    }
+    const int need = kint - ngt;  // >= 1 entries taken among the ties at T
+    if (neq > need) {
+      // need-th smallest index among the ties
+      uint32_t I = 0;
 #pragma unroll 1
-    for (int bit = 30; bit >= 0; --bit) {
-      const uint32_t c = I | (1u << bit);
-      int n = 0;
+      for (int bit = st.cbit; bit >= 0; --bit) {
+        const uint32_t c = I | (1u << bit);
+        int n = 0;
 #pragma unroll
-      for (int q = 0; q < kRounds; ++q)
-        if (q < per) n += __popcll(ballot(key[q] == T && (uint32_t)idx[q] < c));
-      if (n < need) I = c;
+        for (int q = 0; q < kRounds; ++q)
+          if (q < per) n += __popcll(ballot(key[q] == T && (uint32_t)idx[q] < c));
+        if (n < need) I = c;
+      }
+      isel = (int)I;
     }
-    isel = (int)I;
   }
   // compaction in entry order; all entries are in registers, so the buffer
   // can be overwritten freely
@@ -224,9 +248,9 @@ __device__ __forceinline__ void flush_candidates(Cand *cb, WaveState &st, int ki
 #pragma unroll
   for (int q = 0; q < kRounds; ++q) {
     if (q < per) {
-      const bool keep = key[q] > T || (key[q] == T && idx[q] <= isel);
-      const uint64_t m = ballot(keep);
-      if (keep) {
+      const bool kp = key[q] > T || (key[q] == T && idx[q] <= isel);
+      const uint64_t m = ballot(kp);
+      if (kp) {
         const int pos = fill + prefix_count(m);
         cb[pos] = Cand{rank_key_inv(key[q]), idx[q]};
       }
@@ -519,7 +543,7 @@ __device__ __forceinline__ uint32_t nonzero16x2(uint32_t x) {
 
 // ---------------------------------------------------------------- one wave step
 
-template <bool CMP, bool BITS, bool W16, bool MAPB>
+template <bool CMP, bool BITS, bool W16, bool MAPB, bool A16>
 __device__ __forceinline__ void process_step(const uint32_t (&ua)[8], const uint32_t (&ub)[8],
                                              const uint32_t (&wa)[4], const uint32_t (&wb)[4],
                                              uint32_t valid, bool tail, int base, int lane,
@@ -759,13 +783,21 @@ __device__ __forceinline__ void process_step(const uint32_t (&ua)[8], const uint
       // first full step: the kint-th largest of the 64 lane maxima bounds the
       // chunk's kint-th key from below
       if (!st.tau_set && !tail) {
+        // (a prefix with exactly kint maxima at or above it bounds it too)
         const uint32_t kg = rank_key(ga);
         uint32_t T = 0;
+        bool early = false;
 #pragma unroll 1
-        for (int bit = 31; bit >= 0; --bit) {
+        for (int bit = 31; bit >= (A16 ? 16 : 0); --bit) {
           const uint32_t c = T | (1u << bit);
-          if (__popcll(ballot(kg >= c)) >= kint) T = c;
+          const int n = __popcll(ballot(kg >= c));
+          if (n >= kint) T = c;
+          if (n == kint && T >= kKeyFinite) {
+            early = true;
+            break;
+          }
         }
+        if (A16 && !early && T < 0x80000000u) T |= 0xffffu;
         st.tau_a = rank_key_inv(T);
         st.tau_cmp = st.tau_a;  // no column bound: equal values pass
         st.tau_set = 1;
@@ -777,10 +809,10 @@ __device__ __forceinline__ void process_step(const uint32_t (&ua)[8], const uint
       // at most 4 appends per passing lane and half step: make room first if
       // that could overflow
       const int npass = __popcll(ballot(ga >= st.tau_a));
-      if (st.cnt + 4 * npass > kCapW) flush_candidates(cb, st, kint);
+      if (st.cnt + 4 * npass > kCapW) flush_candidates<A16>(cb, st, kint);
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        if (j == 4 && st.cnt + 4 * npass > kCapW) flush_candidates(cb, st, kint);
+        if (j == 4 && st.cnt + 4 * npass > kCapW) flush_candidates<A16>(cb, st, kint);
         // the value test alone: in the step of a flush an element equal to
         // the threshold value that ranks below the threshold entry (a higher
         // column) may ride along and lose in the next reduction
@@ -794,7 +826,7 @@ __device__ __forceinline__ void process_step(const uint32_t (&ua)[8], const uint
           st.cnt += __popcll(m);
         }
       }
-      if (st.cnt > kFlushAt) flush_candidates(cb, st, kint);
+      if (st.cnt > kFlushAt) flush_candidates<A16>(cb, st, kint);
     }
     // candidate argmax, lowest index on ties (steps of a wave ascend in index)
     if (ballot(gb > st.bmax)) {
@@ -857,6 +889,7 @@ __attribute__((amdgpu_waves_per_eu(4, 8))) void k_row_stats(StreamArgs args) {
   using SH = Shape<TA, TB, CMP, VEC>;
   constexpr bool MAPB = (TA == 1 && TB == 1);
   constexpr bool W16 = (TA == 1 && TB == 1);
+  constexpr bool A16 = (TA == 1);  // baseline values (the top-k keys) are bf16
   constexpr int SA = SH::SA, SB = SH::SB;
   constexpr int kStepA = SH::kStepA, kStepB = SH::kStepB;
   constexpr bool RING = SH::RING;
@@ -896,6 +929,7 @@ __attribute__((amdgpu_waves_per_eu(4, 8))) void k_row_stats(StreamArgs args) {
   st.tau_fresh = 0;
   st.tau_set = 0;
   st.cnt = 0;
+  st.cbit = args.v > 1 ? 63 - __builtin_clzll((unsigned long long)(args.v - 1)) : 0;
   st.n_bad = st.n_ainf = st.n_binf = st.n_qzero = 0;
   st.ndiff = 0;
   st.first = -1;
@@ -956,8 +990,8 @@ __attribute__((amdgpu_waves_per_eu(4, 8))) void k_row_stats(StreamArgs args) {
       cur.a.decode(ua);
       cur.b.decode(ub);
       raw_words(cur, wa, wb);
-      process_step<CMP, BITS, W16, MAPB>(ua, ub, wa, wb, 0xffu, false, lo + sp * kSpan, lane, kint,
-                                         st, cb);
+      process_step<CMP, BITS, W16, MAPB, A16>(ua, ub, wa, wb, 0xffu, false, lo + sp * kSpan, lane,
+                                              kint, st, cb);
       rd = rd + 1 == R ? 0 : rd + 1;
       wr = wr + 1 == R ? 0 : wr + 1;
     }
@@ -977,8 +1011,8 @@ __attribute__((amdgpu_waves_per_eu(4, 8))) void k_row_stats(StreamArgs args) {
       r.a.decode(ua);
       r.b.decode(ub);
       raw_words(r, wa, wb);
-      process_step<CMP, BITS, W16, MAPB>(ua, ub, wa, wb, 0xffu, false, lo + s * kSpan, lane, kint, st,
-                                         cb);
+      process_step<CMP, BITS, W16, MAPB, A16>(ua, ub, wa, wb, 0xffu, false, lo + s * kSpan, lane,
+                                              kint, st, cb);
     };
     if (nfull > 0) fetch(r0, 0);
     int sp = 0;
@@ -998,7 +1032,7 @@ __attribute__((amdgpu_waves_per_eu(4, 8))) void k_row_stats(StreamArgs args) {
       const uint32_t valid = load_checked<TA, TB, MAPB>(ua, ub, ra, rb, base, hi, lane);
       pack_words(ua, wa);
       pack_words(ub, wb);
-      process_step<CMP, BITS, W16, MAPB>(ua, ub, wa, wb, valid, false, base, lane, kint, st, cb);
+      process_step<CMP, BITS, W16, MAPB, A16>(ua, ub, wa, wb, valid, false, base, lane, kint, st, cb);
     }
   }
   if (lo + nfull * kSpan < hi) {
@@ -1007,7 +1041,7 @@ __attribute__((amdgpu_waves_per_eu(4, 8))) void k_row_stats(StreamArgs args) {
     const uint32_t valid = load_checked<TA, TB, MAPB>(ua, ub, ra, rb, base, hi, lane);
     pack_words(ua, wa);
     pack_words(ub, wb);
-    process_step<CMP, BITS, W16, MAPB>(ua, ub, wa, wb, valid, true, base, lane, kint, st, cb);
+    process_step<CMP, BITS, W16, MAPB, A16>(ua, ub, wa, wb, valid, true, base, lane, kint, st, cb);
   }
   if (CMP && BITS) fold_partials(st);
 
@@ -1015,7 +1049,7 @@ __attribute__((amdgpu_waves_per_eu(4, 8))) void k_row_stats(StreamArgs args) {
   // argument segment here rather than held in scalar registers through the loop.
   const StreamArgs &late = *(const StreamArgs *)__builtin_amdgcn_kernarg_segment_ptr();
   if (CMP) {
-    if (st.cnt > kint) flush_candidates(cb, st, kint);
+    if (st.cnt > kint) flush_candidates<A16>(cb, st, kint);
     wave_fence();
     const int64_t tk = item * kint;
     if (lane < st.cnt) {

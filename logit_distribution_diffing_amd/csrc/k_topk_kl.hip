@@ -225,39 +225,56 @@ __global__ __launch_bounds__(kWave) void k_topk_kl(FinalArgs a) {
   const int top1_cand = bx == 0x7fffffff ? -1 : bx;
 
   // ---- the row's top kint slots: the kint-th largest key T, one bit at a time from the top; then the ties at T
-  // that are kept, lowest indices first
+  // that are kept, lowest indices first.  The search stops as soon as exactly kint keys lie at or above its
+  // prefix (those are the kint largest).  bf16 baseline values give keys whose low 16 bits are all equal
+  // (zeros when positive, ones when negative), so their search ends at bit 16.
+  const bool k16 = a.tb == 1;
   uint32_t T = 0;
+  int nT = kWave * kSlotRounds;  // at least kint keys lie at or above T
+  bool early = false;
 #pragma unroll 1
-  for (int bit = 31; bit >= 0; --bit) {
+  for (int bit = 31; bit >= (k16 ? 16 : 0); --bit) {
     const uint32_t c = T | (1u << bit);
     int n = 0;
 #pragma unroll
     for (int q = 0; q < kSlotRounds; ++q)
       if (q < rounds) n += __popcll(ballot(key[q] >= c));
-    if (n >= kint) T = c;
-  }
-  int ngt = 0, neq = 0;
-#pragma unroll
-  for (int q = 0; q < kSlotRounds; ++q) {
-    if (q < rounds) {
-      ngt += __popcll(ballot(key[q] > T));
-      neq += __popcll(ballot(key[q] == T));
+    if (n >= kint) {
+      T = c;
+      nT = n;
+    }
+    if (nT == kint) {
+      early = true;
+      break;
     }
   }
-  const int need = kint - ngt;
+  if (k16 && !early && T < 0x80000000u) T |= 0xffffu;
   uint32_t isel = 0x7fffffffu;
-  if (neq > need) {
-    uint32_t I = 0;
-#pragma unroll 1
-    for (int bit = 30; bit >= 0; --bit) {
-      const uint32_t c = I | (1u << bit);
-      int n = 0;
+  if (!early) {
+    int ngt = 0, neq = 0;
 #pragma unroll
-      for (int q = 0; q < kSlotRounds; ++q)
-        if (q < rounds) n += __popcll(ballot(key[q] == T && (uint32_t)idx[q] < c));
-      if (n < need) I = c;
+    for (int q = 0; q < kSlotRounds; ++q) {
+      if (q < rounds) {
+        ngt += __popcll(ballot(key[q] > T));
+        neq += __popcll(ballot(key[q] == T));
+      }
     }
-    isel = I;
+    const int need = kint - ngt;
+    if (neq > need) {
+      // columns are below v: the higher bits of the need-th smallest are zero
+      const int cbit = a.v > 1 ? 63 - __builtin_clzll((unsigned long long)(a.v - 1)) : 0;
+      uint32_t I = 0;
+#pragma unroll 1
+      for (int bit = cbit; bit >= 0; --bit) {
+        const uint32_t c = I | (1u << bit);
+        int n = 0;
+#pragma unroll
+        for (int q = 0; q < kSlotRounds; ++q)
+          if (q < rounds) n += __popcll(ballot(key[q] == T && (uint32_t)idx[q] < c));
+        if (n < need) I = c;
+      }
+      isel = I;
+    }
   }
   // compact the kint kept slots, then order them: lane j < kint holds kept
   // entry j and counts the kept entries ahead of it
