@@ -185,9 +185,11 @@ int lcmp_compare_logits(const void *base, int tb, int64_t ld_base, const void *c
 
 /*
  * Instrumented form of lcmp_compare_logits for measuring the streaming pass:
- * when ev_before / ev_after (hipEvent_t) are non-NULL they are recorded on
- * `stream` immediately before and after the streaming kernel, so their
- * elapsed time is that kernel's duration.  Everything else is identical.
+ * ev_before / ev_after (hipEvent_t created with timing, or NULL) are given to
+ * the dispatch of the streaming kernel (hipExtLaunchKernel), so they take its
+ * start and end time and their elapsed time is that kernel's duration.  With
+ * n == 0 nothing is launched and both are recorded on `stream` back to back.
+ * Everything else is identical.
  */
 int lcmp_compare_logits_timed(const void *base, int tb, int64_t ld_base, const void *cand, int tc,
                               int64_t ld_cand, int64_t n, int64_t v, int k, uint32_t flags,
@@ -233,7 +235,8 @@ int lcmp_bitdiff(const void *a, int ta, int64_t lda, const void *b, int tb, int6
                  size_t ws_bytes, void *stream);
 
 /* Instrumented form of lcmp_bitdiff: ev_before / ev_after (hipEvent_t, may be
- * NULL) are recorded on `stream` around the streaming kernel. */
+ * NULL) take the start and end time of the streaming kernel's dispatch, as in
+ * lcmp_compare_logits_timed. */
 int lcmp_bitdiff_timed(const void *a, int ta, int64_t lda, const void *b, int tb, int64_t ldb,
                        int64_t rows, int64_t cols, lcmp_bitdiff_row *out, void *workspace,
                        size_t ws_bytes, void *stream, void *ev_before, void *ev_after);
@@ -328,8 +331,9 @@ int lcmp_compare_record(const lcmp_record *rec, int k_rec, const void *cand, int
                         int64_t ld_cand, int64_t n, int64_t v, int k, const lcmp_row_out *out,
                         void *workspace, size_t ws_bytes, void *stream);
 
-/* Instrumented form: ev_before / ev_after (hipEvent_t, may be NULL) are recorded
- * on `stream` around the candidate's streaming kernel. */
+/* Instrumented form: ev_before / ev_after (hipEvent_t, may be NULL) take the
+ * start and end time of the candidate's streaming kernel, as in
+ * lcmp_compare_logits_timed. */
 int lcmp_compare_record_timed(const lcmp_record *rec, int k_rec, const void *cand, int tc,
                               int64_t ld_cand, int64_t n, int64_t v, int k,
                               const lcmp_row_out *out, void *workspace, size_t ws_bytes,
@@ -378,7 +382,8 @@ int lcmp_bin_report(const double *margin, const uint8_t *flip, const double *kl_
  * read time this access pattern reaches on the device.  One 32-bit word per
  * (row, chunk) is written to the workspace, which must hold at least
  * lcmp_compare_workspace_bytes(n, v, 1, 0) bytes.  ev_before / ev_after
- * (hipEvent_t, may be NULL) are recorded around the kernel.
+ * (hipEvent_t, may be NULL) take the start and end time of the kernel, as in
+ * lcmp_compare_logits_timed.
  * Errors as lcmp_compare_logits; LCMP_EINVAL also when a row start of either
  * tensor is not 16-byte aligned (the comparison then takes its scalar-load path).
  */

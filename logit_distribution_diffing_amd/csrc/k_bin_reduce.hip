@@ -10,7 +10,7 @@
 //            atomics (exact, order-free).
 //   level 2: one wave per bin (and per group) adds the block partials in a
 //            fixed lane-then-wave-reduction order.
-// Reports of at most 64 blocks, 64 bins and 16 groups run both levels in one
+// Reports of at most 16 blocks, 64 bins and 16 groups run both levels in one
 // launch of one block (k_bin_small), with the same per-block code.
 #include "common.hpp"
 #include "launch.hpp"
@@ -26,10 +26,29 @@ struct BlockAcc {
   double kt[NB], kf[NB], mx[NB];
   unsigned long long cnt[NB][4];
   unsigned long long grp[NG][3];
+
+  __device__ BinAcc bin(int t) const {
+    BinAcc o;
+    o.count = (int64_t)cnt[t][0];
+    o.flips = (int64_t)cnt[t][1];
+    o.ties = (int64_t)cnt[t][2];
+    o.tie_flips = (int64_t)cnt[t][3];
+    o.sum_kl_topk = kt[t];
+    o.sum_kl_full = kf[t];
+    o.max_kl_topk = mx[t];
+    return o;
+  }
+  __device__ GroupAcc group(int g) const {
+    GroupAcc o;
+    o.big_margin_flips = (int64_t)grp[g][0];
+    o.excluded = (int64_t)grp[g][1];
+    o.unbinned = (int64_t)grp[g][2];
+    return o;
+  }
 };
 
-// Level 1 for block `blk`: its rows in batches of 64, then its partials to
-// the workspace.  One wave, all 64 lanes.
+// Level 1 for block `blk`: its rows in batches of 64 into the accumulators.
+// One wave, all 64 lanes.
 template <int NB, int NG>
 __device__ __forceinline__ void bin_block(const BinArgs &a, int64_t blk, BlockAcc<NB, NG> &acc) {
   const int lane = lane_id();
@@ -96,39 +115,33 @@ __device__ __forceinline__ void bin_block(const BinArgs &a, int64_t blk, BlockAc
   }
   __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
   __builtin_amdgcn_wave_barrier();
+}
+
+// The block's partials to the workspace.
+template <int NB, int NG>
+__device__ __forceinline__ void bin_block_store(const BinArgs &a, int64_t blk,
+                                                const BlockAcc<NB, NG> &acc) {
+  const int lane = lane_id();
+  const int nbins = a.n_groups * a.n_edges;
   BinAcc *pb = a.part_bins + blk * nbins;
-  for (int t = lane; t < nbins; t += kWave) {
-    BinAcc o;
-    o.count = (int64_t)acc.cnt[t][0];
-    o.flips = (int64_t)acc.cnt[t][1];
-    o.ties = (int64_t)acc.cnt[t][2];
-    o.tie_flips = (int64_t)acc.cnt[t][3];
-    o.sum_kl_topk = acc.kt[t];
-    o.sum_kl_full = acc.kf[t];
-    o.max_kl_topk = acc.mx[t];
-    pb[t] = o;
-  }
+  for (int t = lane; t < nbins; t += kWave) pb[t] = acc.bin(t);
   GroupAcc *pg = a.part_groups + blk * a.n_groups;
-  for (int g = lane; g < a.n_groups; g += kWave) {
-    GroupAcc o;
-    o.big_margin_flips = (int64_t)acc.grp[g][0];
-    o.excluded = (int64_t)acc.grp[g][1];
-    o.unbinned = (int64_t)acc.grp[g][2];
-    pg[g] = o;
-  }
+  for (int g = lane; g < a.n_groups; g += kWave) pg[g] = acc.group(g);
 }
 
 // Level 2 for output t: bin t (t < nbins) or group t - nbins.  Lane l adds
 // partials l, l+64, ... in order, then the fixed-order wave reduction
-// combines the lanes.  One wave, all 64 lanes.
-__device__ __forceinline__ void bin_final(const BinArgs &a, int t) {
+// combines the lanes.  One wave, all 64 lanes.  part(b) gives block b's
+// partials: .bin(t) and .group(g).
+template <class Part>
+__device__ __forceinline__ void bin_final(const BinArgs &a, int t, const Part &part) {
   const int lane = lane_id();
   const int nbins = a.n_groups * a.n_edges;
   if (t < nbins) {
     int64_t c0 = 0, c1 = 0, c2 = 0, c3 = 0;
     double s0 = 0.0, s1 = 0.0, mx = -INFINITY;
     for (int b = lane; b < a.nblk; b += kWave) {
-      const BinAcc p = a.part_bins[(int64_t)b * nbins + t];
+      const BinAcc p = part(b).bin(t);
       c0 += p.count;
       c1 += p.flips;
       c2 += p.ties;
@@ -150,7 +163,7 @@ __device__ __forceinline__ void bin_final(const BinArgs &a, int t) {
     const int g = t - nbins;
     int64_t c0 = 0, c1 = 0, c2 = 0;
     for (int b = lane; b < a.nblk; b += kWave) {
-      const GroupAcc p = a.part_groups[(int64_t)b * a.n_groups + g];
+      const GroupAcc p = part(b).group(g);
       c0 += p.big_margin_flips;
       c1 += p.excluded;
       c2 += p.unbinned;
@@ -163,28 +176,44 @@ __device__ __forceinline__ void bin_final(const BinArgs &a, int t) {
   }
 }
 
+// The partials of block b, read back from the workspace.
+struct StoredPart {
+  const BinArgs &a;
+  struct Ref {
+    const BinArgs &a;
+    int64_t b;
+    __device__ BinAcc bin(int t) const { return a.part_bins[b * a.n_groups * a.n_edges + t]; }
+    __device__ GroupAcc group(int g) const { return a.part_groups[b * a.n_groups + g]; }
+  };
+  __device__ Ref operator()(int b) const { return Ref{a, b}; }
+};
+
 __global__ __launch_bounds__(kWave) void k_bin_partial(BinArgs a) {
   __shared__ BlockAcc<kMaxBins, kMaxGroups> acc;
   bin_block(a, blockIdx.x, acc);
+  bin_block_store(a, blockIdx.x, acc);
 }
 
 // One wave per bin (then per group).
-__global__ __launch_bounds__(kWave) void k_bin_final(BinArgs a) { bin_final(a, blockIdx.x); }
+__global__ __launch_bounds__(kWave) void k_bin_final(BinArgs a) {
+  bin_final(a, blockIdx.x, StoredPart{a});
+}
 
-// Small reports in one launch: kSmallWaves waves take the level-1 blocks in
-// turn, each with its own LDS accumulators, then, after the block barrier,
-// the level-2 outputs in turn.  The same per-block and per-output code as the
-// two kernels above, so the results are the same bits.
+// Small reports in one launch: wave w is level-1 block w, with its own LDS
+// accumulators; after the block barrier the waves take the level-2 outputs in
+// turn and read the partials from LDS.  The same per-block and per-output
+// code, and the same values, as the two kernels above: the same bits.
 constexpr int kSmallWaves = 16;
-constexpr int kSmallBins = 64, kSmallGroups = 16, kSmallBlocks = 64;
+constexpr int kSmallBins = 64, kSmallGroups = 16, kSmallBlocks = kSmallWaves;
 __global__ __launch_bounds__(kSmallWaves * kWave) void k_bin_small(BinArgs a) {
-  __shared__ BlockAcc<kSmallBins, kSmallGroups> acc[kSmallWaves];
+  using Acc = BlockAcc<kSmallBins, kSmallGroups>;
+  __shared__ Acc acc[kSmallWaves];
   const int w = __builtin_amdgcn_readfirstlane((int)(threadIdx.x / kWave));
-  for (int blk = w; blk < a.nblk; blk += kSmallWaves) bin_block(a, blk, acc[w]);
-  __threadfence_block();
+  if (w < a.nblk) bin_block(a, w, acc[w]);
   __syncthreads();
   const int nout = a.n_groups * a.n_edges + a.n_groups;
-  for (int t = w; t < nout; t += kSmallWaves) bin_final(a, t);
+  for (int t = w; t < nout; t += kSmallWaves)
+    bin_final(a, t, [&](int b) -> const Acc & { return acc[b]; });
 }
 
 hipError_t launch_bin_reduce(const BinArgs &a, hipStream_t stream) {

@@ -105,22 +105,23 @@ __global__ __launch_bounds__(kBlock) void k_read_probe(StreamArgs args, uint32_t
 }
 
 template <int SA, int SB>
-hipError_t launch_probe_typed(const StreamArgs &a, uint32_t *sink, hipStream_t s) {
+hipError_t launch_probe_typed(const StreamArgs &a, uint32_t *sink, hipStream_t s, const Timing &t) {
   const int64_t items = a.n * a.nchunks;
   const dim3 grid((unsigned)((items + kWavesPerBlock - 1) / kWavesPerBlock));
-  hipLaunchKernelGGL((k_read_probe<SA, SB>), grid, dim3(kBlock), 0, s, a, sink);
+  hipExtLaunchKernelGGL((k_read_probe<SA, SB>), grid, dim3(kBlock), 0, s, t.before, t.after, 0, a,
+                        sink);
   return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_read_probe(const StreamArgs &a, int ta, int tb, uint32_t *sink,
-                             hipStream_t s) {
-  if (a.n * a.nchunks == 0) return hipSuccess;
-  if (ta == 0 && tb == 0) return launch_probe_typed<4, 4>(a, sink, s);
-  if (ta == 0 && tb == 1) return launch_probe_typed<4, 2>(a, sink, s);
-  if (ta == 1 && tb == 0) return launch_probe_typed<2, 4>(a, sink, s);
-  return launch_probe_typed<2, 2>(a, sink, s);
+                             hipStream_t s, const Timing &t) {
+  if (a.n * a.nchunks == 0) return record_empty(t, s);
+  if (ta == 0 && tb == 0) return launch_probe_typed<4, 4>(a, sink, s, t);
+  if (ta == 0 && tb == 1) return launch_probe_typed<4, 2>(a, sink, s, t);
+  if (ta == 1 && tb == 0) return launch_probe_typed<2, 4>(a, sink, s, t);
+  return launch_probe_typed<2, 2>(a, sink, s, t);
 }
 
 }  // namespace lcmp

@@ -288,19 +288,21 @@ __global__ __launch_bounds__(kBlock) void k_rest_sum(RestArgs a) {
 }
 
 template <int T, bool VEC>
-hipError_t launch_typed(const RestArgs &a, hipStream_t s) {
+hipError_t launch_typed(const RestArgs &a, hipStream_t s, const Timing &t) {
   const int64_t items = a.n * a.nchunks;
   const dim3 grid((unsigned)((items + kWavesPerBlock - 1) / kWavesPerBlock));
-  hipLaunchKernelGGL((k_rest_sum<T, VEC>), grid, dim3(kBlock), 0, s, a);
+  hipExtLaunchKernelGGL((k_rest_sum<T, VEC>), grid, dim3(kBlock), 0, s, t.before, t.after, 0, a);
   return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_rest_sum(const RestArgs &a, int tx, bool vec, hipStream_t stream) {
-  if (a.n * a.nchunks == 0) return hipSuccess;
-  if (tx == 1) return vec ? launch_typed<1, true>(a, stream) : launch_typed<1, false>(a, stream);
-  return vec ? launch_typed<0, true>(a, stream) : launch_typed<0, false>(a, stream);
+hipError_t launch_rest_sum(const RestArgs &a, int tx, bool vec, hipStream_t stream,
+                           const Timing &t) {
+  if (a.n * a.nchunks == 0) return record_empty(t, stream);
+  if (tx == 1)
+    return vec ? launch_typed<1, true>(a, stream, t) : launch_typed<1, false>(a, stream, t);
+  return vec ? launch_typed<0, true>(a, stream, t) : launch_typed<0, false>(a, stream, t);
 }
 
 }  // namespace lcmp

@@ -1114,36 +1114,38 @@ __attribute__((amdgpu_waves_per_eu(4, 8))) void k_row_stats(StreamArgs args) {
 // ---------------------------------------------------------------- launcher
 
 template <int TA, int TB, bool CMP, bool BITS, bool VEC>
-static void launch_shape(const StreamArgs &a, hipStream_t stream) {
+static void launch_shape(const StreamArgs &a, hipStream_t stream, const Timing &t) {
   constexpr int W = Shape<TA, TB, CMP, VEC>::W;
   const int64_t items = a.n * a.nchunks;
   const dim3 grid((unsigned)((items + W - 1) / W));
-  hipLaunchKernelGGL((k_row_stats<TA, TB, CMP, BITS, VEC>), grid, dim3(W * kWave), 0, stream, a);
+  hipExtLaunchKernelGGL((k_row_stats<TA, TB, CMP, BITS, VEC>), grid, dim3(W * kWave), 0, stream,
+                        t.before, t.after, 0, a);
 }
 
 template <int TA, int TB, bool CMP, bool BITS>
-static hipError_t launch_typed(const StreamArgs &a, bool vec, hipStream_t stream) {
+static hipError_t launch_typed(const StreamArgs &a, bool vec, hipStream_t stream, const Timing &t) {
   if (vec)
-    launch_shape<TA, TB, CMP, BITS, true>(a, stream);
+    launch_shape<TA, TB, CMP, BITS, true>(a, stream, t);
   else
-    launch_shape<TA, TB, CMP, BITS, false>(a, stream);
+    launch_shape<TA, TB, CMP, BITS, false>(a, stream, t);
   return hipGetLastError();
 }
 
 template <bool CMP, bool BITS>
-static hipError_t launch_mode(const StreamArgs &a, int ta, int tb, bool vec, hipStream_t s) {
-  if (ta == 0 && tb == 0) return launch_typed<0, 0, CMP, BITS>(a, vec, s);
-  if (ta == 0 && tb == 1) return launch_typed<0, 1, CMP, BITS>(a, vec, s);
-  if (ta == 1 && tb == 0) return launch_typed<1, 0, CMP, BITS>(a, vec, s);
-  return launch_typed<1, 1, CMP, BITS>(a, vec, s);
+static hipError_t launch_mode(const StreamArgs &a, int ta, int tb, bool vec, hipStream_t s,
+                              const Timing &t) {
+  if (ta == 0 && tb == 0) return launch_typed<0, 0, CMP, BITS>(a, vec, s, t);
+  if (ta == 0 && tb == 1) return launch_typed<0, 1, CMP, BITS>(a, vec, s, t);
+  if (ta == 1 && tb == 0) return launch_typed<1, 0, CMP, BITS>(a, vec, s, t);
+  return launch_typed<1, 1, CMP, BITS>(a, vec, s, t);
 }
 
 hipError_t launch_row_stats(const StreamArgs &a, int ta, int tb, bool cmp, bool bits, bool vec,
-                            hipStream_t stream) {
-  if (a.n * a.nchunks == 0) return hipSuccess;
-  if (cmp && bits) return launch_mode<true, true>(a, ta, tb, vec, stream);
-  if (cmp) return launch_mode<true, false>(a, ta, tb, vec, stream);
-  return launch_mode<false, true>(a, ta, tb, vec, stream);
+                            hipStream_t stream, const Timing &t) {
+  if (a.n * a.nchunks == 0) return record_empty(t, stream);
+  if (cmp && bits) return launch_mode<true, true>(a, ta, tb, vec, stream, t);
+  if (cmp) return launch_mode<true, false>(a, ta, tb, vec, stream, t);
+  return launch_mode<false, true>(a, ta, tb, vec, stream, t);
 }
 
 }  // namespace lcmp

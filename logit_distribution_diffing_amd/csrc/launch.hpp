@@ -2,6 +2,7 @@
 // translation units of liblcmp (internal; not part of the C ABI).
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -160,17 +161,27 @@ struct RecordCmpArgs {
   int32_t *topk_idx;
   double *logp_base, *logp_cand;
 };
-hipError_t launch_rest_sum(const RestArgs &a, int tx, bool vec, hipStream_t stream);
+// Optional timing of a streaming kernel: events given to the kernel's own
+// dispatch (hipExtLaunchKernelGGL), so they take its start and end time and no
+// marker is added to the stream.  With nothing to launch both are recorded
+// back to back.
+struct Timing {
+  hipEvent_t before = nullptr, after = nullptr;
+};
+hipError_t record_empty(const Timing &t, hipStream_t stream);
+
+hipError_t launch_rest_sum(const RestArgs &a, int tx, bool vec, hipStream_t stream,
+                           const Timing &t = Timing());
 hipError_t launch_record_final(const RecordArgs &a, hipStream_t stream);
 hipError_t launch_record_cmp(const RecordCmpArgs &a, hipStream_t stream);
 hipError_t launch_perturb(const PerturbArgs &a, hipStream_t stream);
 
 hipError_t launch_row_stats(const StreamArgs &a, int ta, int tb, bool cmp, bool bits, bool vec,
-                            hipStream_t stream);
+                            hipStream_t stream, const Timing &t = Timing());
 hipError_t launch_topk_kl(const FinalArgs &a, hipStream_t stream);
 hipError_t launch_bitdiff_final(const BitsFinalArgs &a, hipStream_t stream);
 hipError_t launch_bin_reduce(const BinArgs &a, hipStream_t stream);
 hipError_t launch_read_probe(const StreamArgs &a, int ta, int tb, uint32_t *sink,
-                             hipStream_t stream);
+                             hipStream_t stream, const Timing &t = Timing());
 
 }  // namespace lcmp

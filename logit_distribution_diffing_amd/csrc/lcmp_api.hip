@@ -20,11 +20,24 @@ static_assert(kMaxGroups == LCMP_MAX_GROUPS && kMaxBins == LCMP_MAX_BINS &&
                   kMaxBinRows == LCMP_MAX_BIN_ROWS,
               "limits of the header and of the kernels agree");
 
+hipError_t lcmp::record_empty(const Timing &t, hipStream_t stream) {
+  if (t.before && hipEventRecord(t.before, stream) != hipSuccess) return hipErrorUnknown;
+  if (t.after && hipEventRecord(t.after, stream) != hipSuccess) return hipErrorUnknown;
+  return hipSuccess;
+}
+
 namespace {
 
 constexpr size_t kAlign = 256;
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+Timing timing(void *ev_before, void *ev_after) {
+  Timing t;
+  t.before = (hipEvent_t)ev_before;
+  t.after = (hipEvent_t)ev_after;
+  return t;
+}
 
 bool dtype_ok(int t) { return t == LCMP_F32 || t == LCMP_BF16; }
 size_t esize(int t) { return t == LCMP_BF16 ? 2 : 4; }
@@ -212,11 +225,9 @@ static int compare_impl(const void *base, int tb, int64_t ld_base, const void *c
   sa.ta = (float *)(ws + L.off_ta);
   sa.ti = (int32_t *)(ws + L.off_ti);
   hipStream_t s = (hipStream_t)stream;
-  if (ev_before && hipEventRecord((hipEvent_t)ev_before, s) != hipSuccess) return LCMP_EHIP;
   if (launch_row_stats(sa, tb, tc, true, with_bits, vector_ok(base, tb, ld_base, cand, tc, ld_cand),
-                       s) != hipSuccess)
+                       s, timing(ev_before, ev_after)) != hipSuccess)
     return LCMP_EHIP;
-  if (ev_after && hipEventRecord((hipEvent_t)ev_after, s) != hipSuccess) return LCMP_EHIP;
 
   FinalArgs fa;
   fa.stats = sa.stats;
@@ -358,11 +369,9 @@ static int bitdiff_impl(const void *a, int ta, int64_t lda, const void *b, int t
   sa.kint = 2;
   sa.bits = (ChunkBits *)workspace;
   hipStream_t s = (hipStream_t)stream;
-  if (ev_before && hipEventRecord((hipEvent_t)ev_before, s) != hipSuccess) return LCMP_EHIP;
-  if (launch_row_stats(sa, ta, tb, false, true, vector_ok(a, ta, lda, b, tb, ldb), s) !=
-      hipSuccess)
+  if (launch_row_stats(sa, ta, tb, false, true, vector_ok(a, ta, lda, b, tb, ldb), s,
+                       timing(ev_before, ev_after)) != hipSuccess)
     return LCMP_EHIP;
-  if (ev_after && hipEventRecord((hipEvent_t)ev_after, s) != hipSuccess) return LCMP_EHIP;
   BitsFinalArgs fa;
   fa.bits = sa.bits;
   fa.rows = rows;
@@ -410,9 +419,9 @@ int lcmp_read_probe(const void *base, int tb, int64_t ld_base, const void *cand,
   sa.chunk = ch.chunk;
   sa.nchunks = ch.nchunks;
   hipStream_t s = (hipStream_t)stream;
-  if (ev_before && hipEventRecord((hipEvent_t)ev_before, s) != hipSuccess) return LCMP_EHIP;
-  if (launch_read_probe(sa, tb, tc, (uint32_t *)workspace, s) != hipSuccess) return LCMP_EHIP;
-  if (ev_after && hipEventRecord((hipEvent_t)ev_after, s) != hipSuccess) return LCMP_EHIP;
+  if (launch_read_probe(sa, tb, tc, (uint32_t *)workspace, s, timing(ev_before, ev_after)) !=
+      hipSuccess)
+    return LCMP_EHIP;
   return LCMP_OK;
 }
 
@@ -607,9 +616,9 @@ static int compare_record_impl(const lcmp_record *rec, int k_rec, const void *ca
   ra.ldh = k_rec;
   ra.kh = k;
   ra.out = (RestChunk *)workspace;
-  if (ev_before && hipEventRecord((hipEvent_t)ev_before, s) != hipSuccess) return LCMP_EHIP;
-  if (launch_rest_sum(ra, tc, rows_aligned(cand, tc, ld_cand), s) != hipSuccess) return LCMP_EHIP;
-  if (ev_after && hipEventRecord((hipEvent_t)ev_after, s) != hipSuccess) return LCMP_EHIP;
+  if (launch_rest_sum(ra, tc, rows_aligned(cand, tc, ld_cand), s, timing(ev_before, ev_after)) !=
+      hipSuccess)
+    return LCMP_EHIP;
   RecordCmpArgs ca;
   ca.idx = rec->topk_idx;
   ca.val = rec->topk_val;
