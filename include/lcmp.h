@@ -176,6 +176,8 @@ size_t lcmp_workspace_bytes(int64_t n, int64_t v, int k, uint32_t flags);
  * mass inside the baseline's top-k) have their two buckets summed again
  * directly by the wave that finishes the row, so such rows read their pair
  * once more; ordinary rows never are.
+ * With n == 0 nothing is launched and no row, output or workspace pointer is
+ * read (they may be NULL).
  * Returns LCMP_OK or a negative lcmp_status.
  */
 int lcmp_compare_logits(const void *base, int tb, int64_t ld_base, const void *cand, int tc,

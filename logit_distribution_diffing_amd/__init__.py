@@ -153,6 +153,8 @@ def _dtype_code(t: torch.Tensor) -> int:
 
 
 def _ld(t: torch.Tensor) -> int:
+    if t.dim() == 2 and t.numel() == 0:
+        return t.size(1)  # no element is read: any layout will do
     if t.dim() != 2 or t.stride(1) != 1:
         raise ValueError("expected a 2-D tensor with unit stride along the vocabulary")
     return t.stride(0) if t.size(0) > 1 else max(t.stride(0), t.size(1))

@@ -39,6 +39,13 @@ Timing timing(void *ev_before, void *ev_after) {
   return t;
 }
 
+// A call with no rows: nothing to launch, but the timing events of an
+// instrumented call are still recorded (back to back).
+int empty_call(void *ev_before, void *ev_after, void *stream) {
+  return record_empty(timing(ev_before, ev_after), (hipStream_t)stream) == hipSuccess ? LCMP_OK
+                                                                                      : LCMP_EHIP;
+}
+
 bool dtype_ok(int t) { return t == LCMP_F32 || t == LCMP_BF16; }
 size_t esize(int t) { return t == LCMP_BF16 ? 2 : 4; }
 
@@ -201,9 +208,9 @@ static int compare_impl(const void *base, int tb, int64_t ld_base, const void *c
       ld_cand < v)
     return LCMP_ESHAPE;
   const bool with_bits = (flags & LCMP_WITH_BITDIFF) != 0;
-  if (with_bits && !bd) return LCMP_EINVAL;
   if ((out->logp_base || out->logp_cand) && !out->target) return LCMP_EINVAL;
-  if (n == 0) return LCMP_OK;
+  if (n == 0) return empty_call(ev_before, ev_after, stream);
+  if (with_bits && !bd) return LCMP_EINVAL;
   if (!base || !cand) return LCMP_EINVAL;
   const CompareLayout L = compare_layout(n, v, k, flags);
   if (!workspace || ws_bytes < L.total) return LCMP_EWORKSPACE;
@@ -350,7 +357,7 @@ static int bitdiff_impl(const void *a, int ta, int64_t lda, const void *b, int t
   if (rows < 0) return LCMP_EINVAL;
   if (cols < 1 || cols > kMaxCols || rows > kMaxRows || lda < cols || ldb < cols)
     return LCMP_ESHAPE;
-  if (rows == 0) return LCMP_OK;
+  if (rows == 0) return empty_call(ev_before, ev_after, stream);
   if (!a || !b || !out) return LCMP_EINVAL;
   const Chunking ch = choose_chunks(rows, cols);
   const size_t need = align_up((size_t)rows * (size_t)ch.nchunks * sizeof(ChunkBits));
@@ -402,7 +409,7 @@ int lcmp_read_probe(const void *base, int tb, int64_t ld_base, const void *cand,
   if (!dtype_ok(tb) || !dtype_ok(tc)) return LCMP_EDTYPE;
   if (n < 0) return LCMP_EINVAL;
   if (v < 2 || v > kMaxCols || n > kMaxRows || ld_base < v || ld_cand < v) return LCMP_ESHAPE;
-  if (n == 0) return LCMP_OK;
+  if (n == 0) return empty_call(ev_before, ev_after, stream);
   if (!base || !cand || !vector_ok(base, tb, ld_base, cand, tc, ld_cand)) return LCMP_EINVAL;
   const Chunking ch = choose_chunks(n, v);
   if (!workspace || ws_bytes < (size_t)n * (size_t)ch.nchunks * sizeof(uint32_t))
@@ -599,7 +606,7 @@ static int compare_record_impl(const lcmp_record *rec, int k_rec, const void *ca
   if (out->kl_full) return LCMP_EINVAL;  // needs the whole baseline row
   if ((out->logp_base || out->logp_cand) && !out->target) return LCMP_EINVAL;
   if (out->logp_base && !rec->logp_target) return LCMP_EINVAL;
-  if (n == 0) return LCMP_OK;
+  if (n == 0) return empty_call(ev_before, ev_after, stream);
   if (!cand || !record_ok(rec)) return LCMP_EINVAL;
   const RestLayout RL = rest_layout(n, v);
   if (!workspace || ws_bytes < RL.bytes) return LCMP_EWORKSPACE;

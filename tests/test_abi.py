@@ -96,6 +96,7 @@ def test_compare_argument_errors(L):
     assert _compare(L, ws_bytes=16) == -4
     assert _compare(L, ws=FAKE + 4) == -1                # misaligned workspace
     assert _compare(L, n=0) == 0                         # empty batch: nothing to do
+    assert _compare(L, n=0, flags=1, bd=None, base=None, ws=None) == 0  # and nothing is read
     assert _compare(L, n=1 << 31) == -3                  # more rows than LCMP_MAX_ROWS
     ro = L.RowOut()
     ro.logp_cand = FAKE
