@@ -9,11 +9,11 @@ N=10240 positions x V=151936, fp32 baseline, bf16 candidate, k=20, six margin
 bins, ten row groups.  Inputs are generated on the host, copied to HBM once,
 and are resident before the timed region starts.
 
-After W warm-up steps the K steps are timed twice: first as a caller runs
-them (value, ms_per_step), then with HIP events given to the dispatch of each
-step's streaming kernel on its own stream (the kernel's duration).  Timing
+After W warm-up steps the K steps are timed twice: first with HIP events
+given to the dispatch of each step's streaming kernel on its own stream (the
+kernel's duration), then as a caller runs them (value, ms_per_step).  Timing
 events leave the stream idle for a few microseconds around the kernel they
-time; roofline.ms_per_step_timed_pass is the step time of that second pass.
+time; roofline.ms_per_step_timed_pass is the step time of the event pass.
 
 Prints ONE JSON line on stdout (everything else goes to stderr):
   value      positions per second over the timed steps (whole job, one GPU)
@@ -289,15 +289,16 @@ def copy_probe(nbytes: int):
 
 def time_steps(step, steps, warmup, hip, torch, stream, nev=1):
     """W untimed steps, then two timed passes of K steps, each between
-    synchronisations.  The first runs the steps as a caller would: its stream
-    time gives ms_per_step and value.  In the second, step(i, evs) gives the
-    `nev` HIP event pairs of `evs` to the dispatch of the step's streaming
-    kernel(s) (evs is None otherwise): their durations are the kernel times.
-    Timing events leave the stream idle for about 4.5 us before and after the
-    kernel they time, so the second pass is slower per step than the first.
-    Returns the stream time of the first pass (ms), its wall time (s), per
-    event pair the list of its K durations (ms), and the stream time of the
-    second pass (ms)."""
+    synchronisations.  In the first, step(i, evs) gives the `nev` HIP event
+    pairs of `evs` to the dispatch of the step's streaming kernel(s) (evs is
+    None otherwise): their durations are the kernel times.  The second runs
+    the steps as a caller would: its stream time gives ms_per_step and value
+    (timing events leave the stream idle for a few microseconds around the
+    kernel they time).  With the driver's short warm-up the first pass also
+    finishes settling the clocks, so the untimed-event pass measures the
+    steady state.  Returns the stream time of the plain pass (ms), its wall
+    time (s), per event pair the list of its K durations (ms), and the stream
+    time of the event pass (ms)."""
     for i in range(warmup):
         step(i, None)
     torch.cuda.synchronize()
@@ -313,9 +314,9 @@ def time_steps(step, steps, warmup, hip, torch, stream, nev=1):
         torch.cuda.synchronize()
         return t_start.elapsed_time(t_stop), time.perf_counter() - wall0
 
-    gpu_ms, wall = timed(warmup, None)
     evs = [[(hip.event(), hip.event()) for _ in range(nev)] for _ in range(steps)]
-    ev_ms, _ = timed(warmup + steps, evs)
+    ev_ms, _ = timed(warmup, evs)
+    gpu_ms, wall = timed(warmup + steps, None)
     per = [[hip.elapsed_ms(a, b) for a, b in (evs[i][j] for i in range(steps))]
            for j in range(nev)]
     return gpu_ms, wall, per, ev_ms
