@@ -71,6 +71,37 @@ def test_ties_and_signed_zeros():
     assert_compare_equal(g, oracle.compare(a, b, k=64))
 
 
+@pytest.mark.parametrize("tb,tc", [("bf16", "bf16"), ("bf16", "f32")])
+@pytest.mark.parametrize("k", [1, 20, 64])
+def test_bf16_baseline_negative_ties(tb, tc, k):
+    """bf16 baselines whose top-k lies among negative, heavily tied values over
+    full-length rows (many buffer reductions per chunk): the bf16 key search
+    stops at bit 16 and completes negative keys, and ties at the k-th value
+    are cut by column."""
+    _case(f"bf16 negative ties {tb}/{tc} k={k}")
+    rng = np.random.default_rng(31 + k)
+    n, v = 6, 151936
+    levels = -np.array([0.5, 0.75, 1.0, 1.5, 2.0, 3.0], dtype=np.float32)
+    a = levels[rng.integers(0, levels.size, (n, v))]
+    a[1] = -rng.uniform(0.0, 8.0, v).astype(np.float32)          # all negative, few ties
+    a[2, :] = -1.0                                                # one value everywhere
+    a[3] = np.where(rng.random(v) < 0.5, -0.0, -2.0**-10).astype(np.float32)
+    a[4, rng.integers(0, v, 300)] = -0.25                         # 300 ties at the top
+    a[5] = np.sort(a[5])                                          # ascending row
+    b = a + 0.01 * rng.standard_normal((n, v)).astype(np.float32)
+    import torch
+
+    def conv(t, arr):
+        if t == "f32":
+            return arr
+        return torch.from_numpy(arr).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+
+    A, B = conv(tb, a), conv(tc, b)
+    g = gpu_compare(A, B, k=k, with_bitdiff=True)
+    assert_compare_equal(g, oracle.compare(A, B, k=k))
+    assert_bitdiff_equal(g["bitdiff"], oracle.bitdiff(A, B))
+
+
 @pytest.mark.parametrize("order", ["ascending", "descending", "clustered"])
 def test_adversarial_orders_for_topk(order):
     _case(f"order {order}")
