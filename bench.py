@@ -9,17 +9,30 @@ N=10240 positions x V=151936, fp32 baseline, bf16 candidate, k=20, six margin
 bins, ten row groups.  Inputs are generated on the host, copied to HBM once,
 and are resident before the timed region starts.
 
-After W warm-up steps the K steps are timed twice: first with HIP events
-given to the dispatch of each step's streaming kernel on its own stream (the
-kernel's duration), then as a caller runs them (value, ms_per_step).  Timing
-events leave the stream idle for a few microseconds around the kernel they
-time; roofline.ms_per_step_timed_pass is the step time of the event pass.
+After W warm-up steps the K steps are timed in three passes, each between
+synchronisations:
+  1. one after the other on one stream, as one caller's stream runs them:
+     roofline.ms_per_step_one_stream;
+  2. on --streams S streams in turn (default 2), each stream with its own
+     outputs and workspaces, as a caller scoring a sequence of batches would
+     issue them: consecutive batches overlap, so one batch's latency-bound
+     per-row finalize and bin report (and the ramp and tail of its streaming
+     pass) run beside the next batch's streaming pass.  value and ms_per_step
+     (time per batch) come from this pass (with --streams 1 it repeats pass 1);
+  3. one after the other on one stream, with HIP events given to the dispatch
+     of each step's streaming kernel: the kernel's duration (kernel_us), and
+     roofline.ms_per_step_timed_pass (timing events leave the stream idle for
+     a few microseconds around the kernel they time).
+Kernel durations always come from pass 3, where no two kernels overlap.  With
+a short warm-up the first launches after it still run slower while the clocks
+settle, so the passes that give the figures come after a full pass.
 
 Prints ONE JSON line on stdout (everything else goes to stderr):
-  value      positions per second over the timed steps (whole job, one GPU)
+  value      positions per second over the timed steps of pass 2 (whole job,
+             one GPU)
   roofline   HBM roofline of the streaming kernel: algorithmic bytes per launch
              (N*V*(bytes per baseline + candidate element)) / its average
-             duration over the event-timed pass.  Also: the same bytes over the
+             duration over the event-timed pass (3).  Also: the same bytes over the
              whole step, and over
              the duration of a read-only stream of the same inputs in the same
              access pattern (lcmp_read_probe), the read rate this pattern can
@@ -51,7 +64,7 @@ inputs in the 256 MB last-level cache from the step before.
 Flags: --gpus N (only 1 is supported: this path runs on one GPU),
 --steps K, --warmup W, --workload {corpus,segment,stream,tiny,sweep},
 --path {compare,record}, --copies C, --cpu-seconds S (budget of the oracle
-leg), --no-cpu-baseline, --no-read-probe,
+leg), --no-cpu-baseline, --no-read-probe, --streams S,
 --copy-probe BYTES (run only a plain device copy of that size, for counter
 calibration under rocprofv3).
 """
@@ -287,39 +300,55 @@ def copy_probe(nbytes: int):
                       "dispatches": 5}), flush=True)
 
 
-def time_steps(step, steps, warmup, hip, torch, stream, nev=1):
-    """W untimed steps, then two timed passes of K steps, each between
-    synchronisations.  In the first, step(i, evs) gives the `nev` HIP event
-    pairs of `evs` to the dispatch of the step's streaming kernel(s) (evs is
-    None otherwise): their durations are the kernel times.  The second runs
-    the steps as a caller would: its stream time gives ms_per_step and value
-    (timing events leave the stream idle for a few microseconds around the
-    kernel they time).  With the driver's short warm-up the first pass also
-    finishes settling the clocks, so the untimed-event pass measures the
-    steady state.  Returns the stream time of the plain pass (ms), its wall
-    time (s), per event pair the list of its K durations (ms), and the stream
-    time of the event pass (ms)."""
+def time_steps(step, steps, warmup, hip, torch, stream, lanes, nev=1):
+    """Warm-up and timed passes of K steps.  step(i, evs, lane) runs step i on
+    lane `lane`: one of len(lanes) streams, each with its own outputs and
+    workspaces; `evs` (None outside the event pass) gives `nev` HIP event
+    pairs to the dispatch of the step's streaming kernel(s).
+
+    W untimed warm-up steps (on the lanes in turn), then, each pass between
+    synchronisations on `stream`:
+      1. the K steps one after the other on lane 0, as one stream runs them;
+      2. the K steps on the lanes in turn (step i on lane i mod S): with more
+         than one lane consecutive batches overlap, so one batch's per-row
+         finalize and bin report run beside the next batch's streaming pass;
+      3. the event pass: the K steps one after the other on lane 0, with
+         events; their durations are the kernel times (a timed kernel leaves
+         the stream idle for a few microseconds around it).
+    With the driver's short warm-up the first launches after it still run
+    slower (the clocks settle over some tens of launches), so the event pass
+    comes last and the pass that gives the value comes after a full pass.
+    Returns the stream time of the value pass (2) (ms), its wall time (s), per
+    event pair the list of its K durations (ms), and the stream times of
+    passes 3 and 1 (ms)."""
+    nl = len(lanes)
     for i in range(warmup):
-        step(i, None)
+        step(i, None, i % nl)
     torch.cuda.synchronize()
 
-    def timed(first, evs):
+    def timed(first, evs, pipelined):
         t_start = torch.cuda.Event(enable_timing=True)
         t_stop = torch.cuda.Event(enable_timing=True)
+        used = lanes if pipelined else lanes[:1]
         wall0 = time.perf_counter()
         t_start.record(stream)
+        for s_ in used:
+            s_.wait_stream(stream)
         for i in range(steps):
-            step(first + i, evs and evs[i])
+            step(first + i, evs and evs[i], i % nl if pipelined else 0)
+        for s_ in used:
+            stream.wait_stream(s_)
         t_stop.record(stream)
         torch.cuda.synchronize()
         return t_start.elapsed_time(t_stop), time.perf_counter() - wall0
 
+    one_ms, _ = timed(warmup, None, False)
+    gpu_ms, wall = timed(warmup + steps, None, True)
     evs = [[(hip.event(), hip.event()) for _ in range(nev)] for _ in range(steps)]
-    ev_ms, _ = timed(warmup, evs)
-    gpu_ms, wall = timed(warmup + steps, None)
+    ev_ms, _ = timed(warmup + 2 * steps, evs, False)
     per = [[hip.elapsed_ms(a, b) for a, b in (evs[i][j] for i in range(steps))]
            for j in range(nev)]
-    return gpu_ms, wall, per, ev_ms
+    return gpu_ms, wall, per, ev_ms, one_ms
 
 
 def read_ceiling(L, pairs, hip, torch, stream, reps=12, settle_s=0.2):
@@ -363,57 +392,66 @@ def run_compare(args, torch, L, synth):
         n_groups = synth.CORPUS_GROUPS
     else:
         groups, n_groups = None, 1
-    bws = torch.empty(int(L.lib().lcmp_bin_workspace_bytes(n, n_groups, len(edges))),
-                      dtype=torch.uint8, device="cuda")
-    bins = torch.empty((n_groups * len(edges), L.BIN_BYTES), dtype=torch.uint8, device="cuda")
-    summ = torch.empty((n_groups, L.GROUP_SUMMARY_BYTES), dtype=torch.uint8, device="cuda")
+    lanes = [torch.cuda.Stream() for _ in range(args.streams)]  # default priority
+    bin_sets = [dict(bws=torch.empty(int(L.lib().lcmp_bin_workspace_bytes(n, n_groups, len(edges))),
+                                     dtype=torch.uint8, device="cuda"),
+                     bins=torch.empty((n_groups * len(edges), L.BIN_BYTES), dtype=torch.uint8,
+                                      device="cuda"),
+                     summ=torch.empty((n_groups, L.GROUP_SUMMARY_BYTES), dtype=torch.uint8,
+                                      device="cuda")) for _ in lanes]
 
     if args.path == "compare":
         # the streaming kernel reads both rows once
         bytes_per_launch = n * v * (esize[w["base"]] + esize[w["cand"]])
-        out = L.alloc_compare_outputs(n, k, base.device, with_bitdiff=True)
-        ws = torch.empty(L.compare_workspace_bytes(n, v, k, True), dtype=torch.uint8,
-                         device="cuda")
+        outs = [L.alloc_compare_outputs(n, k, base.device, with_bitdiff=True) for _ in lanes]
+        wss = [torch.empty(L.compare_workspace_bytes(n, v, k, True), dtype=torch.uint8,
+                           device="cuda") for _ in lanes]
 
-        def step(i, evs=None):
+        def step(i, evs, lane):
             b_, c_ = pairs[i % copies]
-            L.lcmp_compare_logits(b_, c_, k=k, with_bitdiff=True, out=out, workspace=ws,
-                                  stream=stream, events=evs and evs[0])
+            out, z, s_ = outs[lane], bin_sets[lane], lanes[lane]
+            L.lcmp_compare_logits(b_, c_, k=k, with_bitdiff=True, out=out, workspace=wss[lane],
+                                  stream=s_, events=evs and evs[0])
             L.lcmp_bin_report(out["margin"], out["flip"], out["kl_topk"], out["kl_full"], edges,
                               status=out["status"], group=groups, n_groups=n_groups,
-                              workspace=bws, stream=stream, bins=bins, summary=summ)
+                              workspace=z["bws"], stream=s_, bins=z["bins"], summary=z["summ"])
     else:
         # the baseline is recorded once; the timed steps read the candidate rows
         # and the record only
         record = L.lcmp_record_baseline(base, k_rec=k)
         torch.cuda.synchronize()
         bytes_per_launch = n * v * esize[w["cand"]]
-        out = L.alloc_compare_outputs(n, k, cand.device)
-        del out["kl_full"]
-        ws = torch.empty(int(L.lib().lcmp_compare_record_workspace_bytes(n, v)),
-                         dtype=torch.uint8, device="cuda")
+        outs = []
+        for _ in lanes:
+            o_ = L.alloc_compare_outputs(n, k, cand.device)
+            del o_["kl_full"]
+            outs.append(o_)
+        wss = [torch.empty(int(L.lib().lcmp_compare_record_workspace_bytes(n, v)),
+                           dtype=torch.uint8, device="cuda") for _ in lanes]
 
-        def step(i, evs=None):
+        def step(i, evs, lane):
             c_ = pairs[i % copies][1]
-            L.lcmp_compare_record(record, c_, k=k, out=out, workspace=ws, stream=stream,
+            out, z, s_ = outs[lane], bin_sets[lane], lanes[lane]
+            L.lcmp_compare_record(record, c_, k=k, out=out, workspace=wss[lane], stream=s_,
                                   events=evs and evs[0])
             L.lcmp_bin_report(out["margin"], out["flip"], out["kl_topk"], None, edges,
                               status=out["status"], group=groups, n_groups=n_groups,
-                              workspace=bws, stream=stream, bins=bins, summary=summ)
+                              workspace=z["bws"], stream=s_, bins=z["bins"], summary=z["summ"])
 
     # the read-only probe first: its untimed launches settle the clocks
     probe = None
     if not args.no_read_probe and args.path == "compare":
         probe = read_ceiling(L, pairs, hip, torch, stream)
-    gpu_ms, wall, (kern_ms,), ev_ms = time_steps(step, args.steps, args.warmup, hip, torch,
-                                                 stream)
+    gpu_ms, wall, (kern_ms,), ev_ms, one_ms = time_steps(step, args.steps, args.warmup, hip,
+                                                         torch, stream, lanes)
     ks = stats_us(kern_ms)
     ms_per_step = gpu_ms / args.steps
-    log(f"[bench] {args.steps} steps: {gpu_ms:.3f} ms on the stream, {wall * 1e3:.3f} ms wall; "
-        f"with timing events {ev_ms:.3f} ms; streaming kernel mean {ks['mean']:.1f} us, "
+    log(f"[bench] {args.steps} steps on {len(lanes)} stream(s): {gpu_ms:.3f} ms, "
+        f"{wall * 1e3:.3f} ms wall; on one stream {one_ms:.3f} ms, with timing events "
+        f"{ev_ms:.3f} ms; streaming kernel mean {ks['mean']:.1f} us, "
         f"median {ks['median']:.1f} (min {ks['min']:.1f}, max {ks['max']:.1f}); first five "
         f"{[round(x * 1e3) for x in kern_ms[:5]]} us; input copies in turn: {copies}")
-    b_np, s_np = L.unpack_bins(bins, summ, n_groups)
+    b_np, s_np = L.unpack_bins(bin_sets[0]["bins"], bin_sets[0]["summ"], n_groups)
     log(f"[bench] bins count {b_np['count'].sum(axis=0).tolist()} flips "
         f"{b_np['flips'].sum(axis=0).tolist()} big-margin flips "
         f"{int(s_np['big_margin_flips'].sum())} over {n_groups} group(s)")
@@ -434,6 +472,7 @@ def run_compare(args, torch, L, synth):
                     achieved_median=gbs(ks["median"]),
                     step_achieved=gbs(1e3 * ms_per_step),
                     step_frac=round(gbs(1e3 * ms_per_step) / HBM_PEAK_GBS, 4),
+                    ms_per_step_one_stream=round(one_ms / args.steps, 4),
                     ms_per_step_timed_pass=round(ev_ms / args.steps, 4))
     if probe is not None:
         roofline["read_ceiling"] = gbs(probe["median"])
@@ -459,7 +498,7 @@ def run_compare(args, torch, L, synth):
                    "k": k, "base": w["base"], "cand": w["cand"],
                    "arithmetic": "fp32 per element, fp64 sums and finalize",
                    "bitwise_stats": args.path == "compare", "margin_edges": len(edges),
-                   "row_groups": n_groups, "input_copies": copies,
+                   "row_groups": n_groups, "input_copies": copies, "streams": len(lanes),
                    "hbm_gbs_step": roofline["step_achieved"]},
         "roofline": roofline,
         "cpu_baseline": cpu,
@@ -494,26 +533,29 @@ def run_sweep(args, torch, L, synth):
         f"{time.time() - t0:.1f}s")
     shape_bytes = [a.size * a.itemsize + b.size * b.itemsize for a, b in host]
     rows_per_step = sum(a.shape[0] for a, _ in host)
-    outs = [torch.empty((a.shape[0], L.BITDIFF_ROW_BYTES), dtype=torch.uint8, device="cuda")
-            for a, _ in host]
-    wss = [torch.empty(int(L.lib().lcmp_bitdiff_workspace_bytes(a.shape[0], a.shape[1])),
-                       dtype=torch.uint8, device="cuda") for a, _ in host]
+    lanes = [torch.cuda.Stream() for _ in range(args.streams)]  # default priority
+    outs = [[torch.empty((a.shape[0], L.BITDIFF_ROW_BYTES), dtype=torch.uint8, device="cuda")
+             for a, _ in host] for _ in lanes]
+    wss = [[torch.empty(int(L.lib().lcmp_bitdiff_workspace_bytes(a.shape[0], a.shape[1])),
+                        dtype=torch.uint8, device="cuda") for a, _ in host] for _ in lanes]
     hip = Hip()
     stream = torch.cuda.current_stream()
 
-    def step(i, evs=None):
+    def step(i, evs, lane):
         for j, (da, db) in enumerate(sets[i % copies]):
-            L.lcmp_bitdiff(da, db, out=outs[j], workspace=wss[j], stream=stream,
-                           events=evs and evs[j])
+            L.lcmp_bitdiff(da, db, out=outs[lane][j], workspace=wss[lane][j],
+                           stream=lanes[lane], events=evs and evs[j])
 
     # the read-only probe first: its untimed launches settle the clocks
     probe = None
     if not args.no_read_probe:
         probe = read_ceiling(L, [s_[-1] for s_ in sets], hip, torch, stream)
-    gpu_ms, wall, per, ev_ms = time_steps(step, args.steps, args.warmup, hip, torch, stream,
-                                          nev=len(host))
+    gpu_ms, wall, per, ev_ms, one_ms = time_steps(step, args.steps, args.warmup, hip, torch,
+                                                  stream, lanes, nev=len(host))
     ms_per_step = gpu_ms / args.steps
     kstats = [stats_us(p) for p in per]
+    log(f"[bench] {args.steps} sweep steps on {len(lanes)} stream(s): {gpu_ms:.3f} ms; on one "
+        f"stream {one_ms:.3f} ms, with timing events {ev_ms:.3f} ms")
     for (a, _), st, nb in zip(host, kstats, shape_bytes):
         log(f"[bench] {list(a.shape)} {a.dtype}: streaming kernel mean {st['mean']:.1f} us, "
             f"median {st['median']:.1f} us, {nb / st['mean'] / 1e3:.1f} GB/s")
@@ -530,6 +572,7 @@ def run_sweep(args, torch, L, synth):
                     all_kernels_achieved=gbs(sum(shape_bytes), kern_total_us),
                     step_achieved=gbs(sum(shape_bytes), 1e3 * ms_per_step),
                     step_frac=round(gbs(sum(shape_bytes), 1e3 * ms_per_step) / HBM_PEAK_GBS, 4),
+                    ms_per_step_one_stream=round(one_ms / args.steps, 4),
                     ms_per_step_timed_pass=round(ev_ms / args.steps, 4))
     if probe is not None:
         roofline["read_ceiling"] = gbs(shape_bytes[-1], probe["median"])
@@ -558,7 +601,7 @@ def run_sweep(args, torch, L, synth):
                    "types": ["bf16" if a.dtype == np.uint16 else "f32" for a, _ in host],
                    "rows_per_step": rows_per_step, "bytes_per_step": sum(shape_bytes),
                    "arithmetic": "integer pattern compares, fp32 differences, fp64 sums",
-                   "input_copies": copies,
+                   "input_copies": copies, "streams": len(lanes),
                    "hbm_gbs_step": roofline["step_achieved"]},
         "roofline": roofline,
         "cpu_baseline": cpu,
@@ -577,6 +620,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-read-probe", action="store_true")
+    ap.add_argument("--streams", type=int, default=2,
+                    help="streams the value pass spreads consecutive steps over (default 2)")
     ap.add_argument("--copy-probe", type=int, default=0)
     ap.add_argument("--path", default="compare", choices=["compare", "record"],
                     help="compare: baseline and candidate rows, full comparison (default); "
@@ -590,6 +635,9 @@ def main():
               f"(got --gpus {args.gpus}, WORLD_SIZE {world}). Rows shard across GPUs "
               "with no exchange but the bin report; that mode is not built here.",
               file=sys.stderr)
+        sys.exit(2)
+    if args.streams < 1:
+        print("bench.py: --streams must be at least 1", file=sys.stderr)
         sys.exit(2)
     if args.copy_probe:
         copy_probe(args.copy_probe)
