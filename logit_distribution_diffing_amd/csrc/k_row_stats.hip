@@ -84,7 +84,8 @@ struct WaveState {
   // fast path with the comparison: signed differences of the ordered images,
   // their running maximum and minimum (|difference| < 2^31 there; bf16 pairs
   // keep one 16-bit lane per half of a word), and the per-lane count of
-  // differing patterns of bf16 pairs
+  // differing patterns (a count in a register: a ballot per element, whose
+  // mask the scalar unit must wait for, measured slower)
   int omax, omin;
   s16x2 hmax, hmin;
   uint32_t ndl;
@@ -698,6 +699,9 @@ __device__ __forceinline__ void process_step(const uint32_t (&ua)[8], const uint
         const int32_t o1 = (int32_t)((uint32_t)order32(ua[j + 1]) - (uint32_t)order32(ub[j + 1]));
         st.omax = max(st.omax, max(o0, o1));
         st.omin = min(st.omin, min(o0, o1));
+        // the ordered image is one-to-one: a difference is zero exactly when
+        // the patterns agree
+        st.ndl += min((uint32_t)o0, 1u) + min((uint32_t)o1, 1u);
       }
     }
   }
@@ -728,6 +732,17 @@ __device__ __forceinline__ void process_step(const uint32_t (&ua)[8], const uint
         }
       }
       const bool act = !ok && ((valid >> j) & 1u);
+      if (ORD) {
+        uint32_t pa = ua[0], pb = ub[0];
+#pragma unroll
+        for (int t = 1; t < 8; ++t) {
+          if (j == t) {
+            pa = ua[t];
+            pb = ub[t];
+          }
+        }
+        if (act && pa != pb) st.ndl += 1u;  // the lanes that are not ok
+      }
       const bool fa = isfinite(a), fb = isfinite(b);
       if (BITS) {
         st.nfa += __popcll(ballot(act && !fa));
@@ -851,6 +866,21 @@ __device__ __forceinline__ void process_step(const uint32_t (&ua)[8], const uint
         const uint32_t any = __builtin_bit_cast(uint32_t, od[0]) | __builtin_bit_cast(uint32_t, od[1]) |
                              __builtin_bit_cast(uint32_t, od[2]) | __builtin_bit_cast(uint32_t, od[3]);
         if (ballot(any != 0)) {
+          int js = 8;  // first differing element of this lane
+#pragma unroll
+          for (int j = 7; j >= 0; --j)
+            if (ua[j] != ub[j]) js = j;
+          const int li = js < 8 ? base + lane_offset_dyn<MAPB>(lane, js) : 0x7fffffff;
+          st.first = uniform(wave_min(li));
+        }
+      }
+    } else if (ORD) {
+      // first differing column, until one is found (the count is per lane)
+      if (st.first < 0) {
+        bool dj = false;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) dj |= (ua[j] != ub[j]);
+        if (ballot(dj)) {
           int js = 8;  // first differing element of this lane
 #pragma unroll
           for (int j = 7; j >= 0; --j)
