@@ -89,6 +89,9 @@ struct WaveState {
   int omax, omin;
   s16x2 hmax, hmin;
   uint32_t ndl;
+  // bf16 pairs: the differing counts of the low and high halves of the
+  // words since the last fold, one 16-bit count per half
+  uint32_t ndh;
   // float partial sums of the fast path, added into the double sums every
   // kFold steps, before the reference moves and at the end of the chunk
   float ps, pd, pf, pab, psd, psb;
@@ -109,6 +112,8 @@ __device__ __forceinline__ void fold_partials(WaveState &st) {
   st.ssd += (double)st.psd;
   st.ssb += (double)st.psb;
   st.ps = st.pd = st.pf = st.pab = st.psd = st.psb = 0.0f;
+  st.ndl += (st.ndh & 0xffffu) + (st.ndh >> 16);
+  st.ndh = 0u;
   st.nstep = 0;
 }
 
@@ -535,12 +540,6 @@ __device__ __forceinline__ s16x2 order16x2(uint32_t w) {
   const s16x2 t = __builtin_bit_cast(s16x2, w) >> (s16x2)15;
   return __builtin_bit_cast(s16x2, w ^ (__builtin_bit_cast(uint32_t, t) & 0x7fff7fffu));
 }
-// Number of nonzero 16-bit lanes of a word: (x & 0x7fff) + 0x7fff carries
-// into bit 15 of its lane exactly when the low 15 bits are not all zero.
-__device__ __forceinline__ uint32_t nonzero16x2(uint32_t x) {
-  const uint32_t t = (x & 0x7fff7fffu) + 0x7fff7fffu;
-  return (uint32_t)__builtin_popcount((t | x) & 0x80008000u);
-}
 
 // ---------------------------------------------------------------- one wave step
 
@@ -660,10 +659,21 @@ __device__ __forceinline__ void process_step(const uint32_t (&ua)[8], const uint
   s16x2 od[4];
   if (PACK) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      od[i] = order16x2(wa[i]) - order16x2(wb[i]);
-      st.ndl += nonzero16x2(__builtin_bit_cast(uint32_t, od[i]));
-    }
+    for (int i = 0; i < 4; ++i) od[i] = order16x2(wa[i]) - order16x2(wb[i]);
+    // min(difference, 1) in each unsigned 16-bit lane is one exactly when
+    // the lane differs; four words add at most 4 to each half per step, and
+    // the halves are folded into ndl every kFold steps, so the low half never
+    // carries into the high one.  The 1s come through an empty asm statement:
+    // a constant would let the compiler turn the packed minimum into a
+    // compare and select per half.
+    uint32_t one2;
+    asm("" : "=v"(one2) : "0"(0x00010001u));
+    uint32_t nz[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      nz[i] = __builtin_bit_cast(uint32_t, __builtin_elementwise_min(__builtin_bit_cast(u16x2, od[i]),
+                                                                     __builtin_bit_cast(u16x2, one2)));
+    st.ndh += nz[0] + nz[1] + nz[2] + nz[3];
   }
 
   if (ok) {
@@ -971,6 +981,7 @@ __attribute__((amdgpu_waves_per_eu(4, 8))) void k_row_stats(StreamArgs args) {
   st.omax = st.omin = 0;
   st.hmax = st.hmin = (s16x2)0;
   st.ndl = 0u;
+  st.ndh = 0u;
   st.ps = st.pd = st.pf = st.pab = st.psd = st.psb = 0.0f;
   st.nstep = 0;
   st.low = -INFINITY;
