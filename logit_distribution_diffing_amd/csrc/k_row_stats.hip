@@ -92,6 +92,14 @@ struct WaveState {
   // bf16 pairs: the differing counts of the low and high halves of the
   // words since the last fold, one 16-bit count per half
   uint32_t ndh;
+  // Two constants the compiler must not see as constants, set once through
+  // empty asm statements: 1 in each 16-bit half (a literal 1 turns the packed
+  // minimum below into a compare and select per half), and log2(e) in a
+  // vector register, so that the exponent's multiply-add reads the reference
+  // from its scalar register directly (with the literal it copies the
+  // reference into a vector register at every step).
+  uint32_t one2;
+  float l2e;
   // float partial sums of the fast path, added into the double sums every
   // kFold steps, before the reference moves and at the end of the chunk
   float ps, pd, pf, pab, psd, psb;
@@ -607,13 +615,13 @@ __device__ __forceinline__ void process_step(const uint32_t (&ua)[8], const uint
     // e*phi(delta) = (e*delta^2) * P(delta), P(d) = 1/2 - d/6 + d^2/24; the
     // dropped d^3/120 term is below 3.3e-5 of P for |d| <= 1/8.  One
     // accumulator per sum: four waves per SIMD hide the chain latency.
-    float e = __builtin_amdgcn_exp2f(fmaf(ya[0], kL2E, st.nr2h));
+    float e = __builtin_amdgcn_exp2f(fmaf(ya[0], st.l2e, st.nr2h));
     sg = e;
     dg = e * d[0];
     fg = e * ((d[0] * d[0]) * fmaf(d[0], fmaf(d[0], 1.0f / 24.0f, -1.0f / 6.0f), 0.5f));
 #pragma unroll
     for (int j = 1; j < 8; ++j) {
-      e = __builtin_amdgcn_exp2f(fmaf(ya[j], kL2E, st.nr2h));
+      e = __builtin_amdgcn_exp2f(fmaf(ya[j], st.l2e, st.nr2h));
       const float q = (d[j] * d[j]) * fmaf(d[j], fmaf(d[j], 1.0f / 24.0f, -1.0f / 6.0f), 0.5f);
       sg += e;
       dg = fmaf(e, d[j], dg);
@@ -663,11 +671,8 @@ __device__ __forceinline__ void process_step(const uint32_t (&ua)[8], const uint
     // min(difference, 1) in each unsigned 16-bit lane is one exactly when
     // the lane differs; four words add at most 4 to each half per step, and
     // the halves are folded into ndl every kFold steps, so the low half never
-    // carries into the high one.  The 1s come through an empty asm statement:
-    // a constant would let the compiler turn the packed minimum into a
-    // compare and select per half.
-    uint32_t one2;
-    asm("" : "=v"(one2) : "0"(0x00010001u));
+    // carries into the high one
+    const uint32_t one2 = st.one2;
     uint32_t nz[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
@@ -982,6 +987,8 @@ __attribute__((amdgpu_waves_per_eu(4, 8))) void k_row_stats(StreamArgs args) {
   st.hmax = st.hmin = (s16x2)0;
   st.ndl = 0u;
   st.ndh = 0u;
+  asm volatile("" : "=v"(st.one2) : "0"(0x00010001u));
+  asm volatile("" : "=v"(st.l2e) : "0"(kL2E));
   st.ps = st.pd = st.pf = st.pab = st.psd = st.psb = 0.0f;
   st.nstep = 0;
   st.low = -INFINITY;
