@@ -176,11 +176,13 @@ struct Cand {
 // LDS) to exactly the kint largest keys -- value descending, index ascending
 // -- and raise the threshold to at most the kint-th key.  Whole wave, uniform
 // control flow.  The entries are read into registers once (lane l holds
-// entries l, l + 64, ...); the selection is a bitwise radix search from the
-// top bit, one ballot per entry round and bit, which stops as soon as exactly
-// kint keys lie at or above its prefix: those are the kint largest, and the
-// prefix serves as the threshold (later elements have higher columns than
-// every entry, so any value with kint entries at or above it will do).
+// entries l, l + 64, ...); the selection is a radix search from the top bit,
+// two bits per round (three ballots per entry round, issued together, so
+// their round trips to the scalar unit overlap: half the rounds of a one-bit
+// search), which stops as soon as exactly kint keys lie at or above its
+// prefix: those are the kint largest, and the prefix serves as the threshold
+// (later elements have higher columns than every entry, so any value with
+// kint entries at or above it will do).
 // A16: the values are bf16, so every key ends in 16 zero bits (positive) or
 // 16 one bits (negative) and the search stops at bit 16.
 constexpr uint32_t kKeyFinite = 0x00800000u;  // rank_key(-FLT_MAX): the lowest finite value
@@ -204,22 +206,34 @@ __device__ __forceinline__ void flush_candidates(Cand *cb, WaveState &st, int ki
       idx[q] = c.i;
     }
   }
-  // kint-th largest value key, one bit at a time from the top; early exit
-  // once the prefix T (a finite value, so that the threshold is one) has
-  // exactly kint keys at or above it
+  // kint-th largest value key, two bits at a time from the top: the largest
+  // of the three extensions of T with at least kint keys at or above it;
+  // early exit once the prefix T (a finite value, so that the threshold is
+  // one) has exactly kint keys at or above it
   uint32_t T = 0;
   int nT = cnt;  // keys >= T: every stored key is above 0
   bool early = false;
 #pragma unroll 1
-  for (int bit = 31; bit >= (A16 ? 16 : 0); --bit) {
-    const uint32_t c = T | (1u << bit);
-    int n = 0;
+  for (int bit = 30; bit >= (A16 ? 16 : 0); bit -= 2) {
+    const uint32_t c1 = T | (1u << bit), c2 = T | (2u << bit), c3 = T | (3u << bit);
+    int n1 = 0, n2 = 0, n3 = 0;
 #pragma unroll
-    for (int q = 0; q < kRounds; ++q)
-      if (q < per) n += __popcll(ballot(key[q] >= c));
-    if (n >= kint) {
-      T = c;
-      nT = n;
+    for (int q = 0; q < kRounds; ++q) {
+      if (q < per) {
+        n1 += __popcll(ballot(key[q] >= c1));
+        n2 += __popcll(ballot(key[q] >= c2));
+        n3 += __popcll(ballot(key[q] >= c3));
+      }
+    }
+    if (n3 >= kint) {
+      T = c3;
+      nT = n3;
+    } else if (n2 >= kint) {
+      T = c2;
+      nT = n2;
+    } else if (n1 >= kint) {
+      T = c1;
+      nT = n1;
     }
     if (nT == kint && T >= kKeyFinite) {
       early = true;
@@ -818,10 +832,22 @@ __device__ __forceinline__ void process_step(const uint32_t (&ua)[8], const uint
         uint32_t T = 0;
         bool early = false;
 #pragma unroll 1
-        for (int bit = 31; bit >= (A16 ? 16 : 0); --bit) {
-          const uint32_t c = T | (1u << bit);
-          const int n = __popcll(ballot(kg >= c));
-          if (n >= kint) T = c;
+        for (int bit = 30; bit >= (A16 ? 16 : 0); bit -= 2) {
+          const uint32_t c1 = T | (1u << bit), c2 = T | (2u << bit), c3 = T | (3u << bit);
+          const int n1 = __popcll(ballot(kg >= c1));
+          const int n2 = __popcll(ballot(kg >= c2));
+          const int n3 = __popcll(ballot(kg >= c3));
+          int n = -1;
+          if (n3 >= kint) {
+            T = c3;
+            n = n3;
+          } else if (n2 >= kint) {
+            T = c2;
+            n = n2;
+          } else if (n1 >= kint) {
+            T = c1;
+            n = n1;
+          }
           if (n == kint && T >= kKeyFinite) {
             early = true;
             break;

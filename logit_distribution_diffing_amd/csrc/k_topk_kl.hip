@@ -224,7 +224,7 @@ __global__ __launch_bounds__(kWave) void k_topk_kl(FinalArgs a) {
   const int bx = lanes_min((has && cs.bidx >= 0 && bm == BM) ? cs.bidx : 0x7fffffff, C);
   const int top1_cand = bx == 0x7fffffff ? -1 : bx;
 
-  // ---- the row's top kint slots: the kint-th largest key T, one bit at a time from the top; then the ties at T
+  // ---- the row's top kint slots: the kint-th largest key T, two bits at a time from the top; then the ties at T
   // that are kept, lowest indices first.  The search stops as soon as exactly kint keys lie at or above its
   // prefix (those are the kint largest).  bf16 baseline values give keys whose low 16 bits are all equal
   // (zeros when positive, ones when negative), so their search ends at bit 16.
@@ -232,16 +232,29 @@ __global__ __launch_bounds__(kWave) void k_topk_kl(FinalArgs a) {
   uint32_t T = 0;
   int nT = kWave * kSlotRounds;  // at least kint keys lie at or above T
   bool early = false;
+  // each round takes the largest of the three extensions of T with at least
+  // kint keys at or above it (three ballots per slot round, issued together)
 #pragma unroll 1
-  for (int bit = 31; bit >= (k16 ? 16 : 0); --bit) {
-    const uint32_t c = T | (1u << bit);
-    int n = 0;
+  for (int bit = 30; bit >= (k16 ? 16 : 0); bit -= 2) {
+    const uint32_t c1 = T | (1u << bit), c2 = T | (2u << bit), c3 = T | (3u << bit);
+    int n1 = 0, n2 = 0, n3 = 0;
 #pragma unroll
-    for (int q = 0; q < kSlotRounds; ++q)
-      if (q < rounds) n += __popcll(ballot(key[q] >= c));
-    if (n >= kint) {
-      T = c;
-      nT = n;
+    for (int q = 0; q < kSlotRounds; ++q) {
+      if (q < rounds) {
+        n1 += __popcll(ballot(key[q] >= c1));
+        n2 += __popcll(ballot(key[q] >= c2));
+        n3 += __popcll(ballot(key[q] >= c3));
+      }
+    }
+    if (n3 >= kint) {
+      T = c3;
+      nT = n3;
+    } else if (n2 >= kint) {
+      T = c2;
+      nT = n2;
+    } else if (n1 >= kint) {
+      T = c1;
+      nT = n1;
     }
     if (nT == kint) {
       early = true;
